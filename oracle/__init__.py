@@ -1,0 +1,196 @@
+"""CPU oracle for the weight-only-quantized top-k MoE layer and the 2:4-sparse
+W4A16 linear layer.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.
+
+The arithmetic lives in ``oracle.c`` (plain C, double accumulation); this module
+only builds and loads it and marshals numpy arrays.  Inputs are the canonical
+logical tensors of ``gen.synth`` (never a packed layout); 16-bit values are
+passed as the float32 values that hold them exactly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FMA
+    contraction, so results do not depend on the host CPU)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-std=c11",
+                               "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = C.CDLL(_LIB)
+        i64, i32, p = C.c_int64, C.c_int, C.c_void_p
+        L.orc_route.argtypes = [p, i64, i32, i32, i32, p, p]
+        L.orc_align_capacity.argtypes = [i64, i32, i32]
+        L.orc_align_capacity.restype = i64
+        L.orc_align.argtypes = [p, i64, i32, i32, p, p, p, i64]
+        L.orc_moe_up.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, i32, p, i64, p, p]
+        L.orc_moe_down.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, i32, p, i64, p, p]
+        L.orc_moe_combine.argtypes = [i64, i32, i32, p, p, i64, p, p]
+        L.orc_moe_layer.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, p, i32, p, p, p, i32, p, i64,
+                                    p, p, p, p]
+        L.orc_sparse24.argtypes = [i64, i32, i32, p, p, p, p, i32, p, i64, p]
+        for f in ("orc_route", "orc_align", "orc_moe_up", "orc_moe_down", "orc_moe_combine", "orc_moe_layer",
+                  "orc_sparse24"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments" % what)
+
+
+# ----------------------------------------------------------------------------
+def route(logits: np.ndarray, topk: int, renormalize: bool = True):
+    """-> (topk_weights [M, topk] float32, topk_ids [M, topk] int32)"""
+    lg = _c(logits, np.float32)
+    M, E = lg.shape
+    w = np.empty((M, topk), np.float32)
+    ids = np.empty((M, topk), np.int32)
+    _check(lib().orc_route(_ptr(lg), M, E, topk, int(bool(renormalize)), _ptr(w), _ptr(ids)), "route")
+    return w, ids
+
+
+def align_capacity(T: int, E: int, block_size: int) -> int:
+    return int(lib().orc_align_capacity(T, E, block_size))
+
+
+def align(topk_ids: np.ndarray, E: int, block_size: int, capacity: Optional[int] = None):
+    """-> (sorted_token_ids [cap] int32, expert_ids [cap/BS] int32, num_tokens_post_padded int)"""
+    ids = _c(topk_ids, np.int32).reshape(-1)
+    T = ids.size
+    cap = align_capacity(T, E, block_size) if capacity is None else capacity
+    st = np.empty(cap, np.int32)
+    ex = np.empty(cap // block_size, np.int32)
+    nt = np.zeros(1, np.int32)
+    _check(lib().orc_align(_ptr(ids), T, E, block_size, _ptr(st), _ptr(ex), _ptr(nt), cap), "align")
+    return st, ex, int(nt[0])
+
+
+def _groups(s, n_out):
+    return int(s.shape[1])
+
+
+def moe_up(x, topk_ids, w1q, s1, g1=None, rows=None, want_gu=False):
+    """-> (gu [R*topk, 2N] or None, h [R*topk, N]) in float64."""
+    x = _c(x, np.float32)
+    ids = _c(topk_ids, np.int32)
+    M, K = x.shape
+    topk = ids.shape[1]
+    E, n_out, _ = w1q.shape
+    N = n_out // 2
+    rows_a = _c(rows, np.int64)
+    R = M if rows_a is None else rows_a.size
+    gu = np.empty((R * topk, n_out)) if want_gu else None
+    h = np.empty((R * topk, N))
+    _check(lib().orc_moe_up(M, K, N, E, topk, _ptr(x), _ptr(ids), _ptr(_c(w1q, np.int8)), _ptr(_c(s1, np.float32)),
+                            _ptr(_c(g1, np.int32)), s1.shape[1], _ptr(rows_a), R, _ptr(gu), _ptr(h)), "moe_up")
+    return gu, h
+
+
+def moe_down(h, topk_ids, w2q, s2, g2=None, rows=None, M=None):
+    """h [R*topk, N] -> y [R*topk, K] float64 (unweighted expert outputs)."""
+    ids = _c(topk_ids, np.int32)
+    topk = ids.shape[1]
+    M = ids.shape[0] if M is None else M
+    E, K, N = w2q.shape
+    rows_a = _c(rows, np.int64)
+    R = M if rows_a is None else rows_a.size
+    h = _c(h, np.float64)
+    assert h.shape == (R * topk, N)
+    y = np.empty((R * topk, K))
+    _check(lib().orc_moe_down(M, K, N, E, topk, _ptr(ids), _ptr(_c(w2q, np.int8)), _ptr(_c(s2, np.float32)),
+                              _ptr(_c(g2, np.int32)), s2.shape[1], _ptr(rows_a), R, _ptr(h), _ptr(y)), "moe_down")
+    return y
+
+
+def moe_combine(y, topk_weights, rows=None):
+    w = _c(topk_weights, np.float32)
+    M, topk = w.shape
+    rows_a = _c(rows, np.int64)
+    R = M if rows_a is None else rows_a.size
+    K = y.shape[1]
+    out = np.empty((R, K))
+    _check(lib().orc_moe_combine(M, K, topk, _ptr(w), _ptr(rows_a), R, _ptr(_c(y, np.float64)), _ptr(out)),
+           "moe_combine")
+    return out
+
+
+def moe_layer(x, topk_weights, topk_ids, w1q, s1, g1, w2q, s2, g2, rows=None, want=("out",)):
+    """Whole routed layer.  Returns a dict with 'out' [R, K] and, on request,
+    'gu', 'h', 'y' (all float64)."""
+    x = _c(x, np.float32)
+    w = _c(topk_weights, np.float32)
+    ids = _c(topk_ids, np.int32)
+    M, K = x.shape
+    topk = ids.shape[1]
+    E, n_out, _ = w1q.shape
+    N = n_out // 2
+    rows_a = _c(rows, np.int64)
+    R = M if rows_a is None else rows_a.size
+    res = {"out": np.empty((R, K))}
+    if "gu" in want:
+        res["gu"] = np.empty((R * topk, n_out))
+    if "h" in want:
+        res["h"] = np.empty((R * topk, N))
+    if "y" in want:
+        res["y"] = np.empty((R * topk, K))
+    rc = lib().orc_moe_layer(M, K, N, E, topk, _ptr(x), _ptr(w), _ptr(ids),
+                             _ptr(_c(w1q, np.int8)), _ptr(_c(s1, np.float32)), _ptr(_c(g1, np.int32)), s1.shape[1],
+                             _ptr(_c(w2q, np.int8)), _ptr(_c(s2, np.float32)), _ptr(_c(g2, np.int32)), s2.shape[1],
+                             _ptr(rows_a), R, _ptr(res.get("gu")), _ptr(res.get("h")), _ptr(res.get("y")),
+                             _ptr(res["out"]))
+    _check(rc, "moe_layer")
+    return res
+
+
+def moe_layer_from_weights(wts, x_f32, topk_weights, topk_ids, rows=None, want=("out",)):
+    """Convenience: the layer for a gen.synth.MoEWeights bundle."""
+    return moe_layer(x_f32, topk_weights, topk_ids, wts.w1q, wts.s1_f32(), wts.g1, wts.w2q, wts.s2_f32(), wts.g2,
+                     rows=rows, want=want)
+
+
+def sparse24(x, vals, idx, s, group_size, rows=None):
+    """y [R, N] float64 for the 2:4-sparse layer y = x W^T."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    N = vals.shape[0]
+    gs = K if group_size == -1 else group_size
+    rows_a = _c(rows, np.int64)
+    R = M if rows_a is None else rows_a.size
+    y = np.empty((R, N))
+    _check(lib().orc_sparse24(M, K, N, _ptr(x), _ptr(_c(vals, np.int8)), _ptr(_c(idx, np.uint8)),
+                              _ptr(_c(s, np.float32)), gs, _ptr(rows_a), R, _ptr(y)), "sparse24")
+    return y
