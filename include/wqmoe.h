@@ -1,0 +1,239 @@
+/*
+ * wqmoe.h -- C ABI of libwqmoe.so: the fused Mixture-of-Experts layer with
+ * weight-only quantized experts, and the 2:4-sparse W4A16 linear layer, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Hot-path calls (asynchronous on the caller's HIP stream, no allocation, no
+ * host synchronisation, no device-to-host read):
+ *   moe_route             router softmax + top-k
+ *   moe_align             token sort and pad per expert
+ *   moe_w4a16_gemm        grouped GEMM, int4 GPTQ-style weights, fp16 activations
+ *   moe_w8a16_gemm        grouped GEMM, int8 per-column weights, bf16/fp16 activations
+ *   sparse24_w4a16_gemm   2:4-sparse int4 dense linear layer, fp16 activations
+ * Off the hot path (host memory in and out): the packers that turn canonical
+ * quantized tensors into the device layout these kernels read.
+ *
+ * The hot path receives weights that are already quantized and just runs the
+ * kernels; quantisation and repacking live outside it ("Marlin moe
+ * integration", nm-vllm PR 266, review comments on what the hot-path function
+ * should receive).
+ *
+ * Conventions
+ *  - Pointers named d_* or documented "device" are device memory on the
+ *    current HIP device; all others are host memory.  Every device pointer must
+ *    be 16-byte aligned.  Row-major layouts throughout.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Ownership: the caller allocates and frees everything, workspaces
+ *    included.  The library keeps no state beyond a thread-local error text.
+ *  - Errors: arguments are validated on the host before anything is launched.
+ *    A failing call launches nothing and returns a non-zero status; the text of
+ *    the last error on this thread is returned by wq_last_error().  No call
+ *    aborts or throws across this boundary.
+ *  - Activation dtype codes: WQ_F16 = IEEE half, WQ_BF16 = bfloat16.  Scales
+ *    must be in the activation dtype (scales may be stored otherwise on disk;
+ *    conversion belongs to loading, not the hot path -- "Marlin moe
+ *    integration", review question on whether scales are guaranteed fp16).
+ */
+#ifndef WQMOE_H
+#define WQMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int wq_status;
+#define WQ_OK 0
+#define WQ_ERR_INVALID 1      /* null pointer, bad size, capacity/workspace too small, misaligned */
+#define WQ_ERR_UNSUPPORTED 2  /* a valid request this build does not implement (dtype, group size, shape) */
+#define WQ_ERR_DEVICE 3       /* a device pointer that is not on the current device */
+#define WQ_ERR_HIP 4          /* the HIP runtime reported an error at launch */
+
+#define WQ_F16 0
+#define WQ_BF16 1
+
+/* Stages of the grouped GEMM (moe_w4a16_gemm / moe_w8a16_gemm). */
+#define WQ_STAGE_GATE_UP 0 /* H = silu(A W_gate^T) * (A W_up^T), rows in sorted order       */
+#define WQ_STAGE_DOWN 1    /* out[m] = sum_j w[m,j] (H W_down^T)[row of (m,j)]               */
+#define WQ_STAGE_RAW 2     /* Z[i] = A[token of i] W^T in fp32, no epilogue (testing)       */
+
+#define WQ_PACK_INTERLEAVE_GATE_UP 1 /* packer flag: n_out = 2N rows = [gate; up], fused stage */
+
+int wq_version(void);
+const char* wq_status_string(wq_status s);
+const char* wq_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* moe_route                                                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * Router softmax and top-k, one token per row of `logits`.
+ *   d_logits        device float [M, E], finite values
+ *   d_topk_weights  device float [M, topk]  (out)
+ *   d_topk_ids      device int32 [M, topk]  (out)
+ * Slot order: larger logit first, equal logits -> lower expert index.
+ * renormalize = 1: weights are the softmax of the k selected logits (they sum
+ * to 1); renormalize = 0: the selected entries of the softmax over all E.
+ * exp, sum and divide are evaluated in double and rounded once to float.
+ * Limits: 1 <= E <= 1024, 1 <= topk <= min(E, 16), M >= 0 (M = 0 launches nothing).
+ * (The fused_moe interface the pages' kernels plug into: "Marlin moe
+ * integration", nm-vllm PR 266, review comment on the fused_moe interface.)
+ */
+wq_status moe_route(const float* d_logits, int M, int E, int topk, int renormalize,
+                    float* d_topk_weights, int32_t* d_topk_ids, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_align                                                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * Sort the T = M*topk (token, slot) pairs by expert and pad each expert's run
+ * to a multiple of block_size ("Marlin moe integration", nm-vllm PR 266,
+ * review thread on moe_align_block_size_kernel and its hard-coded block of 16).
+ * With i = m*topk + j and c_e the number of pairs routed to expert e:
+ *   p_e = ceil(c_e / block_size) * block_size, o_e = sum_{e'<e} p_e'
+ *   d_sorted_token_ids[o_e + r] = r-th i (ascending) with topk_ids[i] = e,
+ *   pad slots and the tail up to `capacity` hold the sentinel T;
+ *   d_expert_ids[b] = expert of block b, -1 for blocks past the end;
+ *   *d_num_tokens_post_padded = sum_e p_e.
+ * The result is unique (stable order), so it is reproducible bit for bit.
+ *   d_topk_ids                  device int32 [T], values in [0, E)
+ *   d_sorted_token_ids          device int32 [capacity]            (out)
+ *   d_expert_ids                device int32 [capacity/block_size] (out)
+ *   d_num_tokens_post_padded    device int32 [1]                   (out)
+ *   capacity >= moe_align_capacity(M, topk, E, block_size), a multiple of block_size
+ * Limits: 1 <= E <= 1024, block_size in {16, 32, 64, 128, 256}, T <= 2^24.
+ * Ids outside [0, E) are not detected on the device: such pairs are dropped.
+ */
+size_t moe_align_capacity(int M, int topk, int E, int block_size);
+wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block_size,
+                    int32_t* d_sorted_token_ids, int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded,
+                    size_t capacity, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Grouped GEMMs                                                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * One call runs one projection of every expert over the tokens routed to it,
+ * with the weights dequantized in registers and fp32 accumulation:
+ *  - int4: GPTQ-style symmetric codes in [-8, 7], one scale per group of 128
+ *    input channels (or per output column, group_size = -1), optional
+ *    act-order ("Marlin moe integration", nm-vllm PR 266, opening description
+ *    and the end-to-end tests with and without act-order);
+ *  - int8: symmetric per-expert, per-output-column codes, the weight is
+ *    code * scale ("[Kernel] W8A16 Int8 inside FusedMoE", vLLM PR 7415,
+ *    opening description).
+ * Expert rows are those of d_sorted_token_ids (from moe_align with the same
+ * block_size); block_size a multiple of 128 selects the large-batch kernel,
+ * smaller blocks the small-batch (decode) kernel.
+ *
+ * Stages (A is d_a, W the expert's packed weight of n_out rows, k_in columns):
+ *  GATE_UP  d_a = x [M, k_in]; W = w1 packed with WQ_PACK_INTERLEAVE_GATE_UP,
+ *           n_out = 2N.  d_out = H [capacity, N] in act dtype, row p of the
+ *           sorted order: H[p, n] = silu(g) * u with g, u the gate/up outputs
+ *           of row n for the token of sorted_token_ids[p]; pad rows are 0.
+ *           With act-order, d_k_perm is the permutation the packer returned
+ *           and the workspace holds the permuted activations.
+ *  DOWN     d_a = H [capacity, k_in] from GATE_UP (k_in = N); W = w2, n_out =
+ *           hidden size.  d_out = out [M, n_out] act dtype:
+ *           out[m, c] = sum_{j<topk} topk_weights[m,j] * (H W^T)[p(m,j), c],
+ *           summed in ascending j in fp32 and rounded once.  Needs a workspace
+ *           for the per-pair outputs (fp32 [M*topk, n_out]).
+ *  RAW      d_a = x [M, k_in]; d_out = fp32 [M*topk, n_out]:
+ *           Z[i, r] = sum_k x[i/topk, k] * W_{expert(i)}[r, k], packed row order.
+ * The workspace size comes from moe_gemm_workspace_bytes(); pass 0 / NULL if
+ * it returns 0.  Calls sharing a workspace must be stream-ordered.
+ */
+typedef struct wq_moe_gemm_desc {
+    size_t struct_size;          /* = sizeof(wq_moe_gemm_desc) */
+    int stage;                   /* WQ_STAGE_* */
+    int act_dtype;               /* WQ_F16 or WQ_BF16 */
+    const void* d_a;
+    int M, topk, E, n_out, k_in;
+    const void* d_w_packed;      /* from wq_pack_w4 / wq_pack_w8 */
+    const void* d_scales;        /* packed scales from the same packer call, act dtype */
+    int group_size;              /* int4: 128 or -1; int8: -1 */
+    const int32_t* d_k_perm;     /* int4 act-order GATE_UP/RAW: [E, k_in], else NULL */
+    const int32_t* d_sorted_token_ids;
+    const int32_t* d_expert_ids;
+    const int32_t* d_num_tokens_post_padded;
+    size_t capacity;
+    int block_size;
+    const float* d_topk_weights; /* DOWN only: [M, topk] */
+    void* d_out;
+    void* d_workspace;
+    size_t workspace_bytes;
+} wq_moe_gemm_desc;
+
+size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int n_out, int k_in, size_t capacity, int act_order);
+wq_status moe_w4a16_gemm(const wq_moe_gemm_desc* d, void* stream);
+wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 2:4-sparse W4A16 linear layer                                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * y[m, n] = sum_k x[m, k] W[n, k] with W [N, K] keeping 2 of every 4
+ * consecutive input channels, int4 codes in [-8, 7] and one fp16 scale per
+ * group of 128 input channels ("Add GPTQ Marlin 2:4 sparse structured
+ * support", vLLM PR 4790, opening description: group size 128, 4-bit).
+ *   d_x [M, K] fp16, d_y [M, N] fp16 (fp32 accumulation, rounded once)
+ *   d_vals, d_meta, d_scales: from wq_pack_sparse24
+ * Limits: K % 256 == 0, N % 16 == 0, group_size == 128, act_dtype == WQ_F16.
+ */
+wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
+                              const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Offline packers (host memory; not on the hot path)                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * Canonical inputs (per expert e, row r of n_out, input channel k of k_in):
+ *   q        int8   [E, n_out, k_in]  codes (int4: [-8, 7]; int8: [-128, 127])
+ *   scales   uint16 [E, G, n_out]     16-bit float bit patterns (G = k_in /
+ *                                     group_size, or 1 for per-column scales)
+ *   g_idx    int32  [E, k_in] or NULL act-order group of each input channel;
+ *                                     every group must hold exactly group_size
+ *                                     channels
+ *   row_perm int32  [E, n_rows] or NULL  output-row order to produce: packed
+ *                                     row p holds canonical row row_perm[e][p]
+ *                                     (with WQ_PACK_INTERLEAVE_GATE_UP, n_rows
+ *                                     = n_out/2 and the same order applies to
+ *                                     the gate and the up half).  Used to fold
+ *                                     the next projection's act-order input
+ *                                     permutation into this one's outputs.
+ * Outputs:
+ *   packed        wq_pack_w4_bytes() / wq_pack_w8_bytes() bytes
+ *   scales_packed uint16 [E, G, n_out] in packed row order
+ *   k_perm        int32 [E, k_in] (only with g_idx): packed input position k'
+ *                 holds canonical channel k_perm[e][k'] (stable sort by g_idx).
+ *                 Pass it as d_k_perm to the GATE_UP stage; for a DOWN weight
+ *                 pass it as row_perm when packing the GATE_UP weight instead.
+ * Limits: n_out % 16 == 0 (% 32 with interleave), int4 k_in % 128 == 0, int8
+ * k_in % 64 == 0.
+ */
+size_t wq_pack_w4_bytes(int E, int n_out, int k_in);
+size_t wq_pack_w8_bytes(int E, int n_out, int k_in);
+wq_status wq_pack_w4(int E, int n_out, int k_in, const int8_t* q, const uint16_t* scales, int group_size,
+                     const int32_t* g_idx, const int32_t* row_perm, int flags,
+                     void* packed, uint16_t* scales_packed, int32_t* k_perm);
+wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t* scales,
+                     const int32_t* row_perm, int flags, void* packed, uint16_t* scales_packed);
+
+/*
+ * 2:4 sparse canonical input: vals int8 [N, K/2] (kept codes in [-8, 7], two
+ * per group of 4 along K, ascending position), idx uint8 [N, K/2] (their
+ * positions 0..3 inside the group, strictly ascending per pair), scales uint16
+ * [K/128, N].  Outputs: vals_packed (wq_pack_sparse24_vals_bytes),
+ * meta_packed (wq_pack_sparse24_meta_bytes), scales_packed uint16 [K/128, N].
+ */
+size_t wq_pack_sparse24_vals_bytes(int N, int K);
+size_t wq_pack_sparse24_meta_bytes(int N, int K);
+wq_status wq_pack_sparse24(int N, int K, const int8_t* vals, const uint8_t* idx, const uint16_t* scales,
+                           void* vals_packed, void* meta_packed, uint16_t* scales_packed);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WQMOE_H */

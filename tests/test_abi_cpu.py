@@ -1,0 +1,220 @@
+"""CPU-only checks of the C ABI: the library loads and exports every function
+include/wqmoe.h declares, host-side validation rejects bad arguments with a
+status code (no GPU call is reached), and the offline packers produce the
+documented layouts."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gen
+import weight_only_quantized_topk_amd as wq
+from weight_only_quantized_topk_amd import _lib
+from tests.helpers import decode_sparse24, decode_w4, decode_w8, logical_rows
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # aligned, non-null: only ever seen by host-side validation below
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "wqmoe.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_match_header():
+    L = wq.load()
+    names = header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_status_strings_and_version():
+    L = wq.load()
+    assert L.wq_version() >= 1
+    assert L.wq_status_string(0) == b"ok"
+    assert L.wq_status_string(wq.WQ_ERR_UNSUPPORTED) == b"unsupported"
+
+
+def test_align_capacity():
+    L = wq.load()
+    assert L.moe_align_capacity(3, 2, 4, 4) == 20
+    assert L.moe_align_capacity(1, 2, 8, 16) == 32
+    assert L.moe_align_capacity(4096, 6, 160, 128) == 24576 + 160 * 127 + 0 * 0 // 1 + (-(24576 + 160 * 127) % 128)
+    assert L.moe_align_capacity(0, 2, 8, 16) == 0
+
+
+def _status(fn, *args):
+    L = wq.load()
+    st = getattr(L, fn)(*args)
+    return st, L.wq_last_error().decode()
+
+
+def test_route_validation():
+    p = C.c_void_p(FAKE)
+    assert _status("moe_route", p, 4, 8, 9, 1, p, p, None)[0] == wq.WQ_ERR_INVALID      # topk > E
+    assert _status("moe_route", p, -1, 8, 2, 1, p, p, None)[0] == wq.WQ_ERR_INVALID     # M < 0
+    assert _status("moe_route", p, 4, 2048, 2, 1, p, p, None)[0] == wq.WQ_ERR_UNSUPPORTED
+    assert _status("moe_route", p, 4, 64, 17, 1, p, p, None)[0] == wq.WQ_ERR_UNSUPPORTED
+    st, msg = _status("moe_route", None, 4, 8, 2, 1, p, p, None)
+    assert st == wq.WQ_ERR_INVALID and "logits" in msg
+    assert _status("moe_route", C.c_void_p(FAKE + 4), 4, 8, 2, 1, p, p, None)[0] == wq.WQ_ERR_INVALID  # misaligned
+    assert _status("moe_route", p, 0, 8, 2, 1, p, p, None)[0] == wq.WQ_OK  # nothing to do
+
+
+def test_align_validation():
+    p = C.c_void_p(FAKE)
+    assert _status("moe_align", p, 4, 2, 8, 24, p, p, p, 1024, None)[0] == wq.WQ_ERR_UNSUPPORTED   # block size
+    assert _status("moe_align", p, 4, 2, 8, 16, p, p, p, 16, None)[0] == wq.WQ_ERR_INVALID         # capacity
+    assert _status("moe_align", p, 4, 2, 8, 16, p, p, p, 136, None)[0] == wq.WQ_ERR_INVALID        # not multiple
+    assert _status("moe_align", p, 4, 2, 2000, 16, p, p, p, 1 << 20, None)[0] == wq.WQ_ERR_UNSUPPORTED
+    assert _status("moe_align", p, 4, 2, 8, 16, None, p, p, 1024, None)[0] == wq.WQ_ERR_INVALID
+
+
+def _desc(**kw):
+    d = _lib.WqMoeGemmDesc()
+    d.struct_size = C.sizeof(_lib.WqMoeGemmDesc)
+    d.stage = wq.WQ_STAGE_GATE_UP
+    d.act_dtype = wq.WQ_F16
+    d.M, d.topk, d.E, d.n_out, d.k_in = 4, 2, 8, 1024, 256
+    for f in ("d_a", "d_w_packed", "d_scales", "d_sorted_token_ids", "d_expert_ids", "d_num_tokens_post_padded",
+              "d_out", "d_topk_weights"):
+        setattr(d, f, FAKE)
+    d.group_size = 128
+    d.block_size = 16
+    d.capacity = wq.moe_align_capacity(4, 2, 8, 16)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("fn,kw,expect", [
+    ("moe_w4a16_gemm", dict(struct_size=8), wq.WQ_ERR_INVALID),
+    ("moe_w4a16_gemm", dict(stage=7), wq.WQ_ERR_INVALID),
+    ("moe_w4a16_gemm", dict(act_dtype=wq.WQ_BF16), wq.WQ_ERR_UNSUPPORTED),
+    ("moe_w4a16_gemm", dict(topk=9), wq.WQ_ERR_INVALID),
+    ("moe_w4a16_gemm", dict(k_in=200), wq.WQ_ERR_UNSUPPORTED),
+    ("moe_w4a16_gemm", dict(n_out=1008), wq.WQ_ERR_UNSUPPORTED),       # gate/up needs n_out % 32
+    ("moe_w4a16_gemm", dict(group_size=64), wq.WQ_ERR_UNSUPPORTED),
+    ("moe_w4a16_gemm", dict(block_size=8), wq.WQ_ERR_UNSUPPORTED),
+    ("moe_w4a16_gemm", dict(capacity=32), wq.WQ_ERR_INVALID),
+    ("moe_w4a16_gemm", dict(d_a=None), wq.WQ_ERR_INVALID),
+    ("moe_w4a16_gemm", dict(d_out=FAKE + 8), wq.WQ_ERR_INVALID),
+    ("moe_w4a16_gemm", dict(stage=wq.WQ_STAGE_DOWN, n_out=256, k_in=512), wq.WQ_ERR_INVALID),  # no workspace
+    ("moe_w4a16_gemm", dict(d_k_perm=FAKE), wq.WQ_ERR_INVALID),        # act-order needs the gather workspace
+    ("moe_w8a16_gemm", dict(group_size=128), wq.WQ_ERR_UNSUPPORTED),   # int8 is per-column
+    ("moe_w8a16_gemm", dict(group_size=-1, k_in=96), wq.WQ_ERR_UNSUPPORTED),
+    ("moe_w8a16_gemm", dict(group_size=-1, d_k_perm=FAKE), wq.WQ_ERR_INVALID),
+    ("moe_w8a16_gemm", dict(group_size=-1, M=1 << 24), wq.WQ_ERR_UNSUPPORTED),
+])
+def test_gemm_validation(fn, kw, expect):
+    d = _desc(**kw)
+    st, msg = _status(fn, C.byref(d), None)
+    assert st == expect, msg
+    assert msg
+
+
+def test_gemm_workspace_sizes():
+    L = wq.load()
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 1024, 256, 128, 0) == 0
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 1024, 256, 128, 1) == 128 * 256 * 2
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, 4, 2, 256, 512, 128, 0) == 4 * 2 * 256 * 4
+
+
+def test_sparse_validation():
+    p = C.c_void_p(FAKE)
+    L = wq.load()
+    assert L.sparse24_w4a16_gemm(p, 4, 7168, 20480, p, p, p, 64, p, wq.WQ_F16, None) == wq.WQ_ERR_UNSUPPORTED
+    assert L.sparse24_w4a16_gemm(p, 4, 7000, 20480, p, p, p, 128, p, wq.WQ_F16, None) == wq.WQ_ERR_UNSUPPORTED
+    assert L.sparse24_w4a16_gemm(p, 4, 7168, 20480, p, p, p, 128, p, wq.WQ_BF16, None) == wq.WQ_ERR_UNSUPPORTED
+    assert L.sparse24_w4a16_gemm(None, 4, 7168, 20480, p, p, p, 128, p, wq.WQ_F16, None) == wq.WQ_ERR_INVALID
+    assert L.sparse24_w4a16_gemm(p, 0, 7168, 20480, p, p, p, 128, p, wq.WQ_F16, None) == wq.WQ_OK
+
+
+# ----------------------------------------------------------------------------
+# packers
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("act_order,interleave,rowperm", [(False, False, False), (False, True, False),
+                                                          (True, True, True), (True, False, False)])
+def test_pack_w4_layout(act_order, interleave, rowperm):
+    spec = gen.CFG3.with_(E=3, K=256, N=128, act_order=act_order)
+    w = gen.make_moe_weights(spec, seed_config=401)
+    q, s, g = w.w1q, w.s1, w.g1
+    E, n_out, k_in = q.shape
+    rp = None
+    if rowperm:
+        rng = np.random.default_rng(0)
+        rp = np.stack([rng.permutation(n_out // 2 if interleave else n_out) for _ in range(E)]).astype(np.int32)
+    packed, sp, kp = wq.pack_w4(q, s, 128, g_idx=g, row_perm=rp, interleave_gate_up=interleave)
+    dec = decode_w4(packed, E, n_out, k_in)
+    for e in range(E):
+        rows = logical_rows(n_out, interleave, None if rp is None else rp[e])
+        sig = kp[e] if act_order else np.arange(k_in)
+        if act_order:
+            assert (g[e][sig] == np.arange(k_in) // 128).all()          # groups become contiguous
+            assert (np.diff(sig.reshape(-1, 128), axis=1) > 0).all()    # stable inside each group
+        assert np.array_equal(dec[e], q[e][rows][:, sig])
+        assert np.array_equal(sp[e], s[e][:, rows])
+
+
+def test_pack_w8_layout():
+    spec = gen.CFG2.with_(E=2, K=192, N=64)
+    w = gen.make_moe_weights(spec, seed_config=402)
+    for q, s, il in ((w.w1q, w.s1, True), (w.w2q, w.s2, False)):
+        packed, sp = wq.pack_w8(q, s, interleave_gate_up=il)
+        E, n_out, k_in = q.shape
+        dec = decode_w8(packed, E, n_out, k_in)
+        rows = logical_rows(n_out, il)
+        assert np.array_equal(dec, q[:, rows, :])
+        assert np.array_equal(sp, s[:, :, rows])
+
+
+def test_pack_sparse24_layout():
+    spec = gen.CFG4.with_(K=512, N=32)
+    sw = gen.make_sparse_weights(spec, seed_config=403)
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s)
+    v, i = decode_sparse24(vp, mp, spec.N, spec.K)
+    assert np.array_equal(v, sw.vals) and np.array_equal(i, sw.idx)
+    assert np.array_equal(sp, sw.s)
+    assert vp.nbytes == spec.N * spec.K // 4 and mp.nbytes == spec.N * spec.K // 8
+
+
+def test_sparse24_metadata_roundtrip_all_patterns():
+    """All 6 keep patterns x all 16 x 16 code pairs survive pack -> decode."""
+    pairs = [(a, b) for a in range(4) for b in range(a + 1, 4)]
+    combos = [(p, v0, v1) for p in pairs for v0 in range(-8, 8) for v1 in range(-8, 8)]   # 1536 groups
+    K = 4 * 256
+    N = 16 * ((len(combos) + K // 4 - 1) // (K // 4))
+    vals = np.zeros((N, K // 2), np.int8)
+    idx = np.tile(np.array([0, 1], np.uint8), (N, K // 4))
+    flat_v = vals.reshape(-1, 2)
+    flat_i = idx.reshape(-1, 2)
+    for n, (p, v0, v1) in enumerate(combos):
+        flat_v[n] = (v0, v1)
+        flat_i[n] = p
+    s = np.ones((K // 128, N), np.uint16)
+    vp, mp, _ = wq.pack_sparse24(vals, idx, s)
+    v2, i2 = decode_sparse24(vp, mp, N, K)
+    assert np.array_equal(v2, vals) and np.array_equal(i2, idx)
+
+
+def test_packer_rejects_bad_input():
+    spec = gen.CFG3.with_(E=1, K=256, N=64, act_order=True)
+    w = gen.make_moe_weights(spec, seed_config=404)
+    bad = w.w1q.copy()
+    bad[0, 0, 0] = 9
+    with pytest.raises(wq.WqError):
+        wq.pack_w4(bad, w.s1, 128)
+    g = w.g1.copy()
+    g[0, np.argmax(g[0] == 1)] = 0      # group 0 now has 129 members, group 1 has 127
+    with pytest.raises(wq.WqError):
+        wq.pack_w4(w.w1q, w.s1, 128, g_idx=g)
+    idx = gen.make_sparse_weights(gen.CFG4.with_(K=256, N=16), seed_config=405).idx.copy()
+    idx[0, 0], idx[0, 1] = 2, 1
+    with pytest.raises(wq.WqError):
+        wq.pack_sparse24(np.zeros((16, 128), np.int8), idx, np.ones((2, 16), np.uint16))

@@ -1,0 +1,237 @@
+"""GPU parity of the grouped GEMMs, stage by stage and as a whole layer, on
+shapes that span several tiles with ragged token counts, on both kernels
+(small-batch block 16, large-batch block 128):
+  - RAW stage, exact-integer case: the fp32 projection equals the oracle's bit
+    for bit (all partial sums are dyadic numbers below 2^24);
+  - GATE_UP: H against the oracle's silu(gate) * up;
+  - DOWN: from the oracle's H (rounded to the activation type) to the combined
+    output;
+  - the whole layer (route -> align -> GATE_UP -> DOWN) against the oracle;
+  - determinism and token-permutation equivariance, bit for bit.
+Float comparisons use relative Frobenius error <= 5e-3 and max abs error <=
+3e-2 * max |ref| per output tensor."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import weight_only_quantized_topk_amd as wq
+from tests.gpu_common import act_round, dev_u16, host_f32, need_gpu, say, torch
+from tests.helpers import assert_close_fp
+
+pytestmark = pytest.mark.gpu
+
+W4 = gen.CFG3.with_(name="w4-small", E=8, topk=2, K=512, N=384, act_order=False)
+W4AO = W4.with_(name="w4ao-small", act_order=True)
+W4PC = W4.with_(name="w4-percol-small", group_size=-1)
+W8 = gen.CFG2.with_(name="w8-small", E=8, topk=2, K=512, N=384)
+W8E = gen.CFG5.with_(name="w8-many-small", E=40, topk=6, K=256, N=256, zipf_s=1.1)
+SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E}
+SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505}
+
+
+def _pack(spec, wts):
+    return wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2,
+                       torch.float16 if spec.act == "f16" else torch.bfloat16, spec.group_size, wts.g1, wts.g2)
+
+
+_cache = {}
+
+
+def setup(key):
+    if key not in _cache:
+        spec = SPECS[key]
+        wts = gen.make_moe_weights(spec, seed_config=SEED[key])
+        _cache[key] = (spec, wts, _pack(spec, wts))
+    return _cache[key]
+
+
+def routed(spec, M, seed):
+    toks = gen.make_tokens(spec, M, seed_config=seed)
+    w, ids = oracle.route(toks.logits, spec.topk, spec.renormalize)
+    return toks, w, ids
+
+
+def align_dev(ids, E, bs):
+    cap = wq.moe_align_capacity(ids.shape[0], ids.shape[1], E, bs)
+    st, ex, nt = wq.moe_align(torch.from_numpy(ids).cuda(), E, bs, cap)
+    return st, ex, nt, cap
+
+
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("act_order", [False, True])
+def test_raw_exact_integer(bits, bs, act_order):
+    """Power-of-two group scales, x in {-1,0,1}: bit-exact fp32 projections."""
+    need_gpu()
+    if act_order and bits == 8:
+        pytest.skip("act-order is an int4 (GPTQ) feature")
+    spec = (W4AO if act_order else W4) if bits == 4 else W8
+    wts = gen.make_moe_weights(spec, seed_config=510 + bits)
+    E, n_out, K = wts.w1q.shape
+    rng = np.random.default_rng(bits * 10 + bs)
+    G = wts.s1.shape[1]
+    pow2 = np.array([0.25, 0.5, 1.0, 2.0], np.float32)[rng.integers(0, 4, size=(E, G, n_out))]
+    s_bits = gen.round_to(spec.act, pow2)
+    M = 45
+    x = rng.integers(-1, 2, size=(M, K)).astype(np.float32)
+    ids = np.stack([rng.choice(E, spec.topk, replace=False) for _ in range(M)]).astype(np.int32)
+    gu_ref, _ = oracle.moe_up(x, ids, wts.w1q, pow2, wts.g1, want_gu=True)
+    if bits == 4:
+        packed, sp, kp = wq.pack_w4(wts.w1q, s_bits, spec.group_size, g_idx=wts.g1)
+    else:
+        packed, sp = wq.pack_w8(wts.w1q, s_bits)
+        kp = None
+    st, ex, nt, cap = align_dev(ids, E, bs)
+    xd = dev_u16(gen.round_to(spec.act, x), spec.act)
+    out = torch.empty((M * spec.topk, n_out), dtype=torch.float32, device="cuda")
+    wd = torch.from_numpy(packed).cuda()
+    sd = torch.from_numpy(sp.view(np.int16)).cuda()
+    say("raw exact", bits, bs, act_order)
+    if bits == 4:
+        kpd = torch.from_numpy(kp).cuda() if kp is not None else None
+        ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_RAW, M, spec.topk, n_out, K, cap, kp is not None)
+        work = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
+        wq.moe_w4a16_gemm(wq.WQ_STAGE_RAW, xd, M, spec.topk, E, n_out, K, wd, sd, spec.group_size, kpd, st, ex, nt,
+                          cap, bs, None, out, work)
+    else:
+        wq.moe_w8a16_gemm(wq.WQ_STAGE_RAW, xd, M, spec.topk, E, n_out, K, wd, sd, st, ex, nt, cap, bs, None, out,
+                          act_dtype=wq.WQ_BF16)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, gu_ref), "max diff %g" % np.abs(got - gu_ref).max()
+
+
+# ----------------------------------------------------------------------------
+def run_gate_up(spec, p, xd, ids_np, bs):
+    M = xd.shape[0]
+    st, ex, nt, cap = align_dev(ids_np, spec.E, bs)
+    act_order = p.k_perm1 is not None
+    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, M, spec.topk, 2 * spec.N, spec.K, cap, act_order)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
+    h = torch.full((cap, spec.N), float("nan"), dtype=p.act, device="cuda")
+    if spec.bits == 4:
+        wq.moe_w4a16_gemm(wq.WQ_STAGE_GATE_UP, xd, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1, p.s1,
+                          spec.group_size, p.k_perm1, st, ex, nt, cap, bs, None, h, work)
+    else:
+        wq.moe_w8a16_gemm(wq.WQ_STAGE_GATE_UP, xd, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1, p.s1, st, ex, nt,
+                          cap, bs, None, h, work, act_dtype=p.act_code)
+    return h, st, ex, nt, cap
+
+
+def h_perm(spec, wts, e):
+    """Column order of H for expert e: canonical intermediate index of each H column."""
+    if spec.bits == 4 and wts.g2 is not None:
+        return np.argsort(wts.g2[e], kind="stable")
+    return np.arange(spec.N)
+
+
+@pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e"])
+@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("M", [1, 37, 300])
+def test_gate_up(key, bs, M):
+    need_gpu()
+    spec, wts, p = setup(key)
+    toks, w, ids = routed(spec, M, seed=600 + M)
+    say("gate_up", key, bs, M)
+    h, st, ex, nt, cap = run_gate_up(spec, p, dev_u16(toks.x, spec.act), ids, bs)
+    torch.cuda.synchronize()
+    _, h_ref = oracle.moe_up(toks.x_f32(), ids, wts.w1q, wts.s1_f32(), wts.g1)
+    hg = host_f32(h)
+    stn = st.cpu().numpy()
+    exn = ex.cpu().numpy()
+    ntn = int(nt.cpu()[0])
+    T = M * spec.topk
+    got = np.empty((T, spec.N))
+    for pos in range(ntn):
+        i = stn[pos]
+        if i < T:
+            e = exn[pos // bs]
+            got[i, h_perm(spec, wts, e)] = hg[pos]
+        else:
+            assert (hg[pos] == 0).all(), "pad row %d of H is not zero" % pos
+    assert_close_fp(got, h_ref, "H %s bs=%d M=%d" % (key, bs, M))
+
+
+@pytest.mark.parametrize("key", ["w4", "w4ao", "w8", "w8e"])
+@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("M", [1, 37, 300])
+def test_down(key, bs, M):
+    """DOWN from the oracle's H rounded to the activation type."""
+    need_gpu()
+    spec, wts, p = setup(key)
+    toks, w, ids = routed(spec, M, seed=700 + M)
+    T = M * spec.topk
+    _, h_ref = oracle.moe_up(toks.x_f32(), ids, wts.w1q, wts.s1_f32(), wts.g1)
+    h_act = act_round(h_ref, spec.act)
+    y_ref = oracle.moe_down(h_act, ids, wts.w2q, wts.s2_f32(), wts.g2)
+    out_ref = oracle.moe_combine(y_ref, w)
+    st, ex, nt, cap = align_dev(ids, spec.E, bs)
+    stn, exn, ntn = st.cpu().numpy(), ex.cpu().numpy(), int(nt.cpu()[0])
+    hs = np.zeros((cap, spec.N), np.float32)
+    for pos in range(ntn):
+        i = stn[pos]
+        if i < T:
+            hs[pos] = h_act[i][h_perm(spec, wts, exn[pos // bs])]
+    hd = torch.from_numpy(hs).cuda().to(p.act)
+    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, M, spec.topk, spec.K, spec.N, cap, False)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, spec.K), dtype=p.act, device="cuda")
+    wd = torch.from_numpy(w).cuda()
+    say("down", key, bs, M)
+    if spec.bits == 4:
+        wq.moe_w4a16_gemm(wq.WQ_STAGE_DOWN, hd, M, spec.topk, spec.E, spec.K, spec.N, p.w2, p.s2, spec.group_size,
+                          None, st, ex, nt, cap, bs, wd, out, work)
+    else:
+        wq.moe_w8a16_gemm(wq.WQ_STAGE_DOWN, hd, M, spec.topk, spec.E, spec.K, spec.N, p.w2, p.s2, st, ex, nt, cap,
+                          bs, wd, out, work, act_dtype=p.act_code)
+    torch.cuda.synchronize()
+    assert_close_fp(host_f32(out), out_ref, "out %s bs=%d M=%d" % (key, bs, M))
+
+
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e"])
+@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("M", [1, 16, 53, 512])
+def test_layer(key, bs, M):
+    need_gpu()
+    spec, wts, p = setup(key)
+    toks = gen.make_tokens(spec, M, seed_config=800 + M)
+    say("layer", key, bs, M)
+    out, aux = wq.fused_moe(dev_u16(toks.x, spec.act), torch.from_numpy(toks.logits).cuda(), p, spec.topk,
+                            spec.renormalize, block_size=bs, keep=True)
+    torch.cuda.synchronize()
+    w_ref, ids_ref = oracle.route(toks.logits, spec.topk, spec.renormalize)
+    assert np.array_equal(aux["topk_ids"].cpu().numpy(), ids_ref)
+    ref = oracle.moe_layer_from_weights(wts, toks.x_f32(), aux["topk_weights"].cpu().numpy(), ids_ref)["out"]
+    assert_close_fp(host_f32(out), ref, "layer %s bs=%d M=%d" % (key, bs, M))
+
+
+@pytest.mark.parametrize("key", ["w4ao", "w8"])
+@pytest.mark.parametrize("bs", [16, 128])
+def test_layer_deterministic_and_equivariant(key, bs):
+    need_gpu()
+    spec, wts, p = setup(key)
+    M = 97
+    toks = gen.make_tokens(spec, M, seed_config=900)
+    x = dev_u16(toks.x, spec.act)
+    lg = torch.from_numpy(toks.logits).cuda()
+    say("determinism", key, bs)
+    a = wq.fused_moe(x, lg, p, spec.topk, block_size=bs).clone()
+    b = wq.fused_moe(x, lg, p, spec.topk, block_size=bs)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(M)).cuda()
+    c = wq.fused_moe(x[perm].contiguous(), lg[perm].contiguous(), p, spec.topk, block_size=bs)
+    torch.cuda.synchronize()
+    assert torch.equal(c, a[perm])
+
+
+def test_layer_empty_batch():
+    need_gpu()
+    spec, wts, p = setup("w8")
+    out = wq.fused_moe(torch.empty((0, spec.K), dtype=torch.bfloat16, device="cuda"),
+                       torch.empty((0, spec.E), dtype=torch.float32, device="cuda"), p, spec.topk)
+    torch.cuda.synchronize()
+    assert out.shape == (0, spec.K)

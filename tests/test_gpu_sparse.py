@@ -1,0 +1,73 @@
+"""GPU parity of the 2:4-sparse W4A16 linear layer against the oracle: an
+exact-integer case (fp16 output holds the integer results exactly), and float
+cases spanning several tiles with ragged token counts."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import weight_only_quantized_topk_amd as wq
+from tests.gpu_common import dev_u16, host_f32, need_gpu, say, torch
+from tests.helpers import assert_close_fp
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sparse(sw, x_bits, N):
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s)
+    y = wq.sparse24_w4a16_gemm(dev_u16(x_bits, "f16"), torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(),
+                               torch.from_numpy(sp.view(np.int16)).cuda(), N)
+    torch.cuda.synchronize()
+    return host_f32(y)
+
+
+def test_sparse_exact_integer():
+    need_gpu()
+    spec = gen.CFG4.with_(K=512, N=96)
+    sw = gen.make_sparse_weights(spec, seed_config=310)
+    rng = np.random.default_rng(0)
+    x = rng.integers(-1, 2, size=(37, spec.K)).astype(np.float32)
+    ones = np.ones((spec.K // 128, spec.N), np.float32)
+    sw.s = gen.round_to("f16", ones)
+    say("sparse exact")
+    y = run_sparse(sw, gen.round_to("f16", x), spec.N)
+    ref = oracle.sparse24(x, sw.vals, sw.idx, ones, 128)
+    assert np.abs(ref).max() < 2048
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("M", [1, 16, 45, 130])
+def test_sparse_float(M):
+    need_gpu()
+    spec = gen.CFG4.with_(K=1024, N=256)
+    sw = gen.make_sparse_weights(spec, seed_config=311)
+    x = gen.make_sparse_x(spec, M, seed_config=311)
+    say("sparse float", M)
+    y = run_sparse(sw, x, spec.N)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128)
+    assert_close_fp(y, ref, "sparse M=%d" % M)
+
+
+def test_sparse_matches_dense_with_zeros_on_gpu():
+    """The 2:4 kernel and the dense int4 kernel (RAW stage, one expert, top-1)
+    agree on the same weights with zeros at the pruned positions."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=512, N=128)
+    sw = gen.make_sparse_weights(spec, seed_config=312)
+    x = gen.make_sparse_x(spec, 20, seed_config=312)
+    y_sp = run_sparse(sw, x, spec.N)
+    dense = np.zeros((1, spec.N, spec.K), np.int8)
+    grp = np.repeat(np.arange(spec.K // 4), 2)[None, :] * 4
+    np.put_along_axis(dense[0], grp + sw.idx.astype(np.int64), sw.vals, axis=1)
+    s_dense = np.ascontiguousarray(sw.s[None, :, :])                 # [1, G, N]
+    packed, sp, _ = wq.pack_w4(dense, s_dense, 128)
+    M = x.shape[0]
+    ids = np.zeros((M, 1), np.int32)
+    cap = wq.moe_align_capacity(M, 1, 1, 16)
+    st, ex, nt = wq.moe_align(torch.from_numpy(ids).cuda(), 1, 16, cap)
+    out = torch.empty((M, spec.N), dtype=torch.float32, device="cuda")
+    wq.moe_w4a16_gemm(wq.WQ_STAGE_RAW, dev_u16(x, "f16"), M, 1, 1, spec.N, spec.K, torch.from_numpy(packed).cuda(),
+                      torch.from_numpy(sp.view(np.int16)).cuda(), 128, None, st, ex, nt, cap, 16, None, out)
+    torch.cuda.synchronize()
+    dense_y = out.cpu().numpy().astype(np.float64)
+    assert_close_fp(y_sp, dense_y, "2:4 vs dense-with-zeros")

@@ -1,0 +1,555 @@
+// abi.cpp -- the C ABI of libwqmoe.so (declared in include/wqmoe.h): argument
+// validation, device checks, kernel dispatch, and the offline packers.
+//
+// Every entry point validates all sizes, pointers and formats on the host
+// before the first HIP call, so a rejected call launches nothing and the
+// validation itself runs (and is tested) on machines without a GPU.  Device
+// pointers must live on the current device: a multi-device process that hands
+// a kernel another device's buffer gets WQ_ERR_DEVICE instead of an illegal
+// access (the failure reported for moe_align_block_size_kernel on a second
+// device in "Marlin moe integration", nm-vllm PR 266, review thread).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/wqmoe.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+wq_status fail(wq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+wq_status ok() {
+    g_last_error.clear();
+    return WQ_OK;
+}
+
+#define WQ_REQUIRE(cond, st, ...)              \
+    do {                                       \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// host-side pointer sanity (no HIP call): non-null and 16-byte aligned
+wq_status check_ptr(const void* p, const char* name) {
+    WQ_REQUIRE(p != nullptr, WQ_ERR_INVALID, "%s is NULL", name);
+    WQ_REQUIRE(aligned16(p), WQ_ERR_INVALID, "%s is not 16-byte aligned", name);
+    return WQ_OK;
+}
+
+// device check: the pointer is device (or managed) memory of the current device
+wq_status check_dev(const void* p, const char* name) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(WQ_ERR_HIP, "hipGetDevice failed");
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(WQ_ERR_DEVICE, "%s is not a HIP allocation", name);
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(WQ_ERR_DEVICE, "%s is not device memory", name);
+    if (attr.type == hipMemoryTypeDevice && attr.device != cur)
+        return fail(WQ_ERR_DEVICE, "%s lives on device %d, current device is %d", name, attr.device, cur);
+    return WQ_OK;
+}
+
+#define WQ_TRY(expr)                      \
+    do {                                  \
+        wq_status _st = (expr);           \
+        if (_st != WQ_OK) return _st;     \
+    } while (0)
+
+wq_status after_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(WQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool valid_block_size(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+constexpr int64_t MAX_PAIRS = 1 << 24;
+
+template <class F>
+void parallel_for(int n, F f) {
+    unsigned hw = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
+    int nt = std::min<int>(n, (int)hw);
+    if (nt <= 1) {
+        for (int i = 0; i < n; ++i) f(i);
+        return;
+    }
+    std::vector<std::thread> th;
+    for (int t = 0; t < nt; ++t)
+        th.emplace_back([=]() {
+            for (int i = t; i < n; i += nt) f(i);
+        });
+    for (auto& x : th) x.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_version(void) { return 1; }
+
+const char* wq_status_string(wq_status s) {
+    switch (s) {
+        case WQ_OK: return "ok";
+        case WQ_ERR_INVALID: return "invalid argument";
+        case WQ_ERR_UNSUPPORTED: return "unsupported";
+        case WQ_ERR_DEVICE: return "wrong device";
+        case WQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* wq_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+size_t moe_align_capacity(int M, int topk, int E, int block_size) {
+    if (M < 0 || topk <= 0 || E <= 0 || block_size <= 0) return 0;
+    const int64_t T = (int64_t)M * topk;
+    const int64_t nz = std::min<int64_t>(T, E);
+    const int64_t cap = T + nz * (block_size - 1);
+    return (size_t)((cap + block_size - 1) / block_size * block_size);
+}
+
+wq_status moe_route(const float* d_logits, int M, int E, int topk, int renormalize, float* d_topk_weights,
+                    int32_t* d_topk_ids, void* stream) {
+    try {
+        WQ_REQUIRE(M >= 0, WQ_ERR_INVALID, "M = %d < 0", M);
+        WQ_REQUIRE(E >= 1 && topk >= 1 && topk <= E, WQ_ERR_INVALID, "need 1 <= topk <= E (topk %d, E %d)", topk, E);
+        WQ_REQUIRE(E <= 1024, WQ_ERR_UNSUPPORTED, "E = %d > 1024", E);
+        WQ_REQUIRE(topk <= 16, WQ_ERR_UNSUPPORTED, "topk = %d > 16", topk);
+        WQ_REQUIRE((int64_t)M * topk <= MAX_PAIRS, WQ_ERR_UNSUPPORTED, "M*topk > 2^24");
+        if (M == 0) return ok();
+        WQ_TRY(check_ptr(d_logits, "logits"));
+        WQ_TRY(check_ptr(d_topk_weights, "topk_weights"));
+        WQ_TRY(check_ptr(d_topk_ids, "topk_ids"));
+        WQ_TRY(check_dev(d_logits, "logits"));
+        WQ_TRY(check_dev(d_topk_weights, "topk_weights"));
+        WQ_TRY(check_dev(d_topk_ids, "topk_ids"));
+        wq::launch_route(d_logits, M, E, topk, renormalize ? 1 : 0, d_topk_weights, d_topk_ids,
+                         (hipStream_t)stream);
+        return after_launch("moe_route");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_route: unexpected exception");
+    }
+}
+
+wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block_size, int32_t* d_sorted_token_ids,
+                    int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded, size_t capacity, void* stream) {
+    try {
+        WQ_REQUIRE(M >= 0 && topk >= 1 && E >= 1, WQ_ERR_INVALID, "bad sizes M %d topk %d E %d", M, topk, E);
+        WQ_REQUIRE(E <= 1024, WQ_ERR_UNSUPPORTED, "E = %d > 1024", E);
+        WQ_REQUIRE(valid_block_size(block_size), WQ_ERR_UNSUPPORTED, "block_size %d not in {16,32,64,128,256}",
+                   block_size);
+        WQ_REQUIRE((int64_t)M * topk <= MAX_PAIRS, WQ_ERR_UNSUPPORTED, "M*topk > 2^24");
+        const size_t need = moe_align_capacity(M, topk, E, block_size);
+        WQ_REQUIRE(capacity >= need, WQ_ERR_INVALID, "capacity %zu < required %zu", capacity, need);
+        WQ_REQUIRE(capacity % (size_t)block_size == 0, WQ_ERR_INVALID, "capacity not a multiple of block_size");
+        WQ_REQUIRE(capacity <= (size_t)0x7fffffff, WQ_ERR_UNSUPPORTED, "capacity too large");
+        if (M > 0) WQ_TRY(check_ptr(d_topk_ids, "topk_ids"));
+        WQ_TRY(check_ptr(d_sorted_token_ids, "sorted_token_ids"));
+        WQ_TRY(check_ptr(d_expert_ids, "expert_ids"));
+        WQ_TRY(check_ptr(d_num_tokens_post_padded, "num_tokens_post_padded"));
+        if (M > 0) WQ_TRY(check_dev(d_topk_ids, "topk_ids"));
+        WQ_TRY(check_dev(d_sorted_token_ids, "sorted_token_ids"));
+        WQ_TRY(check_dev(d_expert_ids, "expert_ids"));
+        WQ_TRY(check_dev(d_num_tokens_post_padded, "num_tokens_post_padded"));
+        wq::launch_align(d_topk_ids, M * topk, E, block_size, d_sorted_token_ids, d_expert_ids,
+                         d_num_tokens_post_padded, (int)capacity, (hipStream_t)stream);
+        return after_launch("moe_align");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_align: unexpected exception");
+    }
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int n_out, int k_in, size_t capacity, int act_order) {
+    if (M < 0 || topk <= 0 || n_out <= 0 || k_in <= 0) return 0;
+    size_t b = 0;
+    if ((stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_RAW) && act_order) b += round256(capacity * k_in * 2);
+    if (stage == WQ_STAGE_DOWN) b += round256((size_t)M * topk * n_out * sizeof(float));
+    return b;
+}
+
+static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, const char* who) {
+    WQ_REQUIRE(d != nullptr, WQ_ERR_INVALID, "%s: desc is NULL", who);
+    WQ_REQUIRE(d->struct_size >= sizeof(wq_moe_gemm_desc), WQ_ERR_INVALID, "%s: struct_size %zu < %zu", who,
+               d->struct_size, sizeof(wq_moe_gemm_desc));
+    const int stage = d->stage;
+    WQ_REQUIRE(stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_DOWN || stage == WQ_STAGE_RAW, WQ_ERR_INVALID,
+               "%s: bad stage %d", who, stage);
+    WQ_REQUIRE(d->act_dtype == WQ_F16 || d->act_dtype == WQ_BF16, WQ_ERR_INVALID, "%s: bad act dtype", who);
+    if (wbits == 4) WQ_REQUIRE(d->act_dtype == WQ_F16, WQ_ERR_UNSUPPORTED, "%s: int4 path takes fp16 activations", who);
+    WQ_REQUIRE(d->M >= 0 && d->topk >= 1 && d->E >= 1 && d->topk <= d->E, WQ_ERR_INVALID,
+               "%s: bad M/topk/E (%d/%d/%d)", who, d->M, d->topk, d->E);
+    WQ_REQUIRE(d->E <= 1024, WQ_ERR_UNSUPPORTED, "%s: E > 1024", who);
+    WQ_REQUIRE((int64_t)d->M * d->topk <= MAX_PAIRS, WQ_ERR_UNSUPPORTED, "%s: M*topk > 2^24", who);
+    WQ_REQUIRE(d->n_out > 0 && d->k_in > 0, WQ_ERR_INVALID, "%s: bad n_out/k_in", who);
+    const int kchunk = wbits == 4 ? wq::WFmt<4>::KCHUNK : wq::WFmt<8>::KCHUNK;
+    WQ_REQUIRE(d->k_in % kchunk == 0, WQ_ERR_UNSUPPORTED, "%s: k_in %d not a multiple of %d", who, d->k_in, kchunk);
+    WQ_REQUIRE(d->n_out % (stage == WQ_STAGE_GATE_UP ? 32 : 16) == 0, WQ_ERR_UNSUPPORTED,
+               "%s: n_out %d not a multiple of %d", who, d->n_out, stage == WQ_STAGE_GATE_UP ? 32 : 16);
+    if (wbits == 4)
+        WQ_REQUIRE(d->group_size == 128 || d->group_size == -1, WQ_ERR_UNSUPPORTED, "%s: group_size %d", who,
+                   d->group_size);
+    else
+        WQ_REQUIRE(d->group_size == -1, WQ_ERR_UNSUPPORTED, "%s: int8 weights take per-column scales (-1)", who);
+    WQ_REQUIRE(valid_block_size(d->block_size), WQ_ERR_UNSUPPORTED, "%s: block_size %d", who, d->block_size);
+    const size_t need_cap = moe_align_capacity(d->M, d->topk, d->E, d->block_size);
+    WQ_REQUIRE(d->capacity >= need_cap && d->capacity % (size_t)d->block_size == 0 &&
+                   d->capacity <= (size_t)0x7fffffff,
+               WQ_ERR_INVALID, "%s: capacity %zu (need >= %zu, multiple of block_size)", who, d->capacity, need_cap);
+    const bool act_order = d->d_k_perm != nullptr;
+    WQ_REQUIRE(!act_order || (wbits == 4 && stage != WQ_STAGE_DOWN), WQ_ERR_INVALID,
+               "%s: k_perm only applies to int4 GATE_UP/RAW", who);
+    const size_t ws = moe_gemm_workspace_bytes(stage, d->M, d->topk, d->n_out, d->k_in, d->capacity, act_order);
+    WQ_REQUIRE(d->workspace_bytes >= ws, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who, d->workspace_bytes,
+               ws);
+    if (d->M == 0) return ok();
+    WQ_TRY(check_ptr(d->d_a, "a"));
+    WQ_TRY(check_ptr(d->d_w_packed, "w_packed"));
+    WQ_TRY(check_ptr(d->d_scales, "scales"));
+    WQ_TRY(check_ptr(d->d_sorted_token_ids, "sorted_token_ids"));
+    WQ_TRY(check_ptr(d->d_expert_ids, "expert_ids"));
+    WQ_TRY(check_ptr(d->d_num_tokens_post_padded, "num_tokens_post_padded"));
+    WQ_TRY(check_ptr(d->d_out, "out"));
+    if (act_order) WQ_TRY(check_ptr(d->d_k_perm, "k_perm"));
+    if (stage == WQ_STAGE_DOWN) WQ_TRY(check_ptr(d->d_topk_weights, "topk_weights"));
+    if (ws) WQ_TRY(check_ptr(d->d_workspace, "workspace"));
+
+    WQ_TRY(check_dev(d->d_a, "a"));
+    WQ_TRY(check_dev(d->d_w_packed, "w_packed"));
+    WQ_TRY(check_dev(d->d_scales, "scales"));
+    WQ_TRY(check_dev(d->d_sorted_token_ids, "sorted_token_ids"));
+    WQ_TRY(check_dev(d->d_expert_ids, "expert_ids"));
+    WQ_TRY(check_dev(d->d_num_tokens_post_padded, "num_tokens_post_padded"));
+    WQ_TRY(check_dev(d->d_out, "out"));
+    if (act_order) WQ_TRY(check_dev(d->d_k_perm, "k_perm"));
+    if (stage == WQ_STAGE_DOWN) WQ_TRY(check_dev(d->d_topk_weights, "topk_weights"));
+    if (ws) WQ_TRY(check_dev(d->d_workspace, "workspace"));
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = d->act_dtype == WQ_BF16;
+    wq::GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(d->d_a);
+    g.w = static_cast<const uint8_t*>(d->d_w_packed);
+    g.s = static_cast<const uint16_t*>(d->d_scales);
+    g.sorted = d->d_sorted_token_ids;
+    g.expert_ids = d->d_expert_ids;
+    g.ntpp = d->d_num_tokens_post_padded;
+    g.topk_w = d->d_topk_weights;
+    g.out = d->d_out;
+    g.M = d->M;
+    g.topk = d->topk;
+    g.E = d->E;
+    g.n_out = d->n_out;
+    g.k_in = d->k_in;
+    g.block_size = d->block_size;
+    g.groups = (wbits == 4 && d->group_size == 128) ? d->k_in / 128 : 1;
+    g.a_direct = (stage == WQ_STAGE_DOWN) ? 1 : 0;
+    g.cap = (int)d->capacity;
+
+    if (act_order) {
+        uint16_t* a1 = static_cast<uint16_t*>(d->d_workspace);
+        wq::launch_gather_perm(g.a, d->d_k_perm, g.sorted, g.expert_ids, g.ntpp, d->M, d->topk, d->k_in,
+                               d->block_size, g.cap, a1, s);
+        WQ_TRY(after_launch(who));
+        g.a = a1;
+        g.a_direct = 1;
+    }
+    float* y = nullptr;
+    if (stage == WQ_STAGE_DOWN) {
+        y = static_cast<float*>(d->d_workspace);
+        g.out = y;
+    }
+    const bool prefill = (d->block_size % 128 == 0) && (d->n_out % 128 == 0);
+    if (prefill) wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
+    else wq::launch_gemm_decode(wbits, bf16, stage, g, s);
+    WQ_TRY(after_launch(who));
+    if (stage == WQ_STAGE_DOWN) {
+        wq::launch_combine(y, d->M, d->topk, d->n_out, bf16, static_cast<uint16_t*>(d->d_out), s);
+        WQ_TRY(after_launch(who));
+    }
+    return ok();
+}
+
+wq_status moe_w4a16_gemm(const wq_moe_gemm_desc* d, void* stream) {
+    try {
+        return moe_gemm(d, 4, stream, "moe_w4a16_gemm");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_w4a16_gemm: unexpected exception");
+    }
+}
+
+wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream) {
+    try {
+        return moe_gemm(d, 8, stream, "moe_w8a16_gemm");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_w8a16_gemm: unexpected exception");
+    }
+}
+
+wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
+                              const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream) {
+    try {
+        WQ_REQUIRE(M >= 0 && K > 0 && N > 0, WQ_ERR_INVALID, "sparse24: bad sizes M %d K %d N %d", M, K, N);
+        WQ_REQUIRE(act_dtype == WQ_F16, WQ_ERR_UNSUPPORTED, "sparse24: fp16 activations only");
+        WQ_REQUIRE(group_size == 128, WQ_ERR_UNSUPPORTED, "sparse24: group_size %d (128 only)", group_size);
+        WQ_REQUIRE(K % 256 == 0, WQ_ERR_UNSUPPORTED, "sparse24: K %d not a multiple of 256", K);
+        WQ_REQUIRE(N % 16 == 0, WQ_ERR_UNSUPPORTED, "sparse24: N %d not a multiple of 16", N);
+        WQ_REQUIRE(N / 16 <= 0x7fffffff && (M + 63) / 64 <= 65535, WQ_ERR_UNSUPPORTED, "sparse24: M too large");
+        if (M == 0) return ok();
+        WQ_TRY(check_ptr(d_x, "x"));
+        WQ_TRY(check_ptr(d_vals, "vals"));
+        WQ_TRY(check_ptr(d_meta, "meta"));
+        WQ_TRY(check_ptr(d_scales, "scales"));
+        WQ_TRY(check_ptr(d_y, "y"));
+        WQ_TRY(check_dev(d_x, "x"));
+        WQ_TRY(check_dev(d_vals, "vals"));
+        WQ_TRY(check_dev(d_meta, "meta"));
+        WQ_TRY(check_dev(d_scales, "scales"));
+        WQ_TRY(check_dev(d_y, "y"));
+        wq::launch_sparse24(static_cast<const uint16_t*>(d_x), M, K, N, static_cast<const uint8_t*>(d_vals),
+                            static_cast<const uint8_t*>(d_meta), static_cast<const uint16_t*>(d_scales),
+                            static_cast<uint16_t*>(d_y), (hipStream_t)stream);
+        return after_launch("sparse24_w4a16_gemm");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "sparse24: unexpected exception");
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Offline packers
+// ---------------------------------------------------------------------------
+size_t wq_pack_w4_bytes(int E, int n_out, int k_in) {
+    if (E <= 0 || n_out <= 0 || k_in <= 0 || n_out % 16 || k_in % 128) return 0;
+    return (size_t)E * n_out * k_in / 2;
+}
+
+size_t wq_pack_w8_bytes(int E, int n_out, int k_in) {
+    if (E <= 0 || n_out <= 0 || k_in <= 0 || n_out % 16 || k_in % 64) return 0;
+    return (size_t)E * n_out * k_in;
+}
+
+// canonical row held by packed row p of expert e
+static inline int logical_row(int p, int n_out, bool interleave, const int32_t* perm_e) {
+    if (!interleave) return perm_e ? perm_e[p] : p;
+    const int t = p / 16, j = t / 2, half = t % 2, within = p % 16;
+    int lr = 16 * j + within;
+    if (perm_e) lr = perm_e[lr];
+    return half * (n_out / 2) + lr;
+}
+
+static wq_status check_row_perm(int E, int n, const int32_t* perm) {
+    if (!perm) return WQ_OK;
+    std::vector<char> seen((size_t)n);
+    for (int e = 0; e < E; ++e) {
+        std::fill(seen.begin(), seen.end(), 0);
+        for (int i = 0; i < n; ++i) {
+            const int32_t v = perm[(size_t)e * n + i];
+            WQ_REQUIRE(v >= 0 && v < n && !seen[v], WQ_ERR_INVALID, "row_perm of expert %d is not a permutation", e);
+            seen[v] = 1;
+        }
+    }
+    return WQ_OK;
+}
+
+wq_status wq_pack_w4(int E, int n_out, int k_in, const int8_t* q, const uint16_t* scales, int group_size,
+                     const int32_t* g_idx, const int32_t* row_perm, int flags, void* packed, uint16_t* scales_packed,
+                     int32_t* k_perm) {
+    try {
+        WQ_REQUIRE(E > 0 && n_out > 0 && k_in > 0, WQ_ERR_INVALID, "pack_w4: bad sizes");
+        const bool il = (flags & WQ_PACK_INTERLEAVE_GATE_UP) != 0;
+        WQ_REQUIRE(n_out % (il ? 32 : 16) == 0, WQ_ERR_UNSUPPORTED, "pack_w4: n_out %d", n_out);
+        WQ_REQUIRE(k_in % 128 == 0, WQ_ERR_UNSUPPORTED, "pack_w4: k_in %d not a multiple of 128", k_in);
+        WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "pack_w4: group_size %d", group_size);
+        WQ_REQUIRE(q && scales && packed && scales_packed, WQ_ERR_INVALID, "pack_w4: NULL buffer");
+        WQ_REQUIRE(!g_idx || (group_size == 128 && k_perm), WQ_ERR_INVALID,
+                   "pack_w4: act-order needs group_size 128 and a k_perm output");
+        const int G = group_size == -1 ? 1 : k_in / group_size;
+        WQ_TRY(check_row_perm(E, il ? n_out / 2 : n_out, row_perm));
+        const int rows_perm = il ? n_out / 2 : n_out;
+        // input-channel order: stable sort by group
+        std::vector<int32_t> sig((size_t)E * k_in);
+        for (int e = 0; e < E; ++e) {
+            int32_t* s = sig.data() + (size_t)e * k_in;
+            if (!g_idx) {
+                for (int k = 0; k < k_in; ++k) s[k] = k;
+                continue;
+            }
+            const int32_t* gi = g_idx + (size_t)e * k_in;
+            std::vector<int> cnt(G, 0);
+            for (int k = 0; k < k_in; ++k) {
+                WQ_REQUIRE(gi[k] >= 0 && gi[k] < G, WQ_ERR_INVALID, "pack_w4: g_idx out of range (expert %d)", e);
+                cnt[gi[k]]++;
+            }
+            for (int gg = 0; gg < G; ++gg)
+                WQ_REQUIRE(cnt[gg] == group_size, WQ_ERR_UNSUPPORTED,
+                           "pack_w4: act-order group %d of expert %d has %d channels, not %d", gg, e, cnt[gg],
+                           group_size);
+            std::vector<int> pos(G);
+            for (int gg = 0; gg < G; ++gg) pos[gg] = gg * group_size;
+            for (int k = 0; k < k_in; ++k) s[pos[gi[k]]++] = k;
+        }
+        // value range
+        for (size_t i = 0, n = (size_t)E * n_out * k_in; i < n; ++i)
+            WQ_REQUIRE(q[i] >= -8 && q[i] <= 7, WQ_ERR_INVALID, "pack_w4: code %d out of [-8, 7]", (int)q[i]);
+        if (k_perm) std::memcpy(k_perm, sig.data(), sizeof(int32_t) * sig.size());
+
+        const int C = k_in / 128;
+        const size_t expert_bytes = (size_t)n_out * k_in / 2;
+        uint8_t* out = static_cast<uint8_t*>(packed);
+        parallel_for(E * (n_out / 16), [&](int job) {
+            const int e = job / (n_out / 16), t = job % (n_out / 16);
+            const int32_t* pe = row_perm ? row_perm + (size_t)e * rows_perm : nullptr;
+            const int32_t* s = sig.data() + (size_t)e * k_in;
+            for (int l = 0; l < 64; ++l) {
+                const int p = t * 16 + (l & 15);
+                const int lr = logical_row(p, n_out, il, pe);
+                const int8_t* qr = q + ((size_t)e * n_out + lr) * k_in;
+                for (int c = 0; c < C; ++c) {
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(out + (size_t)e * expert_bytes +
+                                                                (((size_t)t * C + c) * 64 + l) * 16);
+                    for (int st = 0; st < 4; ++st) {
+                        uint32_t d = 0;
+                        for (int j = 0; j < 8; ++j) {
+                            const int kp = 128 * c + 32 * st + 8 * (l >> 4) + j;
+                            const uint32_t u = (uint32_t)(qr[s[kp]] + 8);
+                            d |= u << (4 * (j >> 1) + 16 * (j & 1));
+                        }
+                        dst[st] = d;
+                    }
+                }
+            }
+            if (t == 0) {
+                for (int gg = 0; gg < G; ++gg)
+                    for (int pp = 0; pp < n_out; ++pp)
+                        scales_packed[((size_t)e * G + gg) * n_out + pp] =
+                            scales[((size_t)e * G + gg) * n_out + logical_row(pp, n_out, il, pe)];
+            }
+        });
+        return ok();
+    } catch (...) {
+        return fail(WQ_ERR_INVALID, "pack_w4: unexpected exception");
+    }
+}
+
+wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t* scales, const int32_t* row_perm,
+                     int flags, void* packed, uint16_t* scales_packed) {
+    try {
+        WQ_REQUIRE(E > 0 && n_out > 0 && k_in > 0, WQ_ERR_INVALID, "pack_w8: bad sizes");
+        const bool il = (flags & WQ_PACK_INTERLEAVE_GATE_UP) != 0;
+        WQ_REQUIRE(n_out % (il ? 32 : 16) == 0, WQ_ERR_UNSUPPORTED, "pack_w8: n_out %d", n_out);
+        WQ_REQUIRE(k_in % 64 == 0, WQ_ERR_UNSUPPORTED, "pack_w8: k_in %d not a multiple of 64", k_in);
+        WQ_REQUIRE(q && scales && packed && scales_packed, WQ_ERR_INVALID, "pack_w8: NULL buffer");
+        const int rows_perm = il ? n_out / 2 : n_out;
+        WQ_TRY(check_row_perm(E, rows_perm, row_perm));
+        const int C = k_in / 64;
+        const size_t expert_bytes = (size_t)n_out * k_in;
+        uint8_t* out = static_cast<uint8_t*>(packed);
+        parallel_for(E * (n_out / 16), [&](int job) {
+            const int e = job / (n_out / 16), t = job % (n_out / 16);
+            const int32_t* pe = row_perm ? row_perm + (size_t)e * rows_perm : nullptr;
+            for (int l = 0; l < 64; ++l) {
+                const int p = t * 16 + (l & 15);
+                const int lr = logical_row(p, n_out, il, pe);
+                const int8_t* qr = q + ((size_t)e * n_out + lr) * k_in;
+                for (int c = 0; c < C; ++c) {
+                    uint8_t* dst = out + (size_t)e * expert_bytes + (((size_t)t * C + c) * 64 + l) * 16;
+                    for (int st = 0; st < 2; ++st)
+                        for (int j = 0; j < 8; ++j)
+                            dst[8 * st + j] = (uint8_t)((int)qr[64 * c + 32 * st + 8 * (l >> 4) + j] + 128);
+                }
+            }
+            if (t == 0)
+                for (int pp = 0; pp < n_out; ++pp)
+                    scales_packed[(size_t)e * n_out + pp] = scales[(size_t)e * n_out + logical_row(pp, n_out, il, pe)];
+        });
+        return ok();
+    } catch (...) {
+        return fail(WQ_ERR_INVALID, "pack_w8: unexpected exception");
+    }
+}
+
+size_t wq_pack_sparse24_vals_bytes(int N, int K) {
+    if (N <= 0 || K <= 0 || N % 16 || K % 256) return 0;
+    return (size_t)N * K / 4;
+}
+
+size_t wq_pack_sparse24_meta_bytes(int N, int K) {
+    if (N <= 0 || K <= 0 || N % 16 || K % 256) return 0;
+    return (size_t)N * K / 8;
+}
+
+wq_status wq_pack_sparse24(int N, int K, const int8_t* vals, const uint8_t* idx, const uint16_t* scales,
+                           void* vals_packed, void* meta_packed, uint16_t* scales_packed) {
+    try {
+        WQ_REQUIRE(N > 0 && K > 0, WQ_ERR_INVALID, "pack_sparse24: bad sizes");
+        WQ_REQUIRE(N % 16 == 0 && K % 256 == 0, WQ_ERR_UNSUPPORTED, "pack_sparse24: need N %% 16 == 0, K %% 256 == 0");
+        WQ_REQUIRE(vals && idx && scales && vals_packed && meta_packed && scales_packed, WQ_ERR_INVALID,
+                   "pack_sparse24: NULL buffer");
+        const size_t half = (size_t)N * K / 2;
+        for (size_t i = 0; i < half; i += 2) {
+            WQ_REQUIRE(vals[i] >= -8 && vals[i] <= 7 && vals[i + 1] >= -8 && vals[i + 1] <= 7, WQ_ERR_INVALID,
+                       "pack_sparse24: code out of [-8, 7]");
+            WQ_REQUIRE(idx[i] < idx[i + 1] && idx[i + 1] <= 3, WQ_ERR_INVALID,
+                       "pack_sparse24: keep positions must be ascending in 0..3");
+        }
+        const int C = K / 256;
+        uint8_t* vo = static_cast<uint8_t*>(vals_packed);
+        uint8_t* mo = static_cast<uint8_t*>(meta_packed);
+        parallel_for(N / 16, [&](int t) {
+            for (int l = 0; l < 64; ++l) {
+                const int n = t * 16 + (l & 15);
+                const int8_t* vr = vals + (size_t)n * (K / 2);
+                const uint8_t* ir = idx + (size_t)n * (K / 2);
+                for (int c = 0; c < C; ++c) {
+                    uint32_t* vd = reinterpret_cast<uint32_t*>(vo + (((size_t)t * C + c) * 64 + l) * 16);
+                    uint16_t* md = reinterpret_cast<uint16_t*>(mo + (((size_t)t * C + c) * 64 + l) * 8);
+                    for (int st = 0; st < 4; ++st) {
+                        const int g4 = (256 * c + 64 * st + 16 * (l >> 4)) / 4;  // first group of 4 of this lane
+                        uint32_t d = 0;
+                        uint32_t m = 0;
+                        for (int b = 0; b < 4; ++b) {
+                            for (int h = 0; h < 2; ++h) {
+                                const int j = 2 * b + h;
+                                const size_t v = (size_t)2 * (g4 + b) + h;
+                                d |= (uint32_t)(vr[v] + 8) << (4 * (j >> 1) + 16 * (j & 1));
+                                m |= (uint32_t)ir[v] << (4 * b + 2 * h);
+                            }
+                        }
+                        vd[st] = d;
+                        md[st] = (uint16_t)m;
+                    }
+                }
+            }
+        });
+        std::memcpy(scales_packed, scales, sizeof(uint16_t) * (size_t)(K / 128) * N);
+        return ok();
+    } catch (...) {
+        return fail(WQ_ERR_INVALID, "pack_sparse24: unexpected exception");
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,323 @@
+// gemm_decode.hip -- small-batch grouped GEMM of the quantized MoE layer.
+//
+// Work unit: one workgroup per (expert e, 16 weight rows) -- 32 rows for the
+// fused gate/up stage, a gate tile and the matching up tile.  The weights are
+// the MFMA A operand (16 rows x 32 input channels per v_mfma_f32_16x16x32),
+// streamed once from HBM with 128-bit loads: a packed 1 KiB chunk gives every
+// lane 16 bytes, i.e. 4 MFMA k-steps of int4 or 2 of int8.  The token rows of
+// the expert (16 per MFMA, B operand) come from L2.  The four waves split the
+// input channels and meet in LDS; one pass covers up to RMAX 16-row token
+// blocks, so the weights are read once for all of them.  Dequantisation is
+// in registers: int4 -> fp16 by exponent bits, group scale folded in fp32 per
+// 128-channel chunk; int8 -> bf16/fp16 exactly, per-column scale in the fp32
+// epilogue.  Epilogues: SiLU(gate)*up to H (sorted rows), or the routed weight
+// times the down projection to the per-pair buffer Y.
+//
+// Sources: int4 GPTQ group-128 experts ("Marlin moe integration", nm-vllm PR
+// 266, opening description); per-column int8 experts cast to the activation
+// type inside the kernel ("[Kernel] W8A16 Int8 inside FusedMoE", vLLM PR 7415,
+// opening description); small-batch kernels chosen by batch size ("[WIP] AWQ
+// Faster Kernels", vLLM issue 3289, the GEMV/GEMM mix and the batch-dimension
+// heuristics).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace wq {
+
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+
+template <int WBITS, bool BF16, int STAGE, int RMAX>
+__global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
+    constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 : 1;
+    constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
+    constexpr int KSTEPS = KCHUNK / 32;
+    static_assert(RMAX <= DEC_WAVES, "one wave per token block in the epilogue");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int unit = blockIdx.x;
+    const int e = blockIdx.y;
+    const int T = g.M * g.topk;
+    const int BS = g.block_size;
+
+    // this expert's blocks: expert_ids is non-decreasing over the used blocks
+    const int nbu = *g.ntpp / BS;
+    const int b0 = lower_bound_i32(g.expert_ids, 0, nbu, e);
+    const int b1 = lower_bound_i32(g.expert_ids, b0, nbu, e + 1);
+    if (b0 >= b1) return;
+    const int spb = BS / 16;
+    const int sb_first = b0 * spb;
+    int q = 0;  // live 16-row sub-blocks of the last block (its first row is a real pair)
+    while (q < spb && g.sorted[(b1 - 1) * BS + q * 16] < T) ++q;
+    const int S = (b1 - 1 - b0) * spb + q;
+
+    const int C = g.k_in / KCHUNK;
+    const size_t expert_bytes = (size_t)(g.n_out / TILE_ROWS) * C * CHUNK_BYTES;
+    const uint8_t* wt[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        wt[t] = g.w + (size_t)e * expert_bytes + (size_t)(NT * unit + t) * C * CHUNK_BYTES + lane * 16;
+    const uint16_t* se = g.s + (size_t)e * g.groups * g.n_out;
+    const int rowq = 4 * (lane >> 4);  // first of this lane's 4 output rows in a tile
+    constexpr bool GROUPED = (WBITS == 4);
+    const bool grouped = GROUPED && g.groups > 1;
+
+    __shared__ f32x4 red[DEC_WAVES][NT][RMAX][64];
+
+    for (int s0 = 0; s0 < S; s0 += RMAX) {
+        const int R = min(RMAX, S - s0);
+        const uint16_t* arow[RMAX];
+        bool avalid[RMAX];
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) {
+            avalid[r] = false;
+            arow[r] = g.a;
+            if (r < R) {
+                const int p = (sb_first + s0 + r) * 16 + (lane & 15);
+                const int pair = g.sorted[p];
+                avalid[r] = pair < T;
+                const int row = g.a_direct ? p : (avalid[r] ? pair / g.topk : 0);
+                arow[r] = g.a + (size_t)row * g.k_in + 8 * (lane >> 4);
+            }
+        }
+
+        f32x4 acc[NT][RMAX];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        u32x4 wA[NT], wB[NT];
+        u32x4 xA[RMAX][KSTEPS], xB[RMAX][KSTEPS];
+        u32x2 sA[NT], sB[NT];
+
+        auto load = [&](int c, u32x4(&wv)[NT], u32x4(&xv)[RMAX][KSTEPS], u32x2(&sv)[NT]) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) wv[t] = ldg128_stream(wt[t] + (size_t)c * CHUNK_BYTES);
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r)
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s)
+                    xv[r][s] = (r < R && avalid[r]) ? ldg128(arow[r] + c * KCHUNK + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+            if (grouped) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    sv[t] = *reinterpret_cast<const u32x2*>(se + (size_t)c * g.n_out + (NT * unit + t) * TILE_ROWS +
+                                                            rowq);
+            }
+        };
+
+        auto compute = [&](const u32x4(&wv)[NT], const u32x4(&xv)[RMAX][KSTEPS], const u32x2(&sv)[NT]) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (WBITS == 4) {
+                    f32x4 part[RMAX];
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) part[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KSTEPS; ++s) {
+                        const u32x4 a = dequant_w4_f16(wv[t][s]);
+#pragma unroll
+                        for (int r = 0; r < RMAX; ++r)
+                            if (r < R) part[r] = mfma16x16x32<false>(a, xv[r][s], part[r]);
+                    }
+                    if (grouped) {
+                        const float s0f = f16_to_f32((uint16_t)(sv[t][0] & 0xffffu));
+                        const float s1f = f16_to_f32((uint16_t)(sv[t][0] >> 16));
+                        const float s2f = f16_to_f32((uint16_t)(sv[t][1] & 0xffffu));
+                        const float s3f = f16_to_f32((uint16_t)(sv[t][1] >> 16));
+#pragma unroll
+                        for (int r = 0; r < RMAX; ++r) {
+                            acc[t][r][0] += part[r][0] * s0f;
+                            acc[t][r][1] += part[r][1] * s1f;
+                            acc[t][r][2] += part[r][2] * s2f;
+                            acc[t][r][3] += part[r][3] * s3f;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < RMAX; ++r) acc[t][r] += part[r];
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < KSTEPS; ++s) {
+                        const u32x4 a = dequant_w8x8<BF16>(wv[t][2 * s], wv[t][2 * s + 1]);
+#pragma unroll
+                        for (int r = 0; r < RMAX; ++r)
+                            if (r < R) acc[t][r] = mfma16x16x32<BF16>(a, xv[r][s], acc[t][r]);
+                    }
+                }
+            }
+        };
+
+        // split-K over the waves, two chunks in flight per wave (ping-pong)
+        int c = wave;
+        if (c < C) load(c, wA, xA, sA);
+        while (c < C) {
+            const int c1 = c + DEC_WAVES;
+            if (c1 < C) load(c1, wB, xB, sB);
+            compute(wA, xA, sA);
+            if (c1 >= C) break;
+            const int c2 = c1 + DEC_WAVES;
+            if (c2 < C) load(c2, wA, xA, sA);
+            compute(wB, xB, sB);
+            c = c2;
+        }
+
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) red[wave][t][r][lane] = acc[t][r];
+        __syncthreads();
+
+        if (wave < R) {
+            const int r = wave;
+            f32x4 v[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                v[t] = red[0][t][r][lane];
+#pragma unroll
+                for (int w = 1; w < DEC_WAVES; ++w) v[t] += red[w][t][r][lane];
+            }
+            const int p = (sb_first + s0 + r) * 16 + (lane & 15);
+            const int pair = g.sorted[p];
+            if constexpr (STAGE == STAGE_GATE_UP) {
+                const int N = g.n_out / 2;
+                float h[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float gt = v[0][i], up = v[1][i];
+                    if (!grouped) {
+                        gt *= act_to_f32<BF16>(se[(2 * unit) * TILE_ROWS + rowq + i]);
+                        up *= act_to_f32<BF16>(se[(2 * unit + 1) * TILE_ROWS + rowq + i]);
+                    }
+                    h[i] = silu_f32(gt) * up;
+                }
+                u32x2 st;
+                st[0] = (uint32_t)f32_to_act<BF16>(h[0]) | ((uint32_t)f32_to_act<BF16>(h[1]) << 16);
+                st[1] = (uint32_t)f32_to_act<BF16>(h[2]) | ((uint32_t)f32_to_act<BF16>(h[3]) << 16);
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (size_t)p * N + unit * TILE_ROWS + rowq) =
+                    st;
+            } else {
+                if (pair < T) {
+                    f32x4 o = v[0];
+                    if (!grouped) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[i] *= act_to_f32<BF16>(se[unit * TILE_ROWS + rowq + i]);
+                    }
+                    if constexpr (STAGE == STAGE_DOWN) o *= g.topk_w[pair];
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (size_t)pair * g.n_out +
+                                              unit * TILE_ROWS + rowq) = o;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if constexpr (STAGE == STAGE_GATE_UP) {
+        // H rows of all-pad sub-blocks (only with blocks larger than 16) are zero
+        const int N = g.n_out / 2;
+        const int p_lo = (sb_first + S) * 16;
+        const int p_hi = b1 * BS;
+        for (int k = threadIdx.x; k < (p_hi - p_lo) * TILE_ROWS; k += DEC_THREADS) {
+            const int p = p_lo + k / TILE_ROWS;
+            static_cast<uint16_t*>(g.out)[(size_t)p * N + unit * TILE_ROWS + (k % TILE_ROWS)] = 0;
+        }
+    }
+}
+
+template <int WBITS, bool BF16, int STAGE>
+static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
+    constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 : 1;
+    const dim3 grid(g.n_out / (TILE_ROWS * NT), g.E);
+    const int T = g.M * g.topk;
+    const int sub = (T + 15) / 16;  // most 16-row sub-blocks any expert can fill
+    if (sub <= 1)
+        hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, 1>), grid, dim3(DEC_THREADS), 0, s, g);
+    else if (sub <= 2)
+        hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, 2>), grid, dim3(DEC_THREADS), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, 4>), grid, dim3(DEC_THREADS), 0, s, g);
+}
+
+template <int WBITS, bool BF16>
+static void launch_decode_s(int stage, const GemmArgs& g, hipStream_t s) {
+    if (stage == STAGE_GATE_UP) launch_decode_r<WBITS, BF16, STAGE_GATE_UP>(g, s);
+    else if (stage == STAGE_DOWN) launch_decode_r<WBITS, BF16, STAGE_DOWN>(g, s);
+    else launch_decode_r<WBITS, BF16, STAGE_RAW>(g, s);
+}
+
+void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s) {
+    if (wbits == 4) launch_decode_s<4, false>(stage, g, s);  // int4: fp16 activations
+    else if (bf16) launch_decode_s<8, true>(stage, g, s);
+    else launch_decode_s<8, false>(stage, g, s);
+}
+
+// ---------------------------------------------------------------------------
+// act-order gather: A1[p, k'] = x[token(p), perm[e(p), k']], zero rows for pads
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_perm_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ sorted,
+                                                          const int32_t* __restrict__ expert_ids,
+                                                          const int32_t* __restrict__ ntpp, int topk, int T, int k_in,
+                                                          int BS, uint16_t* __restrict__ a1) {
+    const int p = blockIdx.x;
+    if (p >= *ntpp) return;
+    const int pair = sorted[p];
+    uint16_t* dst = a1 + (size_t)p * k_in;
+    if (pair >= T) {
+        for (int k = threadIdx.x * 8; k < k_in; k += 256 * 8)
+            *reinterpret_cast<u32x4*>(dst + k) = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const int e = expert_ids[p / BS];
+    const uint16_t* src = x + (size_t)(pair / topk) * k_in;
+    const int32_t* pe = perm + (size_t)e * k_in;
+    for (int k = threadIdx.x * 8; k < k_in; k += 256 * 8) {
+        const u32x4 i0 = ldg128(pe + k);
+        const u32x4 i1 = ldg128(pe + k + 4);
+        u32x4 v;
+        v[0] = (uint32_t)src[i0[0]] | ((uint32_t)src[i0[1]] << 16);
+        v[1] = (uint32_t)src[i0[2]] | ((uint32_t)src[i0[3]] << 16);
+        v[2] = (uint32_t)src[i1[0]] | ((uint32_t)src[i1[1]] << 16);
+        v[3] = (uint32_t)src[i1[2]] | ((uint32_t)src[i1[3]] << 16);
+        *reinterpret_cast<u32x4*>(dst + k) = v;
+    }
+}
+
+void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* sorted, const int32_t* expert_ids,
+                        const int32_t* ntpp, int M, int topk, int k_in, int block_size, int cap, uint16_t* a1,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(gather_perm_kernel, dim3(cap), dim3(256), 0, s, x, perm, sorted, expert_ids, ntpp, topk,
+                       M * topk, k_in, block_size, a1);
+}
+
+// ---------------------------------------------------------------------------
+// top-k weighted combine: out[m, c] = sum_{j<topk} Y[m*topk+j, c]  (Y already
+// carries the routed weight), ascending j in fp32, one rounding to act
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int M, int topk, int n,
+                                                      uint16_t* __restrict__ out) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // 4 outputs each
+    const size_t total = (size_t)M * n / 4;
+    if (q >= total) return;
+    const size_t m = q * 4 / n;
+    const int c = (int)(q * 4 % n);
+    f32x4 acc = *reinterpret_cast<const f32x4*>(y + (m * topk) * n + c);
+    for (int j = 1; j < topk; ++j) acc += *reinterpret_cast<const f32x4*>(y + (m * topk + j) * n + c);
+    u32x2 st;
+    st[0] = (uint32_t)f32_to_act<BF16>(acc[0]) | ((uint32_t)f32_to_act<BF16>(acc[1]) << 16);
+    st[1] = (uint32_t)f32_to_act<BF16>(acc[2]) | ((uint32_t)f32_to_act<BF16>(acc[3]) << 16);
+    *reinterpret_cast<u32x2*>(out + m * n + c) = st;
+}
+
+void launch_combine(const float* y, int M, int topk, int n, bool bf16, uint16_t* out, hipStream_t s) {
+    const size_t total = (size_t)M * n / 4;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, y, M, topk, n, out);
+    else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, y, M, topk, n, out);
+}
+
+}  // namespace wq

@@ -1,0 +1,61 @@
+// launch.hpp -- internal launchers shared between the kernel translation units
+// and the C ABI layer.  Arguments are validated by the caller (abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wq {
+
+constexpr int STAGE_GATE_UP = 0;
+constexpr int STAGE_DOWN = 1;
+constexpr int STAGE_RAW = 2;
+
+// Packed weight geometry: tiles of 16 output rows; a chunk of one tile holds
+// 64 lanes x 16 bytes = 1 KiB and spans KCHUNK input channels.
+constexpr int TILE_ROWS = 16;
+constexpr int CHUNK_BYTES = 1024;
+template <int WBITS>
+struct WFmt {
+    static constexpr int KCHUNK = WBITS == 4 ? 128 : 64;
+};
+
+void launch_route(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids,
+                  hipStream_t s);
+void launch_align(const int32_t* ids, int T, int E, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp,
+                  int cap, hipStream_t s);
+
+struct GemmArgs {
+    const uint16_t* a;        // activations (x, gathered x, or H), 16-bit
+    const uint8_t* w;         // packed weights, all experts
+    const uint16_t* s;        // packed scales, all experts
+    const int32_t* sorted;    // sorted_token_ids
+    const int32_t* expert_ids;
+    const int32_t* ntpp;
+    const float* topk_w;      // DOWN
+    void* out;                // H (act) / Y (f32) / Z (f32)
+    int M, topk, E, n_out, k_in;
+    int block_size;
+    int groups;               // scale groups along k_in (1 = per column)
+    int a_direct;             // 1: A row = sorted position; 0: A row = token of the pair
+    int cap;
+};
+
+// small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
+// across its waves, all of the expert's 16-row token blocks per pass
+void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
+// large-batch path: 128 x 128 tiles through LDS (block_size % 128 == 0)
+void launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
+
+// act-order: A1[p, k'] = x[token(p), perm[expert(p), k']] for sorted rows p
+void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* sorted, const int32_t* expert_ids,
+                        const int32_t* ntpp, int M, int topk, int k_in, int block_size, int cap, uint16_t* a1,
+                        hipStream_t s);
+// out[m, c] = sum_j Y[m*topk + j, c] (ascending j, fp32), rounded to act
+void launch_combine(const float* y, int M, int topk, int n, bool bf16, uint16_t* out, hipStream_t s);
+
+void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+                     const uint16_t* scales, uint16_t* y, hipStream_t s);
+
+}  // namespace wq

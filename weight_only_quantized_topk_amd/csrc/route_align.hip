@@ -1,0 +1,198 @@
+// route_align.hip -- moe_route (router softmax + top-k) and moe_align (token
+// sort and pad per expert) for gfx950.
+//
+// moe_route: one 64-lane wave per token.  Each lane holds up to 16 logits
+// (E <= 1024).  Top-k is k rounds of a wave-wide arg-max over the experts not
+// yet chosen, comparing (larger logit, then smaller expert index).  The slot
+// weights are exp(l_j - max) / sum, evaluated in double with the sum taken in
+// ascending slot order, rounded once to float.
+//
+// moe_align: one 1024-thread workgroup.  (1) per-expert counts with LDS
+// integer atomics (order-free, hence deterministic); (2) padded exclusive scan
+// over experts, expert_ids and pad/tail sentinels written by the expert's own
+// thread; (3) a stable scatter, 1024 pairs at a time: inside a wave, lanes with
+// the same expert are found with one ballot per expert-id bit and ranked with a
+// popcount of the lower lanes; across the 16 waves, per-wave counts in LDS give
+// each wave its offset.  No LDS atomic decides an order, so the output is the
+// unique stable one.
+// (The token sort is the moe_align_block_size step of "Marlin moe integration",
+// nm-vllm PR 266, review thread on its kernel and its block size of 16.)
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace wq {
+
+constexpr int ROUTE_MAX_PER_LANE = 16;  // E <= 1024
+
+__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+    return va > vb || (va == vb && ea < eb);
+}
+
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int M, int E, int topk,
+                                                    int renormalize, float* __restrict__ w_out,
+                                                    int32_t* __restrict__ ids_out) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const float* l = logits + (size_t)m * E;
+    float v[ROUTE_MAX_PER_LANE];
+    uint32_t avail = 0;  // bit i: slot i of this lane holds a not-yet-chosen expert
+#pragma unroll
+    for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = (e < E) ? l[e] : 0.0f;
+        if (e < E) avail |= 1u << i;
+    }
+    float sel_v = 0.0f;  // lane j < topk ends up holding slot j's logit
+    int sel_e = 0;
+    for (int j = 0; j < topk; ++j) {
+        // lane-local best; ascending i means ascending expert index
+        float bv = 0.0f;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
+            if ((avail >> i) & 1u) {
+                const int e = lane + 64 * i;
+                if (be == 0x7fffffff || better(v[i], e, bv, be)) {
+                    bv = v[i];
+                    be = e;
+                }
+            }
+        }
+        // wave-wide arg-max
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (oe != 0x7fffffff && (be == 0x7fffffff || better(ov, oe, bv, be))) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+        if (lane == j) {
+            sel_v = bv;
+            sel_e = be;
+        }
+    }
+    const double mu = (double)__shfl(sel_v, 0, 64);
+    const double ex = (lane < topk) ? exp((double)sel_v - mu) : 0.0;
+    double denom = 0.0;
+    if (renormalize) {
+        for (int j = 0; j < topk; ++j) denom += __shfl(ex, j, 64);
+    } else {
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i)
+            if (lane + 64 * i < E) part += exp((double)v[i] - mu);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        denom = part;
+    }
+    if (lane < topk) {
+        w_out[(size_t)m * topk + lane] = (float)(ex / denom);
+        ids_out[(size_t)m * topk + lane] = sel_e;
+    }
+}
+
+void launch_route(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids,
+                  hipStream_t s) {
+    hipLaunchKernelGGL(route_kernel, dim3((M + 3) / 4), dim3(256), 0, s, logits, M, E, topk, renormalize, w, ids);
+}
+
+// ---------------------------------------------------------------------------
+constexpr int ALIGN_THREADS = 1024;
+constexpr int ALIGN_WAVES = ALIGN_THREADS / 64;
+
+__global__ __launch_bounds__(ALIGN_THREADS) void align_kernel(const int32_t* __restrict__ ids, int T, int E, int BS,
+                                                              int nbits, int32_t* __restrict__ sorted,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ ntpp, int cap) {
+    extern __shared__ int smem[];
+    int* cnt = smem;            // [E]   counts, later the running write position
+    int* wcnt = smem + E;       // [ALIGN_WAVES][E] per-wave counts of the current chunk
+    __shared__ int wsum[ALIGN_WAVES];
+    __shared__ int total_s;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    for (int e = tid; e < E; e += ALIGN_THREADS) cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < T; i += ALIGN_THREADS) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    // exclusive scan of the padded counts (E <= 1024: one expert per thread)
+    const int c_e = (tid < E) ? cnt[tid] : 0;
+    const int p_e = (c_e + BS - 1) / BS * BS;
+    int incl = p_e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wave_off = 0;
+    for (int w = 0; w < wave; ++w) wave_off += wsum[w];
+    const int o_e = wave_off + incl - p_e;
+    if (tid == ALIGN_THREADS - 1) total_s = wave_off + incl;
+    __syncthreads();
+    const int total = total_s;
+    if (tid < E) {
+        cnt[tid] = o_e;  // running write position
+        for (int b = o_e / BS; b < (o_e + p_e) / BS; ++b) expert_ids[b] = tid;
+        for (int p = o_e + c_e; p < o_e + p_e; ++p) sorted[p] = T;
+    }
+    if (tid == 0) *ntpp = total;
+    for (int p = total + tid; p < cap; p += ALIGN_THREADS) sorted[p] = T;
+    for (int b = total / BS + tid; b < cap / BS; b += ALIGN_THREADS) expert_ids[b] = -1;
+
+    // stable scatter
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < T; base += ALIGN_THREADS) {
+        for (int k = tid; k < ALIGN_WAVES * E; k += ALIGN_THREADS) wcnt[k] = 0;
+        const int i = base + tid;
+        const int e = (i < T) ? ids[i] : -1;
+        const bool valid = (e >= 0 && e < E);
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        __syncthreads();  // wcnt cleared
+        if (valid && rank == 0) wcnt[wave * E + e] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int pos = cnt[e] + rank;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+            sorted[pos] = i;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += ALIGN_THREADS) {
+            int s = 0;
+            for (int w = 0; w < ALIGN_WAVES; ++w) s += wcnt[w * E + x];
+            cnt[x] += s;
+        }
+        __syncthreads();
+    }
+}
+
+void launch_align(const int32_t* ids, int T, int E, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp,
+                  int cap, hipStream_t s) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const size_t lds = sizeof(int) * (size_t)E * (1 + ALIGN_WAVES);
+    if (lds > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&align_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(ALIGN_THREADS), lds, s, ids, T, E, BS, nbits, sorted, expert_ids,
+                       ntpp, cap);
+}
+
+}  // namespace wq

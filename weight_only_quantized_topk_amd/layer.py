@@ -1,0 +1,116 @@
+"""The fused MoE layer composed from the library's calls.
+
+pack_moe() runs the offline packers once (host) and uploads the packed
+weights; fused_moe() runs the hot path on the current stream:
+    moe_route -> moe_align -> GATE_UP (int4/int8 GEMM + SiLU*up) -> DOWN (GEMM x
+    routed weight + top-k combine)
+Python only allocates buffers and passes pointers; every step runs in the
+library's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import ops
+from ._lib import WQ_STAGE_DOWN, WQ_STAGE_GATE_UP
+
+DECODE_BLOCK = 16    # token block of the small-batch kernel
+PREFILL_BLOCK = 128  # token block of the large-batch kernel
+
+
+@dataclass
+class PackedMoE:
+    bits: int
+    E: int
+    K: int          # hidden size (w1 input, w2 output)
+    N: int          # intermediate size
+    group_size: int
+    act: object     # torch dtype of activations and scales
+    w1: object      # packed gate/up weights (device uint8)
+    s1: object      # packed scales (device, act dtype bits)
+    k_perm1: Optional[object]  # act-order input permutation of w1 (device int32) or None
+    w2: object
+    s2: object
+
+    @property
+    def act_code(self) -> int:
+        return ops.act_code(self.act)
+
+
+def pack_moe(bits: int, w1q: np.ndarray, s1_bits: np.ndarray, w2q: np.ndarray, s2_bits: np.ndarray, act,
+             group_size: int = -1, g1: Optional[np.ndarray] = None, g2: Optional[np.ndarray] = None,
+             device="cuda") -> PackedMoE:
+    """Canonical weights (w1q [E,2N,K], s1 [E,G1,2N], w2q [E,K,N], s2 [E,G2,K], optional act-order g_idx) ->
+    device-resident packed layout."""
+    import torch
+    E, n2, K = w1q.shape
+    N = n2 // 2
+    k_perm1 = None
+    if bits == 4:
+        row_perm = None
+        if g2 is not None:
+            w2p, s2p, kp2 = ops.pack_w4(w2q, s2_bits, group_size, g_idx=g2)
+            row_perm = kp2
+        else:
+            w2p, s2p, _ = ops.pack_w4(w2q, s2_bits, group_size)
+        w1p, s1p, kp1 = ops.pack_w4(w1q, s1_bits, group_size, g_idx=g1, row_perm=row_perm, interleave_gate_up=True)
+        if kp1 is not None:
+            k_perm1 = torch.from_numpy(kp1).to(device)
+    elif bits == 8:
+        w1p, s1p = ops.pack_w8(w1q, s1_bits, interleave_gate_up=True)
+        w2p, s2p = ops.pack_w8(w2q, s2_bits)
+    else:
+        raise ValueError("bits must be 4 or 8")
+
+    def dev(a):
+        return torch.from_numpy(a).to(device)
+
+    return PackedMoE(bits, E, K, N, group_size, act, dev(w1p), dev(s1p.view(np.int16)), k_perm1, dev(w2p),
+                     dev(s2p.view(np.int16)))
+
+
+def choose_block_size(M: int, topk: int, E: int) -> int:
+    """Batch-size heuristic: expected rows per touched expert decides between the
+    small-batch (block 16) and the large-batch (block 128) kernel."""
+    T = M * topk
+    if T == 0:
+        return DECODE_BLOCK
+    rows_per_expert = T / min(E, T)
+    return PREFILL_BLOCK if rows_per_expert > 64 else DECODE_BLOCK
+
+
+def fused_moe(x, logits, p: PackedMoE, topk: int, renormalize: bool = True, block_size: Optional[int] = None,
+              stream=None, keep=False):
+    """x [M, K] act, logits [M, E] float32 -> out [M, K] act.  With keep=True also
+    returns a dict of the intermediate device buffers."""
+    import torch
+    M = x.shape[0]
+    dev = x.device
+    bs = choose_block_size(M, topk, p.E) if block_size is None else block_size
+    w, ids = ops.moe_route(logits, topk, renormalize, stream=stream)
+    cap = ops.moe_align_capacity(M, topk, p.E, bs)
+    st, ex, nt = ops.moe_align(ids, p.E, bs, cap, stream=stream)
+    act_order = p.k_perm1 is not None
+    ws1 = ops.moe_gemm_workspace_bytes(WQ_STAGE_GATE_UP, M, topk, 2 * p.N, p.K, cap, act_order)
+    ws2 = ops.moe_gemm_workspace_bytes(WQ_STAGE_DOWN, M, topk, p.K, p.N, cap, False)
+    work1 = torch.empty(ws1, dtype=torch.uint8, device=dev) if ws1 else None
+    work2 = torch.empty(ws2, dtype=torch.uint8, device=dev) if ws2 else None
+    h = torch.empty((max(cap, 1), p.N), dtype=p.act, device=dev)
+    out = torch.empty((M, p.K), dtype=p.act, device=dev)
+    if p.bits == 4:
+        ops.moe_w4a16_gemm(WQ_STAGE_GATE_UP, x, M, topk, p.E, 2 * p.N, p.K, p.w1, p.s1, p.group_size, p.k_perm1,
+                           st, ex, nt, cap, bs, None, h, work1, stream, p.act_code)
+        ops.moe_w4a16_gemm(WQ_STAGE_DOWN, h, M, topk, p.E, p.K, p.N, p.w2, p.s2, p.group_size, None, st, ex, nt,
+                           cap, bs, w, out, work2, stream, p.act_code)
+    else:
+        ops.moe_w8a16_gemm(WQ_STAGE_GATE_UP, x, M, topk, p.E, 2 * p.N, p.K, p.w1, p.s1, st, ex, nt, cap, bs, None,
+                           h, work1, stream, p.act_code)
+        ops.moe_w8a16_gemm(WQ_STAGE_DOWN, h, M, topk, p.E, p.K, p.N, p.w2, p.s2, st, ex, nt, cap, bs, w, out,
+                           work2, stream, p.act_code)
+    if keep:
+        return out, {"topk_weights": w, "topk_ids": ids, "sorted_token_ids": st, "expert_ids": ex,
+                     "num_tokens_post_padded": nt, "h": h, "y": work2, "block_size": bs, "capacity": cap}
+    return out

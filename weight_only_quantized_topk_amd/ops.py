@@ -1,0 +1,214 @@
+"""Thin Python binding over libwqmoe.so.
+
+Every function here only marshals arguments: torch tensors supply device
+memory and the current HIP stream, numpy arrays supply host memory for the
+offline packers.  All computation happens in the library's kernels (or, for
+the packers, in its host code).  The names follow include/wqmoe.h.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, WQ_STAGE_GATE_UP, WQ_STAGE_RAW,
+                   WqMoeGemmDesc, check, load)
+
+__all__ = [
+    "moe_route", "moe_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
+    "sparse24_w4a16_gemm", "pack_w4", "pack_w8", "pack_sparse24", "act_code",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(stream)
+    torch = _torch()
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def act_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float16:
+        return WQ_F16
+    if dtype == torch.bfloat16:
+        return WQ_BF16
+    raise ValueError("activation dtype must be float16 or bfloat16, got %s" % dtype)
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+# ----------------------------------------------------------------------------
+# hot path
+# ----------------------------------------------------------------------------
+def moe_route(logits, topk: int, renormalize: bool = True, topk_weights=None, topk_ids=None, stream=None):
+    """logits [M, E] float32 (device) -> (topk_weights [M, topk] f32, topk_ids [M, topk] i32)."""
+    torch = _torch()
+    M, E = logits.shape
+    if topk_weights is None:
+        topk_weights = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((M, topk), dtype=torch.int32, device=logits.device)
+    check(load().moe_route(_ptr(logits), M, E, topk, int(bool(renormalize)), _ptr(topk_weights), _ptr(topk_ids),
+                           _stream(stream)), "moe_route")
+    return topk_weights, topk_ids
+
+
+def moe_align_capacity(M: int, topk: int, E: int, block_size: int) -> int:
+    return int(load().moe_align_capacity(M, topk, E, block_size))
+
+
+def moe_align(topk_ids, E: int, block_size: int, capacity: Optional[int] = None, sorted_token_ids=None,
+              expert_ids=None, num_tokens_post_padded=None, stream=None):
+    """topk_ids [M, topk] i32 (device) -> (sorted_token_ids [cap], expert_ids [cap/BS], num_tokens_post_padded [1])."""
+    torch = _torch()
+    M, topk = topk_ids.shape
+    cap = moe_align_capacity(M, topk, E, block_size) if capacity is None else capacity
+    dev = topk_ids.device
+    if sorted_token_ids is None:
+        sorted_token_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(max(cap // block_size, 1), dtype=torch.int32, device=dev)
+    if num_tokens_post_padded is None:
+        num_tokens_post_padded = torch.empty(4, dtype=torch.int32, device=dev)
+    check(load().moe_align(_ptr(topk_ids), M, topk, E, block_size, _ptr(sorted_token_ids), _ptr(expert_ids),
+                           _ptr(num_tokens_post_padded), cap, _stream(stream)), "moe_align")
+    return sorted_token_ids, expert_ids, num_tokens_post_padded
+
+
+def moe_gemm_workspace_bytes(stage: int, M: int, topk: int, n_out: int, k_in: int, capacity: int,
+                             act_order: bool) -> int:
+    return int(load().moe_gemm_workspace_bytes(stage, M, topk, n_out, k_in, capacity, int(bool(act_order))))
+
+
+def _gemm(fn_name: str, stage: int, a, M: int, topk: int, E: int, n_out: int, k_in: int, w_packed, scales,
+          group_size: int, k_perm, sorted_token_ids, expert_ids, num_tokens_post_padded, capacity: int,
+          block_size: int, topk_weights, out, workspace, stream, act_dtype: int):
+    d = WqMoeGemmDesc()
+    d.struct_size = C.sizeof(WqMoeGemmDesc)
+    d.stage = stage
+    d.act_dtype = act_dtype
+    d.d_a = _ptr(a)
+    d.M, d.topk, d.E, d.n_out, d.k_in = M, topk, E, n_out, k_in
+    d.d_w_packed = _ptr(w_packed)
+    d.d_scales = _ptr(scales)
+    d.group_size = group_size
+    d.d_k_perm = _ptr(k_perm)
+    d.d_sorted_token_ids = _ptr(sorted_token_ids)
+    d.d_expert_ids = _ptr(expert_ids)
+    d.d_num_tokens_post_padded = _ptr(num_tokens_post_padded)
+    d.capacity = capacity
+    d.block_size = block_size
+    d.d_topk_weights = _ptr(topk_weights)
+    d.d_out = _ptr(out)
+    d.d_workspace = _ptr(workspace)
+    d.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(getattr(load(), fn_name)(C.byref(d), _stream(stream)), fn_name)
+    return out
+
+
+def moe_w4a16_gemm(stage, a, M, topk, E, n_out, k_in, w_packed, scales, group_size, k_perm, sorted_token_ids,
+                   expert_ids, num_tokens_post_padded, capacity, block_size, topk_weights, out, workspace=None,
+                   stream=None, act_dtype=WQ_F16):
+    return _gemm("moe_w4a16_gemm", stage, a, M, topk, E, n_out, k_in, w_packed, scales, group_size, k_perm,
+                 sorted_token_ids, expert_ids, num_tokens_post_padded, capacity, block_size, topk_weights, out,
+                 workspace, stream, act_dtype)
+
+
+def moe_w8a16_gemm(stage, a, M, topk, E, n_out, k_in, w_packed, scales, sorted_token_ids, expert_ids,
+                   num_tokens_post_padded, capacity, block_size, topk_weights, out, workspace=None, stream=None,
+                   act_dtype=WQ_BF16):
+    return _gemm("moe_w8a16_gemm", stage, a, M, topk, E, n_out, k_in, w_packed, scales, -1, None,
+                 sorted_token_ids, expert_ids, num_tokens_post_padded, capacity, block_size, topk_weights, out,
+                 workspace, stream, act_dtype)
+
+
+def sparse24_w4a16_gemm(x, vals, meta, scales, N: int, out=None, group_size: int = 128, stream=None):
+    """x [M, K] fp16 (device) -> y [M, N] fp16."""
+    torch = _torch()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    check(load().sparse24_w4a16_gemm(_ptr(x), M, K, N, _ptr(vals), _ptr(meta), _ptr(scales), group_size, _ptr(out),
+                                     act_code(x.dtype), _stream(stream)), "sparse24_w4a16_gemm")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# offline packers (host numpy in / out)
+# ----------------------------------------------------------------------------
+def pack_w4(q: np.ndarray, scales_bits: np.ndarray, group_size: int, g_idx: Optional[np.ndarray] = None,
+            row_perm: Optional[np.ndarray] = None, interleave_gate_up: bool = False
+            ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
+    """q int8 [E, n_out, k_in], scales uint16 [E, G, n_out] -> (packed uint8, scales uint16, k_perm or None)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    E, n_out, k_in = q.shape
+    s = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    L = load()
+    nbytes = int(L.wq_pack_w4_bytes(E, n_out, k_in))
+    if nbytes == 0:
+        raise ValueError("unsupported int4 shape %s" % (q.shape,))
+    packed = np.empty(nbytes, np.uint8)
+    sp = np.empty_like(s)
+    gi = None if g_idx is None else np.ascontiguousarray(g_idx, dtype=np.int32)
+    rp = None if row_perm is None else np.ascontiguousarray(row_perm, dtype=np.int32)
+    kp = np.empty((E, k_in), np.int32) if gi is not None else None
+    flags = WQ_PACK_INTERLEAVE_GATE_UP if interleave_gate_up else 0
+    check(L.wq_pack_w4(E, n_out, k_in, _np_ptr(q), _np_ptr(s), group_size, _np_ptr(gi), _np_ptr(rp), flags,
+                       _np_ptr(packed), _np_ptr(sp), _np_ptr(kp)), "wq_pack_w4")
+    return packed, sp, kp
+
+
+def pack_w8(q: np.ndarray, scales_bits: np.ndarray, row_perm: Optional[np.ndarray] = None,
+            interleave_gate_up: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """q int8 [E, n_out, k_in], scales uint16 [E, 1, n_out] -> (packed uint8, scales uint16)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    E, n_out, k_in = q.shape
+    s = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    L = load()
+    nbytes = int(L.wq_pack_w8_bytes(E, n_out, k_in))
+    if nbytes == 0:
+        raise ValueError("unsupported int8 shape %s" % (q.shape,))
+    packed = np.empty(nbytes, np.uint8)
+    sp = np.empty_like(s)
+    rp = None if row_perm is None else np.ascontiguousarray(row_perm, dtype=np.int32)
+    flags = WQ_PACK_INTERLEAVE_GATE_UP if interleave_gate_up else 0
+    check(L.wq_pack_w8(E, n_out, k_in, _np_ptr(q), _np_ptr(s), _np_ptr(rp), flags, _np_ptr(packed), _np_ptr(sp)),
+          "wq_pack_w8")
+    return packed, sp
+
+
+def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray):
+    """vals int8 [N, K/2], idx uint8 [N, K/2], scales uint16 [K/128, N] -> (vals, meta, scales) packed."""
+    vals = np.ascontiguousarray(vals, dtype=np.int8)
+    idx = np.ascontiguousarray(idx, dtype=np.uint8)
+    s = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    N, Kh = vals.shape
+    K = 2 * Kh
+    L = load()
+    vb = int(L.wq_pack_sparse24_vals_bytes(N, K))
+    mb = int(L.wq_pack_sparse24_meta_bytes(N, K))
+    if vb == 0 or mb == 0:
+        raise ValueError("unsupported 2:4 shape N=%d K=%d" % (N, K))
+    vp = np.empty(vb, np.uint8)
+    mp = np.empty(mb, np.uint8)
+    sp = np.empty_like(s)
+    check(L.wq_pack_sparse24(N, K, _np_ptr(vals), _np_ptr(idx), _np_ptr(s), _np_ptr(vp), _np_ptr(mp), _np_ptr(sp)),
+          "wq_pack_sparse24")
+    return vp, mp, sp
+
+
+_ = (WQ_STAGE_GATE_UP, WQ_STAGE_DOWN, WQ_STAGE_RAW, WQ_F16, WQ_BF16, _lib)
