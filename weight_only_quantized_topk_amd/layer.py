@@ -82,35 +82,77 @@ def choose_block_size(M: int, topk: int, E: int) -> int:
     return PREFILL_BLOCK if rows_per_expert > 64 else DECODE_BLOCK
 
 
+class MoERunner:
+    """The hot path for one batch shape with every buffer allocated up front, so
+    a call allocates nothing.  marks: optional 3 events recorded on the stream
+    after alignment, after GATE_UP and after DOWN (stage timing)."""
+
+    def __init__(self, p: PackedMoE, M: int, topk: int, renormalize: bool = True, block_size: Optional[int] = None,
+                 device="cuda"):
+        import torch
+        self.p, self.M, self.topk, self.renormalize = p, M, topk, renormalize
+        self.bs = choose_block_size(M, topk, p.E) if block_size is None else block_size
+        self.cap = ops.moe_align_capacity(M, topk, p.E, self.bs)
+        dev = torch.device(device)
+        self.w = torch.empty((M, topk), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((M, topk), dtype=torch.int32, device=dev)
+        self.st = torch.empty(max(self.cap, 1), dtype=torch.int32, device=dev)
+        self.ex = torch.empty(max(self.cap // self.bs, 1), dtype=torch.int32, device=dev)
+        self.nt = torch.empty(4, dtype=torch.int32, device=dev)
+        act_order = p.k_perm1 is not None
+        ws1 = ops.moe_gemm_workspace_bytes(WQ_STAGE_GATE_UP, M, topk, 2 * p.N, p.K, self.cap, act_order)
+        ws2 = ops.moe_gemm_workspace_bytes(WQ_STAGE_DOWN, M, topk, p.K, p.N, self.cap, False)
+        self.work1 = torch.empty(ws1, dtype=torch.uint8, device=dev) if ws1 else None
+        self.work2 = torch.empty(ws2, dtype=torch.uint8, device=dev) if ws2 else None
+        self.h = torch.empty((max(self.cap, 1), p.N), dtype=p.act, device=dev)
+        self.out = torch.empty((M, p.K), dtype=p.act, device=dev)
+
+    def route_align(self, logits, stream=None):
+        ops.moe_route(logits, self.topk, self.renormalize, self.w, self.ids, stream=stream)
+        ops.moe_align(self.ids, self.p.E, self.bs, self.cap, self.st, self.ex, self.nt, stream=stream)
+
+    def gate_up(self, x, stream=None):
+        p = self
+        q = self.p
+        if q.bits == 4:
+            ops.moe_w4a16_gemm(WQ_STAGE_GATE_UP, x, p.M, p.topk, q.E, 2 * q.N, q.K, q.w1, q.s1, q.group_size,
+                               q.k_perm1, p.st, p.ex, p.nt, p.cap, p.bs, None, p.h, p.work1, stream, q.act_code)
+        else:
+            ops.moe_w8a16_gemm(WQ_STAGE_GATE_UP, x, p.M, p.topk, q.E, 2 * q.N, q.K, q.w1, q.s1, p.st, p.ex, p.nt,
+                               p.cap, p.bs, None, p.h, p.work1, stream, q.act_code)
+
+    def down(self, stream=None):
+        p = self
+        q = self.p
+        if q.bits == 4:
+            ops.moe_w4a16_gemm(WQ_STAGE_DOWN, p.h, p.M, p.topk, q.E, q.K, q.N, q.w2, q.s2, q.group_size, None,
+                               p.st, p.ex, p.nt, p.cap, p.bs, p.w, p.out, p.work2, stream, q.act_code)
+        else:
+            ops.moe_w8a16_gemm(WQ_STAGE_DOWN, p.h, p.M, p.topk, q.E, q.K, q.N, q.w2, q.s2, p.st, p.ex, p.nt, p.cap,
+                               p.bs, p.w, p.out, p.work2, stream, q.act_code)
+
+    def __call__(self, x, logits, marks=None, stream=None):
+        self.route_align(logits, stream)
+        if marks:
+            marks[0].record()
+        self.gate_up(x, stream)
+        if marks:
+            marks[1].record()
+        self.down(stream)
+        if marks:
+            marks[2].record()
+        return self.out
+
+    def aux(self):
+        return {"topk_weights": self.w, "topk_ids": self.ids, "sorted_token_ids": self.st, "expert_ids": self.ex,
+                "num_tokens_post_padded": self.nt, "h": self.h, "y": self.work2, "block_size": self.bs,
+                "capacity": self.cap}
+
+
 def fused_moe(x, logits, p: PackedMoE, topk: int, renormalize: bool = True, block_size: Optional[int] = None,
               stream=None, keep=False):
     """x [M, K] act, logits [M, E] float32 -> out [M, K] act.  With keep=True also
     returns a dict of the intermediate device buffers."""
-    import torch
-    M = x.shape[0]
-    dev = x.device
-    bs = choose_block_size(M, topk, p.E) if block_size is None else block_size
-    w, ids = ops.moe_route(logits, topk, renormalize, stream=stream)
-    cap = ops.moe_align_capacity(M, topk, p.E, bs)
-    st, ex, nt = ops.moe_align(ids, p.E, bs, cap, stream=stream)
-    act_order = p.k_perm1 is not None
-    ws1 = ops.moe_gemm_workspace_bytes(WQ_STAGE_GATE_UP, M, topk, 2 * p.N, p.K, cap, act_order)
-    ws2 = ops.moe_gemm_workspace_bytes(WQ_STAGE_DOWN, M, topk, p.K, p.N, cap, False)
-    work1 = torch.empty(ws1, dtype=torch.uint8, device=dev) if ws1 else None
-    work2 = torch.empty(ws2, dtype=torch.uint8, device=dev) if ws2 else None
-    h = torch.empty((max(cap, 1), p.N), dtype=p.act, device=dev)
-    out = torch.empty((M, p.K), dtype=p.act, device=dev)
-    if p.bits == 4:
-        ops.moe_w4a16_gemm(WQ_STAGE_GATE_UP, x, M, topk, p.E, 2 * p.N, p.K, p.w1, p.s1, p.group_size, p.k_perm1,
-                           st, ex, nt, cap, bs, None, h, work1, stream, p.act_code)
-        ops.moe_w4a16_gemm(WQ_STAGE_DOWN, h, M, topk, p.E, p.K, p.N, p.w2, p.s2, p.group_size, None, st, ex, nt,
-                           cap, bs, w, out, work2, stream, p.act_code)
-    else:
-        ops.moe_w8a16_gemm(WQ_STAGE_GATE_UP, x, M, topk, p.E, 2 * p.N, p.K, p.w1, p.s1, st, ex, nt, cap, bs, None,
-                           h, work1, stream, p.act_code)
-        ops.moe_w8a16_gemm(WQ_STAGE_DOWN, h, M, topk, p.E, p.K, p.N, p.w2, p.s2, st, ex, nt, cap, bs, w, out,
-                           work2, stream, p.act_code)
-    if keep:
-        return out, {"topk_weights": w, "topk_ids": ids, "sorted_token_ids": st, "expert_ids": ex,
-                     "num_tokens_post_padded": nt, "h": h, "y": work2, "block_size": bs, "capacity": cap}
-    return out
+    r = MoERunner(p, x.shape[0], topk, renormalize, block_size, device=x.device)
+    out = r(x, logits, stream=stream)
+    return (out, r.aux()) if keep else out
