@@ -24,15 +24,16 @@
 
 namespace wq {
 
-constexpr int DEC_WAVES = 4;
-constexpr int DEC_THREADS = 64 * DEC_WAVES;
-
-template <int WBITS, bool BF16, int STAGE, int RMAX>
-__global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
-    constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 : 1;
+// Kernel shape: NP weight-row tiles per workgroup (pairs of gate+up tiles for
+// the fused stage), NW waves splitting the input channels, DEPTH 1 KiB chunks
+// per tile in flight per wave, up to RMAX 16-row token blocks per pass.
+template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH>
+__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
+    constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;  // 16-row tiles per workgroup
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     constexpr int KSTEPS = KCHUNK / 32;
-    static_assert(RMAX <= DEC_WAVES, "one wave per token block in the epilogue");
+    constexpr int ITEMS = NP * RMAX;  // epilogue items (tile or tile pair, token block)
+    static_assert(NW * NT * RMAX * 1024 <= 64 * 1024, "LDS reduction buffer");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -60,10 +61,9 @@ __global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
         wt[t] = g.w + (size_t)e * expert_bytes + (size_t)(NT * unit + t) * C * CHUNK_BYTES + lane * 16;
     const uint16_t* se = g.s + (size_t)e * g.groups * g.n_out;
     const int rowq = 4 * (lane >> 4);  // first of this lane's 4 output rows in a tile
-    constexpr bool GROUPED = (WBITS == 4);
-    const bool grouped = GROUPED && g.groups > 1;
+    const bool grouped = (WBITS == 4) && g.groups > 1;
 
-    __shared__ f32x4 red[DEC_WAVES][NT][RMAX][64];
+    __shared__ f32x4 red[NW][NT][RMAX][64];
 
     for (int s0 = 0; s0 < S; s0 += RMAX) {
         const int R = min(RMAX, S - s0);
@@ -88,27 +88,29 @@ __global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        u32x4 wA[NT], wB[NT];
-        u32x4 xA[RMAX][KSTEPS], xB[RMAX][KSTEPS];
-        u32x2 sA[NT], sB[NT];
+        // DEPTH rotating buffers of one chunk each
+        u32x4 wv[DEPTH][NT];
+        u32x4 xv[DEPTH][RMAX][KSTEPS];
+        u32x2 sv[DEPTH][NT];
 
-        auto load = [&](int c, u32x4(&wv)[NT], u32x4(&xv)[RMAX][KSTEPS], u32x2(&sv)[NT]) {
+        auto load = [&](int c, int d) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) wv[t] = ldg128_stream(wt[t] + (size_t)c * CHUNK_BYTES);
+            for (int t = 0; t < NT; ++t) wv[d][t] = ldg128_stream(wt[t] + (size_t)c * CHUNK_BYTES);
 #pragma unroll
             for (int r = 0; r < RMAX; ++r)
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s)
-                    xv[r][s] = (r < R && avalid[r]) ? ldg128(arow[r] + c * KCHUNK + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+                    xv[d][r][s] =
+                        (r < R && avalid[r]) ? ldg128(arow[r] + c * KCHUNK + 32 * s) : u32x4{0u, 0u, 0u, 0u};
             if (grouped) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    sv[t] = *reinterpret_cast<const u32x2*>(se + (size_t)c * g.n_out + (NT * unit + t) * TILE_ROWS +
-                                                            rowq);
+                    sv[d][t] = *reinterpret_cast<const u32x2*>(se + (size_t)c * g.n_out +
+                                                               (NT * unit + t) * TILE_ROWS + rowq);
             }
         };
 
-        auto compute = [&](const u32x4(&wv)[NT], const u32x4(&xv)[RMAX][KSTEPS], const u32x2(&sv)[NT]) {
+        auto compute = [&](int d) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if constexpr (WBITS == 4) {
@@ -117,16 +119,17 @@ __global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
                     for (int r = 0; r < RMAX; ++r) part[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KSTEPS; ++s) {
-                        const u32x4 a = dequant_w4_f16(wv[t][s]);
+                        const u32x4 a = dequant_w4_f16(wv[d][t][s]);
 #pragma unroll
                         for (int r = 0; r < RMAX; ++r)
-                            if (r < R) part[r] = mfma16x16x32<false>(a, xv[r][s], part[r]);
+                            if (r < R) part[r] = mfma16x16x32<false>(a, xv[d][r][s], part[r]);
                     }
                     if (grouped) {
-                        const float s0f = f16_to_f32((uint16_t)(sv[t][0] & 0xffffu));
-                        const float s1f = f16_to_f32((uint16_t)(sv[t][0] >> 16));
-                        const float s2f = f16_to_f32((uint16_t)(sv[t][1] & 0xffffu));
-                        const float s3f = f16_to_f32((uint16_t)(sv[t][1] >> 16));
+                        const uint32_t lo = sv[d][t][0], hi = sv[d][t][1];
+                        const float s0f = f16_to_f32((uint16_t)(lo & 0xffffu));
+                        const float s1f = f16_to_f32((uint16_t)(lo >> 16));
+                        const float s2f = f16_to_f32((uint16_t)(hi & 0xffffu));
+                        const float s3f = f16_to_f32((uint16_t)(hi >> 16));
 #pragma unroll
                         for (int r = 0; r < RMAX; ++r) {
                             acc[t][r][0] += part[r][0] * s0f;
@@ -141,27 +144,27 @@ __global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
                 } else {
 #pragma unroll
                     for (int s = 0; s < KSTEPS; ++s) {
-                        const u32x4 a = dequant_w8x8<BF16>(wv[t][2 * s], wv[t][2 * s + 1]);
+                        const u32x4 a = dequant_w8x8<BF16>(wv[d][t][2 * s], wv[d][t][2 * s + 1]);
 #pragma unroll
                         for (int r = 0; r < RMAX; ++r)
-                            if (r < R) acc[t][r] = mfma16x16x32<BF16>(a, xv[r][s], acc[t][r]);
+                            if (r < R) acc[t][r] = mfma16x16x32<BF16>(a, xv[d][r][s], acc[t][r]);
                     }
                 }
             }
         };
 
-        // split-K over the waves, two chunks in flight per wave (ping-pong)
-        int c = wave;
-        if (c < C) load(c, wA, xA, sA);
-        while (c < C) {
-            const int c1 = c + DEC_WAVES;
-            if (c1 < C) load(c1, wB, xB, sB);
-            compute(wA, xA, sA);
-            if (c1 >= C) break;
-            const int c2 = c1 + DEC_WAVES;
-            if (c2 < C) load(c2, wA, xA, sA);
-            compute(wB, xB, sB);
-            c = c2;
+        // split-K over the waves; DEPTH - 1 chunks in flight while one is multiplied
+#pragma unroll
+        for (int i = 0; i < DEPTH - 1; ++i)
+            if (wave + i * NW < C) load(wave + i * NW, i);
+        for (int base = wave; base < C; base += DEPTH * NW) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int c = base + d * NW;
+                const int cl = c + (DEPTH - 1) * NW;
+                if (cl < C) load(cl, (d + DEPTH - 1) % DEPTH);
+                if (c < C) compute(d);
+            }
         }
 
 #pragma unroll
@@ -170,44 +173,48 @@ __global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
             for (int r = 0; r < RMAX; ++r) red[wave][t][r][lane] = acc[t][r];
         __syncthreads();
 
-        if (wave < R) {
-            const int r = wave;
-            f32x4 v[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                v[t] = red[0][t][r][lane];
-#pragma unroll
-                for (int w = 1; w < DEC_WAVES; ++w) v[t] += red[w][t][r][lane];
-            }
+        for (int item = wave; item < ITEMS; item += NW) {
+            const int pp = item / RMAX;  // tile (or gate/up tile pair) within the workgroup
+            const int r = item % RMAX;
+            if (r >= R) continue;
             const int p = (sb_first + s0 + r) * 16 + (lane & 15);
             const int pair = g.sorted[p];
             if constexpr (STAGE == STAGE_GATE_UP) {
+                const int tg = 2 * pp, tu = 2 * pp + 1;  // gate and up tile within the workgroup
+                f32x4 gv = red[0][tg][r][lane], uv = red[0][tu][r][lane];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) {
+                    gv += red[w][tg][r][lane];
+                    uv += red[w][tu][r][lane];
+                }
                 const int N = g.n_out / 2;
+                const int hcol = (NP * unit + pp) * TILE_ROWS + rowq;
                 float h[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float gt = v[0][i], up = v[1][i];
+                    float gt = gv[i], up = uv[i];
                     if (!grouped) {
-                        gt *= act_to_f32<BF16>(se[(2 * unit) * TILE_ROWS + rowq + i]);
-                        up *= act_to_f32<BF16>(se[(2 * unit + 1) * TILE_ROWS + rowq + i]);
+                        gt *= act_to_f32<BF16>(se[(NT * unit + tg) * TILE_ROWS + rowq + i]);
+                        up *= act_to_f32<BF16>(se[(NT * unit + tu) * TILE_ROWS + rowq + i]);
                     }
                     h[i] = silu_f32(gt) * up;
                 }
                 u32x2 st;
                 st[0] = (uint32_t)f32_to_act<BF16>(h[0]) | ((uint32_t)f32_to_act<BF16>(h[1]) << 16);
                 st[1] = (uint32_t)f32_to_act<BF16>(h[2]) | ((uint32_t)f32_to_act<BF16>(h[3]) << 16);
-                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (size_t)p * N + unit * TILE_ROWS + rowq) =
-                    st;
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (size_t)p * N + hcol) = st;
             } else {
                 if (pair < T) {
-                    f32x4 o = v[0];
+                    f32x4 o = red[0][pp][r][lane];
+#pragma unroll
+                    for (int w = 1; w < NW; ++w) o += red[w][pp][r][lane];
+                    const int row = (NT * unit + pp) * TILE_ROWS + rowq;
                     if (!grouped) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] *= act_to_f32<BF16>(se[unit * TILE_ROWS + rowq + i]);
+                        for (int i = 0; i < 4; ++i) o[i] *= act_to_f32<BF16>(se[row + i]);
                     }
                     if constexpr (STAGE == STAGE_DOWN) o *= g.topk_w[pair];
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (size_t)pair * g.n_out +
-                                              unit * TILE_ROWS + rowq) = o;
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (size_t)pair * g.n_out + row) = o;
                 }
             }
         }
@@ -219,25 +226,45 @@ __global__ __launch_bounds__(DEC_THREADS) void gemm_decode_kernel(GemmArgs g) {
         const int N = g.n_out / 2;
         const int p_lo = (sb_first + S) * 16;
         const int p_hi = b1 * BS;
-        for (int k = threadIdx.x; k < (p_hi - p_lo) * TILE_ROWS; k += DEC_THREADS) {
-            const int p = p_lo + k / TILE_ROWS;
-            static_cast<uint16_t*>(g.out)[(size_t)p * N + unit * TILE_ROWS + (k % TILE_ROWS)] = 0;
+        constexpr int COLS = NP * TILE_ROWS;
+        for (int k = threadIdx.x; k < (p_hi - p_lo) * COLS; k += 64 * NW) {
+            const int p = p_lo + k / COLS;
+            static_cast<uint16_t*>(g.out)[(size_t)p * N + NP * unit * TILE_ROWS + (k % COLS)] = 0;
         }
     }
 }
 
+template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH>
+static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
+    constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;
+    const dim3 grid(g.n_out / (TILE_ROWS * NT), g.E);
+    hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH>), grid, dim3(64 * NW), 0, s, g);
+}
+
+// Shapes by batch (measured on MI355X with the cfg2 Mixtral shapes): one
+// token block per pass when the experts are thin (each wave then keeps one
+// chunk in flight while it multiplies one; the down stage, with half as many
+// weight rows, takes two row tiles per workgroup, 8 waves and two chunks in
+// flight), two blocks and two row tiles when experts average up to ~24 rows,
+// four blocks beyond.  Token blocks an expert has beyond RMAX cost another
+// pass over its weights.
 template <int WBITS, bool BF16, int STAGE>
 static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
-    constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 : 1;
-    const dim3 grid(g.n_out / (TILE_ROWS * NT), g.E);
+    constexpr int NT1 = (STAGE == STAGE_GATE_UP) ? 2 : 1;
     const int T = g.M * g.topk;
-    const int sub = (T + 15) / 16;  // most 16-row sub-blocks any expert can fill
-    if (sub <= 1)
-        hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, 1>), grid, dim3(DEC_THREADS), 0, s, g);
-    else if (sub <= 2)
-        hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, 2>), grid, dim3(DEC_THREADS), 0, s, g);
-    else
-        hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, 4>), grid, dim3(DEC_THREADS), 0, s, g);
+    const int touched = T < g.E ? T : g.E;
+    const int rows = (T + touched - 1) / touched;  // expected rows per touched expert
+    const bool np2_ok = (g.n_out % (TILE_ROWS * NT1 * 2)) == 0;
+    if (T <= 16 || rows <= 8) {
+        if (STAGE == STAGE_GATE_UP) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
+        else if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 8, 3>(g, s);
+        else launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 8, 4>(g, s);
+    } else if (rows <= 24) {
+        if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);
+        else launch_decode_cfg<WBITS, BF16, STAGE, 2, 1, 4, 2>(g, s);
+    } else {
+        launch_decode_cfg<WBITS, BF16, STAGE, 4, 1, 4, 2>(g, s);
+    }
 }
 
 template <int WBITS, bool BF16>
