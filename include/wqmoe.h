@@ -125,8 +125,9 @@ wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block
  *    code * scale ("[Kernel] W8A16 Int8 inside FusedMoE", vLLM PR 7415,
  *    opening description).
  * Expert rows are those of d_sorted_token_ids (from moe_align with the same
- * block_size); block_size a multiple of 128 selects the large-batch kernel,
- * smaller blocks the small-batch (decode) kernel.
+ * block_size); block_size 64 or a multiple of 128 (with n_out a multiple of 128
+ * and k_in a multiple of 64) selects the large-batch kernel, other blocks the
+ * small-batch (decode) kernel.
  *
  * Stages (A is d_a, W the expert's packed weight of n_out rows, k_in columns):
  *  GATE_UP  d_a = x [M, k_in]; W = w1 packed with WQ_PACK_INTERLEAVE_GATE_UP,

@@ -44,7 +44,7 @@ def decode_w8(packed: np.ndarray, E: int, n_out: int, k_in: int) -> np.ndarray:
     b = packed.reshape(E, n_out // 16, C, 64, 2, 8)
     out = np.empty((E, n_out // 16, 16, C, 2, 4, 8), np.int8)   # e, t, row, c, s, lanegroup, j
     for l in range(64):
-        out[:, :, l % 16, :, :, l // 16, :] = (b[:, :, :, l, :, :].astype(np.int16) - 128).astype(np.int8)
+        out[:, :, l % 16, :, :, l // 16, :] = b[:, :, :, l, :, :].view(np.int8)
     return out.reshape(E, n_out, k_in)
 
 

@@ -60,7 +60,7 @@ def align_dev(ids, E, bs):
 
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("act_order", [False, True])
 def test_raw_exact_integer(bits, bs, act_order):
     """Power-of-two group scales, x in {-1,0,1}: bit-exact fp32 projections."""
@@ -128,7 +128,7 @@ def h_perm(spec, wts, e):
 
 
 @pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e"])
-@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_gate_up(key, bs, M):
     need_gpu()
@@ -155,7 +155,7 @@ def test_gate_up(key, bs, M):
 
 
 @pytest.mark.parametrize("key", ["w4", "w4ao", "w8", "w8e"])
-@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_down(key, bs, M):
     """DOWN from the oracle's H rounded to the activation type."""
@@ -192,7 +192,7 @@ def test_down(key, bs, M):
 
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e"])
-@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("M", [1, 16, 53, 512])
 def test_layer(key, bs, M):
     need_gpu()
@@ -209,7 +209,7 @@ def test_layer(key, bs, M):
 
 
 @pytest.mark.parametrize("key", ["w4ao", "w8"])
-@pytest.mark.parametrize("bs", [16, 128])
+@pytest.mark.parametrize("bs", [16, 64, 128])
 def test_layer_deterministic_and_equivariant(key, bs):
     need_gpu()
     spec, wts, p = setup(key)

@@ -283,7 +283,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
         y = static_cast<float*>(d->d_workspace);
         g.out = y;
     }
-    const bool prefill = (d->block_size % 128 == 0) && (d->n_out % 128 == 0);
+    const bool prefill = wq::prefill_supported(d->n_out, d->k_in, d->block_size);
     if (prefill) wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
     else wq::launch_gemm_decode(wbits, bf16, stage, g, s);
     WQ_TRY(after_launch(who));
@@ -479,7 +479,7 @@ wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t
                     uint8_t* dst = out + (size_t)e * expert_bytes + (((size_t)t * C + c) * 64 + l) * 16;
                     for (int st = 0; st < 2; ++st)
                         for (int j = 0; j < 8; ++j)
-                            dst[8 * st + j] = (uint8_t)((int)qr[64 * c + 32 * st + 8 * (l >> 4) + j] + 128);
+                            dst[8 * st + j] = (uint8_t)qr[64 * c + 32 * st + 8 * (l >> 4) + j];
                 }
             }
             if (t == 0)

@@ -119,21 +119,24 @@ __device__ __forceinline__ u32x4 dequant_w4_f16_scaled(uint32_t d, f16x2 s2) {
 }
 
 // ---------------------------------------------------------------------------
-// int8 codes -> 16-bit floats.  Bytes are stored offset-binary u = q + 128,
+// int8 codes -> 16-bit floats.  Bytes are the two's-complement codes q,
 // consecutive input channels in consecutive bytes.
-//  bf16: u as float minus 128 is q exactly; q has at most 8 significant bits,
-//        so the upper half of its float32 pattern is q in bf16 exactly.
-//  f16:  the half with bits 0x64uu is 1024 + u exactly; minus 1152 gives q.
+//  bf16: q converts to float exactly in one instruction (a sign-extending
+//        byte-select of the source operand feeds the int->float convert); q
+//        has at most 8 significant bits, so the upper half of its float32
+//        pattern is q in bf16 exactly.
+//  f16:  with u = q ^ 0x80 = q + 128, the half with bits 0x64uu is 1024 + u
+//        exactly; minus 1152 gives q.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 __device__ __forceinline__ u32x2 dequant_w8x4_bf16(uint32_t d) {
-    float f0 = (float)(d & 0xffu) - 128.0f;
-    float f1 = (float)((d >> 8) & 0xffu) - 128.0f;
-    float f2 = (float)((d >> 16) & 0xffu) - 128.0f;
-    float f3 = (float)(d >> 24) - 128.0f;
+    const float f0 = (float)(signed char)(d & 0xffu);
+    const float f1 = (float)(signed char)((d >> 8) & 0xffu);
+    const float f2 = (float)(signed char)((d >> 16) & 0xffu);
+    const float f3 = (float)((int)d >> 24);
     u32x2 r;
     r[0] = pack_hi16(f0, f1);
     r[1] = pack_hi16(f2, f3);
@@ -142,8 +145,9 @@ __device__ __forceinline__ u32x2 dequant_w8x4_bf16(uint32_t d) {
 
 __device__ __forceinline__ u32x2 dequant_w8x4_f16(uint32_t d) {
     const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, d, 0x05010400u);  // bytes [u0, 64, u1, 64]
-    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, d, 0x05030402u);  // bytes [u2, 64, u3, 64]
+    const uint32_t u = d ^ 0x80808080u;
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);  // bytes [u0, 64, u1, 64]
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u);  // bytes [u2, 64, u3, 64]
     return u32x2{f16x2_sub(lo, bias), f16x2_sub(hi, bias)};
 }
 

@@ -45,7 +45,8 @@ struct GemmArgs {
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
 void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
-// large-batch path: 128 x 128 tiles through LDS (block_size % 128 == 0)
+// large-batch path: 256 weight rows x 128 token rows through LDS
+bool prefill_supported(int n_out, int k_in, int block_size);
 void launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
 
 // act-order: A1[p, k'] = x[token(p), perm[expert(p), k']] for sorted rows p

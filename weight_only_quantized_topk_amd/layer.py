@@ -19,6 +19,7 @@ from ._lib import WQ_STAGE_DOWN, WQ_STAGE_GATE_UP
 
 DECODE_BLOCK = 16    # token block of the small-batch kernel
 PREFILL_BLOCK = 128  # token block of the large-batch kernel
+PREFILL_BLOCK_THIN = 64
 
 
 @dataclass
@@ -72,14 +73,20 @@ def pack_moe(bits: int, w1q: np.ndarray, s1_bits: np.ndarray, w2q: np.ndarray, s
                      dev(s2p.view(np.int16)))
 
 
-def choose_block_size(M: int, topk: int, E: int) -> int:
+def choose_block_size(M: int, topk: int, E: int, bits: int = 8) -> int:
     """Batch-size heuristic: expected rows per touched expert decides between the
-    small-batch (block 16) and the large-batch (block 128) kernel."""
+    small-batch kernel (block 16) and the large-batch kernel (block 64 or 128).
+    Blocks of 64 halve the padding of thin experts; int4 dequantisation costs
+    more VALU per MFMA, so int4 keeps 128-row token tiles."""
     T = M * topk
     if T == 0:
         return DECODE_BLOCK
     rows_per_expert = T / min(E, T)
-    return PREFILL_BLOCK if rows_per_expert > 64 else DECODE_BLOCK
+    if rows_per_expert <= 64:
+        return DECODE_BLOCK
+    if bits == 4 or rows_per_expert >= 512:
+        return PREFILL_BLOCK
+    return PREFILL_BLOCK_THIN
 
 
 class MoERunner:
@@ -91,7 +98,7 @@ class MoERunner:
                  device="cuda"):
         import torch
         self.p, self.M, self.topk, self.renormalize = p, M, topk, renormalize
-        self.bs = choose_block_size(M, topk, p.E) if block_size is None else block_size
+        self.bs = choose_block_size(M, topk, p.E, p.bits) if block_size is None else block_size
         self.cap = ops.moe_align_capacity(M, topk, p.E, self.bs)
         dev = torch.device(device)
         self.w = torch.empty((M, topk), dtype=torch.float32, device=dev)
