@@ -178,7 +178,7 @@ def main(argv=None):
         achieved = head["gate_up_GBps"]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4)}
-    roof["kernel"] = "gemm_%s_kernel gate/up (W%dA16)" % ("prefill" if head["block_size"] % 128 == 0 else "decode",
+    roof["kernel"] = "gemm_%s_kernel gate/up (W%dA16)" % ("prefill" if head["block_size"] >= 64 else "decode",
                                                         spec.bits)
     roof["kernel_avg_ms"] = round(head["gate_up_ms"], 4)
     roof["alg_bytes_per_launch"] = int(head["gate_up_alg_bytes"])

@@ -139,8 +139,11 @@ wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block
  *  DOWN     d_a = H [capacity, k_in] from GATE_UP (k_in = N); W = w2, n_out =
  *           hidden size.  d_out = out [M, n_out] act dtype:
  *           out[m, c] = sum_{j<topk} topk_weights[m,j] * (H W^T)[p(m,j), c],
- *           summed in ascending j in fp32 and rounded once.  Needs a workspace
- *           for the per-pair outputs (fp32 [M*topk, n_out]).
+ *           summed in fp32 and rounded once.  Needs a workspace for the
+ *           per-pair outputs: fp32 [M*topk, n_out], times 2 or 4 when the
+ *           large-batch kernel splits k_in to fill the GPU (small M*topk *
+ *           n_out); the slices are added in a fixed order, so results do not
+ *           vary from run to run.
  *  RAW      d_a = x [M, k_in]; d_out = fp32 [M*topk, n_out]:
  *           Z[i, r] = sum_k x[i/topk, k] * W_{expert(i)}[r, k], packed row order.
  * The workspace size comes from moe_gemm_workspace_bytes(); pass 0 / NULL if

@@ -26,8 +26,11 @@ W4AO = W4.with_(name="w4ao-small", act_order=True)
 W4PC = W4.with_(name="w4-percol-small", group_size=-1)
 W8 = gen.CFG2.with_(name="w8-small", E=8, topk=2, K=512, N=384)
 W8E = gen.CFG5.with_(name="w8-many-small", E=40, topk=6, K=256, N=256, zipf_s=1.1)
-SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E}
-SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505}
+# long k_in, narrow output: the large-batch DOWN splits K into 4 slices
+W4K = W4.with_(name="w4-longk", K=256, N=4096)
+W8K = W8.with_(name="w8-longk", K=256, N=4096)
+SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E, "w4k": W4K, "w8k": W8K}
+SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505, "w4k": 506, "w8k": 507}
 
 
 def _pack(spec, wts):
@@ -159,6 +162,20 @@ def test_gate_up(key, bs, M):
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_down(key, bs, M):
     """DOWN from the oracle's H rounded to the activation type."""
+    _check_down(key, bs, M)
+
+
+@pytest.mark.parametrize("key", ["w4k", "w8k"])
+@pytest.mark.parametrize("M", [37, 300])
+def test_down_split_k(key, M):
+    """k_in = 4096 with 256 outputs: the large-batch DOWN writes 4 fp32 slabs
+    of partial sums (its workspace says so) that the combine adds."""
+    spec = SPECS[key]
+    ws = _check_down(key, 128, M)
+    assert ws >= 4 * M * spec.topk * spec.K * 4
+
+
+def _check_down(key, bs, M):
     need_gpu()
     spec, wts, p = setup(key)
     toks, w, ids = routed(spec, M, seed=700 + M)
@@ -188,6 +205,7 @@ def test_down(key, bs, M):
                           bs, wd, out, work, act_dtype=p.act_code)
     torch.cuda.synchronize()
     assert_close_fp(host_f32(out), out_ref, "out %s bs=%d M=%d" % (key, bs, M))
+    return ws
 
 
 # ----------------------------------------------------------------------------

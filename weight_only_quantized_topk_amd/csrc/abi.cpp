@@ -188,7 +188,8 @@ size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int n_out, int k_in,
     if (M < 0 || topk <= 0 || n_out <= 0 || k_in <= 0) return 0;
     size_t b = 0;
     if ((stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_RAW) && act_order) b += round256(capacity * k_in * 2);
-    if (stage == WQ_STAGE_DOWN) b += round256((size_t)M * topk * n_out * sizeof(float));
+    if (stage == WQ_STAGE_DOWN)
+        b += round256((size_t)wq::prefill_down_split(M * topk, n_out, k_in) * M * topk * n_out * sizeof(float));
     return b;
 }
 
@@ -283,12 +284,12 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
         y = static_cast<float*>(d->d_workspace);
         g.out = y;
     }
-    const bool prefill = wq::prefill_supported(d->n_out, d->k_in, d->block_size);
-    if (prefill) wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
+    int ksplit = 1;
+    if (wq::prefill_supported(d->n_out, d->k_in, d->block_size)) ksplit = wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
     else wq::launch_gemm_decode(wbits, bf16, stage, g, s);
     WQ_TRY(after_launch(who));
     if (stage == WQ_STAGE_DOWN) {
-        wq::launch_combine(y, d->M, d->topk, d->n_out, bf16, static_cast<uint16_t*>(d->d_out), s);
+        wq::launch_combine(y, d->M, d->topk, d->n_out, ksplit, bf16, static_cast<uint16_t*>(d->d_out), s);
         WQ_TRY(after_launch(who));
     }
     return ok();

@@ -321,30 +321,33 @@ void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* s
 }
 
 // ---------------------------------------------------------------------------
-// top-k weighted combine: out[m, c] = sum_{j<topk} Y[m*topk+j, c]  (Y already
-// carries the routed weight), ascending j in fp32, one rounding to act
+// top-k weighted combine: out[m, c] = sum_{j<topk} sum_{z<ksplit} Y[z][m*topk+j, c]
+// (Y already carries the routed weight; z runs over the K slices of a split
+// DOWN stage), ascending j then z in fp32, one rounding to act
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int M, int topk, int n,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int M, int topk, int n, int ksplit,
                                                       uint16_t* __restrict__ out) {
     const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // 4 outputs each
     const size_t total = (size_t)M * n / 4;
     if (q >= total) return;
     const size_t m = q * 4 / n;
     const int c = (int)(q * 4 % n);
-    f32x4 acc = *reinterpret_cast<const f32x4*>(y + (m * topk) * n + c);
-    for (int j = 1; j < topk; ++j) acc += *reinterpret_cast<const f32x4*>(y + (m * topk + j) * n + c);
+    const size_t slab = (size_t)M * topk * n;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < topk; ++j)
+        for (int z = 0; z < ksplit; ++z) acc += *reinterpret_cast<const f32x4*>(y + z * slab + (m * topk + j) * n + c);
     u32x2 st;
     st[0] = (uint32_t)f32_to_act<BF16>(acc[0]) | ((uint32_t)f32_to_act<BF16>(acc[1]) << 16);
     st[1] = (uint32_t)f32_to_act<BF16>(acc[2]) | ((uint32_t)f32_to_act<BF16>(acc[3]) << 16);
     *reinterpret_cast<u32x2*>(out + m * n + c) = st;
 }
 
-void launch_combine(const float* y, int M, int topk, int n, bool bf16, uint16_t* out, hipStream_t s) {
+void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf16, uint16_t* out, hipStream_t s) {
     const size_t total = (size_t)M * n / 4;
     const dim3 grid((unsigned)((total + 255) / 256));
-    if (bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, y, M, topk, n, out);
-    else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, y, M, topk, n, out);
+    if (bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, y, M, topk, n, ksplit, out);
+    else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, y, M, topk, n, ksplit, out);
 }
 
 }  // namespace wq

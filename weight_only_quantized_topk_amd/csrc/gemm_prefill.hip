@@ -2,17 +2,17 @@
 //
 // Works on blocks of 64 or a multiple of 128 sorted token rows, so every
 // BM-row slice (BM = 64 or 128) of the sorted order belongs to one expert.
-// One workgroup of 4 waves computes BN (128 or 256) weight rows x BM rows:
-//  - the packed weight tile (16 rows x 64 input channels per 1 KiB of int8,
-//    per 512 B of int4) and the token rows (gathered through
-//    sorted_token_ids, or read directly for H and the act-order-permuted
-//    activations) are loaded with vector loads two K steps ahead into
-//    registers, the weights are dequantized once per workgroup (int4: q *
-//    group scale rounded once to fp16; int8: exact) and both tiles stored to
-//    LDS;
-//  - LDS holds two K steps: while the MFMAs of step k read one buffer, the
-//    same waves dequantize and store step k+1 into the other (independent
-//    instruction streams that the SIMD co-issues), one barrier per K step;
+// One workgroup computes BN weight rows x BM token rows of one expert:
+//  - per K step of 64 input channels the packed weight tile (16 rows x 64
+//    channels per 1 KiB of int8, per 512 B of int4) and the token rows
+//    (gathered through sorted_token_ids, or read directly for H and the
+//    act-order-permuted activations) are loaded with vector loads, the weights
+//    dequantized once per workgroup (int4: q * group scale rounded once to
+//    fp16; int8: exact) and both tiles stored to one LDS buffer;
+//  - the next K step's global loads are issued right after the LDS stores, so
+//    they are in flight while the MFMAs of the current step run; several
+//    workgroups (or the 8 waves of a large one) per CU cover each other's
+//    store phases;
 //  - each wave owns a 64 x 64 (or 64 x 32) slice of the outputs as 32 x 32
 //    v_mfma_f32_32x32x16 tiles with fp32 accumulators;
 //  - 128-byte LDS rows are split in 16-byte chunks stored at
@@ -22,16 +22,19 @@
 // tokens, so with the gate/up interleave of the packer a 32-row A tile holds 16
 // gate rows and the matching 16 up rows and SiLU(gate)*up is lane-local
 // (accumulator registers r and r + 8).
+//
+// DOWN may split K over gridDim.z slices when its output grid is too small to
+// fill the chip: slice z writes its partial sums to its own fp32 slab of Y and
+// the combine kernel adds the slabs in ascending order (deterministic).
 #include "common.hpp"
 #include "launch.hpp"
 
-#include <type_traits>
+#include <algorithm>
 
 namespace wq {
 
 constexpr int PF_BK = 64;  // input channels per K step
 constexpr int PF_ROWB = PF_BK * 2;
-constexpr int PF_THREADS = 256;
 
 // 16-byte chunk swizzle of a 128-byte LDS row: measured on gfx950 to be free of
 // bank conflicts for the MFMA operand reads (lane -> row l%32), the weight
@@ -39,18 +42,20 @@ constexpr int PF_THREADS = 256;
 __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int ch) { return row * PF_ROWB + ((ch ^ lds_swz(row)) << 4); }
 
-// BN weight rows x BM token rows per workgroup; WN waves along the weight
-// rows, 4 / WN along the tokens
-template <int WBITS, bool BF16, int STAGE, int BN, int BM, int WN>
-__global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g) {
-    constexpr int WM = 4 / WN;
-    constexpr int TI = BN / WN / 32;                              // 32-row weight tiles per wave
-    constexpr int TJ = BM / WM / 32;                              // 32-row token tiles per wave
-    constexpr int WPIECES = (BN / TILE_ROWS) * 64 / PF_THREADS;  // weight pieces per thread
-    constexpr int TPIECES = BM * (PF_BK / 8) / PF_THREADS;       // token pieces per thread
+// BN weight rows x BM token rows per workgroup of NW waves; WN waves along the
+// weight rows, NW / WN along the tokens; OCC workgroups per CU.  SKIP: a wave
+// skips the MFMAs of its 32-row token tiles that hold pad rows only
+template <int WBITS, bool BF16, int STAGE, int BN, int BM, int WN, int NW, int OCC, bool SKIP>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) {
+    constexpr int NT = NW * 64;
+    constexpr int WM = NW / WN;
+    constexpr int TI = BN / WN / 32;                      // 32-row weight tiles per wave
+    constexpr int TJ = BM / WM / 32;                      // 32-row token tiles per wave
+    constexpr int WPIECES = (BN / TILE_ROWS) * 64 / NT;  // weight pieces (16 rows x 64 ch over 64 lanes) per thread
+    constexpr int TPIECES = BM * (PF_BK / 8) / NT;       // 16-byte token pieces per thread
     constexpr int A_BYTES = BN * PF_ROWB, B_BYTES = BM * PF_ROWB;
     static_assert(TI >= 1 && TJ >= 1 && WPIECES >= 1 && TPIECES >= 1, "tile shape");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[A_BYTES + B_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -61,10 +66,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
     if (row0 >= *g.ntpp) return;
     const int e = g.expert_ids[row0 / g.block_size];
 
-    if (g.sorted[row0] >= T) {  // a slice of pad rows only (blocks larger than 128)
+    if (g.sorted[row0] >= T) {  // a slice of pad rows only (blocks larger than BM)
         if constexpr (STAGE == STAGE_GATE_UP) {
             const int N = g.n_out / 2;
-            for (int k = tid; k < BM * (BN / 2); k += PF_THREADS)
+            for (int k = tid; k < BM * (BN / 2); k += NT)
                 static_cast<uint16_t*>(g.out)[(size_t)(row0 + k / (BN / 2)) * N + ntile * (BN / 2) + k % (BN / 2)] = 0;
         }
         return;
@@ -72,7 +77,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
 
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     const int C = g.k_in / KCHUNK;  // packed chunks per 16-row tile
-    const int STEPS = g.k_in / PF_BK;
+    // K slice of this workgroup (only DOWN is ever split)
+    const int steps_per = g.k_in / PF_BK / (int)gridDim.z;
+    const int step0 = (int)blockIdx.z * steps_per;
+    const int step_end = step0 + steps_per;
     const size_t expert_bytes = (size_t)(g.n_out / TILE_ROWS) * C * CHUNK_BYTES;
     const uint16_t* se = g.s + (size_t)e * g.groups * g.n_out;
 
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
     int wrow[WPIECES];
 #pragma unroll
     for (int i = 0; i < WPIECES; ++i) {
-        const int piece = tid + PF_THREADS * i;
+        const int piece = tid + NT * i;
         const int rt = piece >> 6, l = piece & 63;
         wsrc[i] = we + (size_t)(ntile * (BN / TILE_ROWS) + rt) * C * CHUNK_BYTES + l * 16;
         wrow[i] = rt * TILE_ROWS + (l & 15);
@@ -92,59 +100,54 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
     const uint16_t* tsrc[TPIECES];
 #pragma unroll
     for (int i = 0; i < TPIECES; ++i) {
-        const int id = tid + PF_THREADS * i;
-        const int r = id >> 3, ch = id & 7;
-        const int p = row0 + r;
+        const int id = tid + NT * i;
+        const int p = row0 + (id >> 3);
         const int pair = g.sorted[p];
         const int src = g.a_direct ? p : (pair < T ? pair / g.topk : 0);
-        tsrc[i] = g.a + (size_t)src * g.k_in + ch * 8;
+        tsrc[i] = g.a + (size_t)src * g.k_in + (id & 7) * 8;
     }
 
-    // two register sets: data of even / odd K steps
-    u32x4 wv[2][WPIECES];
-    u32x2 wv4[2][WPIECES];
-    uint32_t sc[2][WPIECES];
-    u32x4 tv[2][TPIECES];
-
-    auto gload = [&](int step, auto SET) {
-        constexpr int set = decltype(SET)::value;
+    u32x4 wv[WPIECES];
+    u32x2 wv4[WPIECES];
+    uint32_t sc[WPIECES];
+    u32x4 tv[TPIECES];
+    auto gload = [&](int step) {
         if constexpr (WBITS == 8) {
 #pragma unroll
-            for (int i = 0; i < WPIECES; ++i) wv[set][i] = ldg128_stream(wsrc[i] + (size_t)step * CHUNK_BYTES);
+            for (int i = 0; i < WPIECES; ++i) wv[i] = ldg128_stream(wsrc[i] + (size_t)step * CHUNK_BYTES);
         } else {
             const int c = step >> 1, half = step & 1;  // a 128-channel chunk spans two K steps
 #pragma unroll
             for (int i = 0; i < WPIECES; ++i)
-                wv4[set][i] = __builtin_nontemporal_load(
+                wv4[i] = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x2*>(wsrc[i] + (size_t)c * CHUNK_BYTES + 8 * half));
             const int grp = g.groups > 1 ? c : 0;
 #pragma unroll
-            for (int i = 0; i < WPIECES; ++i) sc[set][i] = se[(size_t)grp * g.n_out + ntile * BN + wrow[i]];
+            for (int i = 0; i < WPIECES; ++i) sc[i] = se[(size_t)grp * g.n_out + ntile * BN + wrow[i]];
         }
 #pragma unroll
-        for (int i = 0; i < TPIECES; ++i) tv[set][i] = ldg128(tsrc[i] + step * PF_BK);
+        for (int i = 0; i < TPIECES; ++i) tv[i] = ldg128(tsrc[i] + step * PF_BK);
     };
-    // store unit u of one K step: weight units (piece, half) first, then token pieces
-    constexpr int WUNITS = 2 * WPIECES;
-    constexpr int UNITS = WUNITS + TPIECES;
-    auto store_unit = [&](auto SET, int u) {
-        constexpr int set = decltype(SET)::value;  // register set, also the LDS buffer it goes to
-        uint8_t* As = lds + set * (A_BYTES + B_BYTES);
-        uint8_t* Bs = As + A_BYTES;
-        if (u < WUNITS) {
-            const int i = u >> 1, s = u & 1;
-            u32x4 v;
-            if constexpr (WBITS == 8) {
-                v = dequant_w8x8<BF16>(wv[set][i][2 * s], wv[set][i][2 * s + 1]);
-            } else {
-                const uint32_t sv = sc[set][i];
-                v = dequant_w4_f16_scaled(wv4[set][i][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+    auto lds_store = [&]() {
+        uint8_t* As = lds;
+        uint8_t* Bs = lds + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < WPIECES; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 v;
+                if constexpr (WBITS == 8) {
+                    v = dequant_w8x8<BF16>(wv[i][2 * s], wv[i][2 * s + 1]);
+                } else {
+                    const uint32_t sv = sc[i];
+                    v = dequant_w4_f16_scaled(wv4[i][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+                }
+                *reinterpret_cast<u32x4*>(As + lds_off(wrow[i], 4 * s + wlg)) = v;
             }
-            *reinterpret_cast<u32x4*>(As + lds_off(wrow[i], 4 * s + wlg)) = v;
-        } else {
-            const int i = u - WUNITS;
-            const int id = tid + PF_THREADS * i;
-            *reinterpret_cast<u32x4*>(Bs + lds_off(id >> 3, id & 7)) = tv[set][i];
+#pragma unroll
+        for (int i = 0; i < TPIECES; ++i) {
+            const int id = tid + NT * i;
+            *reinterpret_cast<u32x4*>(Bs + lds_off(id >> 3, id & 7)) = tv[i];
         }
     };
 
@@ -158,9 +161,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    int aoff[TI], boff[TJ];  // LDS row byte offsets and swizzles of this lane's operand rows
-    int aswz[TI], bswz[TJ];
+    int aoff[TI], boff[TJ], aswz[TI], bswz[TJ];  // LDS row offsets and swizzles of this lane's operand rows
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
         const int r = (BN / WN) * wn + 32 * i + (lane & 31);
@@ -174,69 +175,47 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
         bswz[j] = lds_swz(r);
     }
     const int khalf = lane >> 5;
-
-    // one K step: MFMAs from buffer BUF; with NEXT, dequantize and store the
-    // following step (register set BUF ^ 1) into the other buffer in between
-    auto step_body = [&](auto BUF, auto NEXT) {
-        constexpr int buf = decltype(BUF)::value;
-        constexpr bool next = decltype(NEXT)::value;
-        const uint8_t* base = lds + buf * (A_BYTES + B_BYTES);
-        u32x4 a[2][TI], b[2][TJ];
-        auto read_ops = [&](int kk, int x) {
-            const int ch = 2 * kk + khalf;
+    // 32-row token tiles of this wave that hold a valid row; the valid rows of
+    // a tile are a prefix (the alignment pads each expert's rows at the end)
+    int jact = TJ;
+    if constexpr (SKIP) {
+        jact = 0;
 #pragma unroll
-            for (int i = 0; i < TI; ++i)
-                a[x][i] = *reinterpret_cast<const u32x4*>(base + aoff[i] + ((ch ^ aswz[i]) << 4));
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-                b[x][j] = *reinterpret_cast<const u32x4*>(base + boff[j] + ((ch ^ bswz[j]) << 4));
-        };
-        read_ops(0, 0);
+        for (int j = 0; j < TJ; ++j)
+            jact += __builtin_amdgcn_readfirstlane(g.sorted[row0 + (BM / WM) * wm + 32 * j]) < T ? 1 : 0;
+    }
+    auto compute = [&]() {
 #pragma unroll
         for (int kk = 0; kk < PF_BK / 16; ++kk) {
-            if (kk + 1 < PF_BK / 16) read_ops(kk + 1, (kk + 1) & 1);
+            const int ch = 2 * kk + khalf;
+            u32x4 a[TI], b[TJ];
 #pragma unroll
-            for (int i = 0; i < TI; ++i)
+            for (int i = 0; i < TI; ++i) a[i] = *reinterpret_cast<const u32x4*>(lds + aoff[i] + ((ch ^ aswz[i]) << 4));
 #pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    acc[i][j] = mfma32x32x16<BF16>(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
-            if constexpr (next) {
+            for (int j = 0; j < TJ; ++j)
+                if (j < jact) b[j] = *reinterpret_cast<const u32x4*>(lds + boff[j] + ((ch ^ bswz[j]) << 4));
 #pragma unroll
-                for (int u = kk * UNITS / (PF_BK / 16); u < (kk + 1) * UNITS / (PF_BK / 16); ++u)
-                    store_unit(std::integral_constant<int, buf ^ 1>{}, u);
-            }
+            for (int j = 0; j < TJ; ++j)
+                if (j < jact) {
+#pragma unroll
+                    for (int i = 0; i < TI; ++i) acc[i][j] = mfma32x32x16<BF16>(a[i], b[j], acc[i][j]);
+                }
         }
     };
-    const std::integral_constant<int, 0> B0{};
-    const std::integral_constant<int, 1> B1{};
-    const std::true_type MORE{};
-    const std::false_type LAST{};
 
-    // K steps two at a time so every buffer and register-set index is static
-    gload(0, B0);
-    if (STEPS > 1) gload(1, B1);
-#pragma unroll
-    for (int u = 0; u < UNITS; ++u) store_unit(B0, u);
-    if (STEPS > 2) gload(2, B0);
-    __syncthreads();
-    int step = 0;
-    for (; step + 2 < STEPS; step += 2) {
-        step_body(B0, MORE);
-        gload(min(step + 3, STEPS - 1), B1);  // the last step is re-read near the end
+    gload(step0);
+    for (int step = step0; step < step_end; ++step) {
+        lds_store();
         __syncthreads();
-        step_body(B1, MORE);
-        gload(min(step + 4, STEPS - 1), B0);
+        gload(min(step + 1, step_end - 1));  // the last step is loaded twice, keeping the loop branch-free
+        compute();
         __syncthreads();
-    }
-    if (step + 1 < STEPS) {
-        step_body(B0, MORE);
-        __syncthreads();
-        step_body(B1, LAST);
-    } else {
-        step_body(B0, LAST);
     }
 
     // epilogue
+    float* yslab = nullptr;
+    if constexpr (STAGE != STAGE_GATE_UP)
+        yslab = static_cast<float*>(g.out) + (size_t)blockIdx.z * ((size_t)T * g.n_out);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
         const int p = row0 + (BM / WM) * wm + 32 * j + (lane & 31);
@@ -280,8 +259,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
                             if constexpr (WBITS == 8) v *= act_to_f32<BF16>(se[wbase + rr + q]);
                             o[q] = v * rw;
                         }
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (size_t)pair * g.n_out + wbase + rr) =
-                            o;
+                        *reinterpret_cast<f32x4*>(yslab + (size_t)pair * g.n_out + wbase + rr) = o;
                     }
                 }
             }
@@ -289,37 +267,85 @@ __global__ __launch_bounds__(PF_THREADS, 2) void gemm_prefill_kernel(GemmArgs g)
     }
 }
 
-template <int WBITS, bool BF16, int STAGE, int BN, int BM, int WN>
-static void launch_prefill_cfg(const GemmArgs& g, hipStream_t s) {
-    const dim3 grid(g.n_out / BN, g.cap / BM);
-    hipLaunchKernelGGL((gemm_prefill_kernel<WBITS, BF16, STAGE, BN, BM, WN>), grid, dim3(PF_THREADS), 0, s, g);
+// ------------------------------------------------------------------ plans
+// Tile shapes, chosen by timing on MI355X with random data:
+//   WIDE8  256 x 128, 8 waves of 64 x 64, one workgroup per CU: the fastest
+//          int8 GATE_UP shape for large grids with little padding;
+//   WIDE4  256 x 128, 4 waves of 128 x 64 with pad-tile skipping, two
+//          workgroups per CU: int4, and int8 with much padding;
+//   SQ     128 x 128, 4 waves of 64 x 64 with pad-tile skipping, three
+//          workgroups per CU: small grids (with K split for DOWN);
+//   THIN   128 x 64, 4 waves of 64 x 32: blocks of 64 token rows.
+enum PrefillShape { PF_WIDE8, PF_WIDE4, PF_SQ, PF_THIN };
+
+// rough count of 128-row token tiles: T rows plus a partial tile
+static long est_mtiles(int T) { return (long)T / 128 + 1; }
+
+// rounds of SQ workgroups (3 per CU) needed for tiles, in units of one full-K workgroup
+static double sq_rounds(long tiles, int ks) {
+    const long slots = 3L * 256;
+    return (double)((tiles * ks + slots - 1) / slots) / ks;
 }
 
-// 128-row token tiles (blocks of 128 or more): 128 x 128 tiles, 2 x 2 waves;
-// 64-row token tiles (blocks of 64, less padding for thin experts): 256 weight
-// rows over 4 waves when n_out allows, else 128 x 64 tiles
+int prefill_down_split(int T, int n_out, int k_in) {
+    if (n_out % 128 != 0 || k_in % PF_BK != 0) return 1;
+    const long tiles = (long)(n_out / 128) * est_mtiles(T);
+    const int steps = k_in / PF_BK;
+    int best = 1;
+    double best_t = sq_rounds(tiles, 1);
+    for (int ks = 2; ks <= 4; ks *= 2) {
+        if (steps % ks != 0 || steps / ks < 16) break;
+        const double t = sq_rounds(tiles, ks);
+        if (t < 0.85 * best_t) best = ks, best_t = t;
+    }
+    return best;
+}
+
+static PrefillShape prefill_shape(int wbits, int stage, const GemmArgs& g, int ksplit) {
+    if (g.block_size == 64) return PF_THIN;
+    if (ksplit > 1 || g.n_out % 256 != 0) return PF_SQ;
+    const int T = g.M * g.topk;
+    const long tiles256 = (long)(g.n_out / 256) * est_mtiles(T);
+    const double pad = (double)std::min(T, g.E) * 64 / (T + (double)std::min(T, g.E) * 64);  // expected pad share
+    if (wbits == 8 && stage != STAGE_DOWN && tiles256 >= 1024 && pad <= 0.25) return PF_WIDE8;
+    return tiles256 >= 512 ? PF_WIDE4 : PF_SQ;
+}
+
+template <int WBITS, bool BF16, int STAGE, int BN, int BM, int WN, int NW, int OCC, bool SKIP>
+static void launch_prefill_cfg(const GemmArgs& g, int ksplit, hipStream_t s) {
+    const dim3 grid(g.n_out / BN, g.cap / BM, ksplit);
+    hipLaunchKernelGGL((gemm_prefill_kernel<WBITS, BF16, STAGE, BN, BM, WN, NW, OCC, SKIP>), grid, dim3(NW * 64), 0, s,
+                       g);
+}
+
 template <int WBITS, bool BF16, int STAGE>
-static void launch_prefill_st(const GemmArgs& g, hipStream_t s) {
-    if (g.block_size % 128 == 0) launch_prefill_cfg<WBITS, BF16, STAGE, 128, 128, 2>(g, s);
-    else if (g.n_out % 256 == 0) launch_prefill_cfg<WBITS, BF16, STAGE, 256, 64, 4>(g, s);
-    else launch_prefill_cfg<WBITS, BF16, STAGE, 128, 64, 2>(g, s);
+static void launch_prefill_st(const GemmArgs& g, int ksplit, hipStream_t s) {
+    switch (prefill_shape(WBITS, STAGE, g, ksplit)) {
+        case PF_WIDE8: launch_prefill_cfg<WBITS, BF16, STAGE, 256, 128, 4, 8, 1, false>(g, ksplit, s); break;
+        case PF_WIDE4: launch_prefill_cfg<WBITS, BF16, STAGE, 256, 128, 2, 4, 2, true>(g, ksplit, s); break;
+        case PF_SQ: launch_prefill_cfg<WBITS, BF16, STAGE, 128, 128, 2, 4, 3, true>(g, ksplit, s); break;
+        default: launch_prefill_cfg<WBITS, BF16, STAGE, 128, 64, 2, 4, 3, true>(g, ksplit, s); break;
+    }
 }
 
 template <int WBITS, bool BF16>
-static void launch_prefill_s(int stage, const GemmArgs& g, hipStream_t s) {
-    if (stage == STAGE_GATE_UP) launch_prefill_st<WBITS, BF16, STAGE_GATE_UP>(g, s);
-    else if (stage == STAGE_DOWN) launch_prefill_st<WBITS, BF16, STAGE_DOWN>(g, s);
-    else launch_prefill_st<WBITS, BF16, STAGE_RAW>(g, s);
+static void launch_prefill_s(int stage, const GemmArgs& g, int ksplit, hipStream_t s) {
+    if (stage == STAGE_GATE_UP) launch_prefill_st<WBITS, BF16, STAGE_GATE_UP>(g, 1, s);
+    else if (stage == STAGE_DOWN) launch_prefill_st<WBITS, BF16, STAGE_DOWN>(g, ksplit, s);
+    else launch_prefill_st<WBITS, BF16, STAGE_RAW>(g, 1, s);
 }
 
 bool prefill_supported(int n_out, int k_in, int block_size) {
     return (block_size == 64 || block_size % 128 == 0) && n_out % 128 == 0 && k_in % PF_BK == 0;
 }
 
-void launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s) {
-    if (wbits == 4) launch_prefill_s<4, false>(stage, g, s);
-    else if (bf16) launch_prefill_s<8, true>(stage, g, s);
-    else launch_prefill_s<8, false>(stage, g, s);
+int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s) {
+    const int ksplit =
+        (stage == STAGE_DOWN && g.block_size % 128 == 0) ? prefill_down_split(g.M * g.topk, g.n_out, g.k_in) : 1;
+    if (wbits == 4) launch_prefill_s<4, false>(stage, g, ksplit, s);
+    else if (bf16) launch_prefill_s<8, true>(stage, g, ksplit, s);
+    else launch_prefill_s<8, false>(stage, g, ksplit, s);
+    return ksplit;
 }
 
 }  // namespace wq

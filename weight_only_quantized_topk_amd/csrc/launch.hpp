@@ -45,16 +45,21 @@ struct GemmArgs {
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
 void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
-// large-batch path: 256 weight rows x 128 token rows through LDS
+// large-batch path: 256 or 128 weight rows x 128 (or 64) token rows through LDS
 bool prefill_supported(int n_out, int k_in, int block_size);
-void launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
+// K slices of the large-batch DOWN stage for T = M*topk rows (1, 2 or 4); the
+// DOWN workspace holds that many fp32 slabs of T x n_out
+int prefill_down_split(int T, int n_out, int k_in);
+// returns the number of K slices (Y slabs) it wrote
+int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
 
 // act-order: A1[p, k'] = x[token(p), perm[expert(p), k']] for sorted rows p
 void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* sorted, const int32_t* expert_ids,
                         const int32_t* ntpp, int M, int topk, int k_in, int block_size, int cap, uint16_t* a1,
                         hipStream_t s);
-// out[m, c] = sum_j Y[m*topk + j, c] (ascending j, fp32), rounded to act
-void launch_combine(const float* y, int M, int topk, int n, bool bf16, uint16_t* out, hipStream_t s);
+// out[m, c] = sum_j sum_z Y[z][m*topk + j, c] over top-k slots j and K slices z
+// (ascending, fp32), rounded to act; slab z starts at y + z * M*topk*n
+void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf16, uint16_t* out, hipStream_t s);
 
 void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                      const uint16_t* scales, uint16_t* y, hipStream_t s);

@@ -19,7 +19,6 @@ from ._lib import WQ_STAGE_DOWN, WQ_STAGE_GATE_UP
 
 DECODE_BLOCK = 16    # token block of the small-batch kernel
 PREFILL_BLOCK = 128  # token block of the large-batch kernel
-PREFILL_BLOCK_THIN = 64
 
 
 @dataclass
@@ -75,18 +74,14 @@ def pack_moe(bits: int, w1q: np.ndarray, s1_bits: np.ndarray, w2q: np.ndarray, s
 
 def choose_block_size(M: int, topk: int, E: int, bits: int = 8) -> int:
     """Batch-size heuristic: expected rows per touched expert decides between the
-    small-batch kernel (block 16) and the large-batch kernel (block 64 or 128).
-    Blocks of 64 halve the padding of thin experts; int4 dequantisation costs
-    more VALU per MFMA, so int4 keeps 128-row token tiles."""
+    small-batch kernel (block 16) and the large-batch kernel (block 128; its
+    64-row tiles were slower than 128-row tiles with their extra padding at
+    every measured shape, so block 64 is left to explicit callers)."""
     T = M * topk
     if T == 0:
         return DECODE_BLOCK
     rows_per_expert = T / min(E, T)
-    if rows_per_expert <= 64:
-        return DECODE_BLOCK
-    if bits == 4 or rows_per_expert >= 512:
-        return PREFILL_BLOCK
-    return PREFILL_BLOCK_THIN
+    return DECODE_BLOCK if rows_per_expert <= 64 else PREFILL_BLOCK
 
 
 class MoERunner:
