@@ -9,17 +9,28 @@ HBM.  The default workload is the Mixtral-8x7B-shaped W8A16 layer (E=8, top-2,
 K=4096, N=14336, int8 per-column weights, bf16 activations) at M=1024, the
 prompt length of the end-to-end latency workload in "[Kernel] W8A16 Int8
 inside FusedMoE" (vLLM PR 7415, latency table).  The other batch sizes of that
-layer's sweep are timed too and reported under "sweep".
+layer's sweep are timed too and reported under "sweep"; the other workloads
+(int4 act-order Mixtral, the 2:4-sparse int4 linear layer, the DeepSeek-V2
+shaped int8 layer) under "rows".
+
+Timing: before every step (warm-up and timed) 1 GiB of scratch memory is
+written, outside the timed span, so the weights come from HBM and not from
+the 256 MB last-level cache; each step is bracketed by stream events, and the
+reported time per step is the mean over the K timed steps of its event span
+(route -> combine).  The wall time of the K steps, flushes included, is
+reported as well.
 
 Printed: one JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel (the gate/up GEMM, timed with stream events over the timed
-steps), and the CPU oracle timed on a bounded sample of the same batch.
+dominant kernel (the gate/up GEMM, timed with stream events), and the CPU
+oracle timed on a bounded sample of the same batch.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,17 +42,44 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense
-SPARSE_NOTE = "2:4 counts nonzero flops against the dense peak"
+FLUSH_BYTES = 1 << 30
+# rocprofv3 counter summary of the large-batch gate/up kernel at the default
+# workload; its traffic figure is used only while the kernel sources hash the same
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill_gate_up_mixtral_w8a16_m1024.md")
+KERNEL_SOURCES = ["gemm_prefill.hip", "common.hpp", "launch.hpp"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "weight_only_quantized_topk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, or None when absent or taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    mh = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    mt = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not mh or not mt or mh.group(1) != kernel_source_hash():
+        return None
+    return int(mt.group(1))
+
+
 def moe_alg_counts(spec, M, ids_np, packed):
     """Algorithmic bytes / flops of the gate/up GEMM launch and of the layer.
-    Bytes: packed weights and scales of the experts the batch touches, the
-    activations read and the outputs written (no padding rows, no re-reads)."""
+    Bytes: packed weights and scales of the experts the batch touches (plus the
+    act-order permutation), the activations read and the outputs written (no
+    padding rows, no re-reads, no H / Y round trips)."""
     touched = int(np.unique(ids_np).size)
     T = M * spec.topk
     E = spec.E
@@ -50,32 +88,59 @@ def moe_alg_counts(spec, M, ids_np, packed):
     s1_bytes = packed.s1.numel() * 2 // E * touched
     w2_bytes = packed.w2.numel() // E * touched
     s2_bytes = packed.s2.numel() * 2 // E * touched
+    perm_bytes = touched * spec.K * 4 if spec.act_order else 0
     g1 = {
         "bytes": w1_bytes + s1_bytes + M * spec.K * act + T * spec.N * act,
         "flops": 2 * T * (2 * spec.N) * spec.K,
     }
     layer = {
-        "bytes": w1_bytes + s1_bytes + w2_bytes + s2_bytes + 2 * M * spec.K * act,
+        "bytes": w1_bytes + s1_bytes + w2_bytes + s2_bytes + perm_bytes + 2 * M * spec.K * act,
         "flops": 6 * T * spec.N * spec.K,
     }
     return touched, g1, layer
 
 
-def time_layer(torch, runner, x, lg, steps, warmup):
-    """Warm up, then time exactly `steps` steps between two synchronisations;
-    stream events after alignment / gate-up / down give per-stage durations."""
-    for _ in range(warmup):
-        runner(x, lg)
-    torch.cuda.synchronize()
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        runner(x, lg, marks=marks[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    g1 = np.array([m[0].elapsed_time(m[1]) for m in marks])     # ms
-    g2 = np.array([m[1].elapsed_time(m[2]) for m in marks])
-    return (t1 - t0) * 1e3 / steps, float(g1.mean()), float(g2.mean())
+def rates(nbytes, flops, ms):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"GBps": gbps, "TFLOPs": tf, "frac_hbm": gbps / HBM_PEAK_GBPS, "frac_mfma": tf / 2500.0}
+
+
+def rounded(d):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+class Timer:
+    """Per-step stream events with a cache flush (1 GiB write) before every step."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.n = 0
+
+    def flush(self):
+        self.n += 1
+        self.scratch.fill_(self.n & 0xFF)
+
+    def run(self, step, steps, warmup, nmarks):
+        """step(marks) runs one step, recording marks (a list of nmarks events) or
+        nothing.  Returns (per-step span ms from the step start to each mark
+        [steps, nmarks], wall ms of the timed loop per step)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.flush()
+            step(None)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nmarks + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.flush()
+            ev[i][0].record()
+            step(ev[i][1:])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        spans = np.array([[e[0].elapsed_time(e[k]) for k in range(1, nmarks + 1)] for e in ev])
+        return spans, wall
 
 
 def cpu_baseline(spec, wts, toks, seconds):
@@ -101,6 +166,77 @@ def cpu_baseline(spec, wts, toks, seconds):
                       "accumulation, OpenMP over (token, slot, output row)" % (n, toks.M, dt)}
 
 
+def measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup):
+    act = torch.float16 if spec.act == "f16" else torch.bfloat16
+    toks = gen.make_tokens(spec, m)
+    x = torch.from_numpy(toks.x.view(np.int16)).cuda().view(act)
+    lg = torch.from_numpy(toks.logits).cuda()
+    runner = wq.MoERunner(packed, m, spec.topk, spec.renormalize)
+    spans, wall = timer.run(lambda marks: runner(x, lg, marks=marks), steps, warmup, 3)
+    ra, g1e, lay = spans[:, 0], spans[:, 1] - spans[:, 0], spans[:, 2]
+    down = spans[:, 2] - spans[:, 1]
+    ids_np = runner.ids.cpu().numpy()
+    touched, g1, layer = moe_alg_counts(spec, m, ids_np, packed)
+    ms = float(lay.mean())
+    r = dict(M=m, ms_per_step=ms, ms_per_step_median=float(np.median(lay)), wall_ms_per_step=wall,
+             tokens_per_s=m / (ms * 1e-3), route_align_ms=float(ra.mean()), gate_up_ms=float(g1e.mean()),
+             down_ms=float(down.mean()), touched_experts=touched, block_size=runner.bs,
+             gate_up_alg_bytes=g1["bytes"], gate_up_alg_flops=g1["flops"],
+             layer_alg_bytes=layer["bytes"], layer_alg_flops=layer["flops"])
+    r.update({"gate_up_" + k: v for k, v in rates(g1["bytes"], g1["flops"], r["gate_up_ms"]).items()})
+    r.update({"layer_" + k: v for k, v in rates(layer["bytes"], layer["flops"], ms).items()})
+    return toks, r
+
+
+def measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup):
+    vd, md, sd = dev
+    x = torch.from_numpy(gen.make_sparse_x(spec, m).view(np.int16)).cuda().view(torch.float16)
+    y = torch.empty((m, spec.N), dtype=torch.float16, device="cuda")
+
+    def step(marks):
+        wq.sparse24_w4a16_gemm(x, vd, md, sd, spec.N, out=y)
+        if marks:
+            marks[0].record()
+
+    spans, wall = timer.run(step, steps, warmup, 1)
+    ms = float(spans[:, 0].mean())
+    nbytes = vd.numel() + md.numel() + sd.numel() * 2 + m * spec.K * 2 + m * spec.N * 2
+    flops = m * spec.N * spec.K   # nonzero multiply-adds x 2 = M*N*K for 2:4
+    r = dict(M=m, ms_per_step=ms, ms_per_step_median=float(np.median(spans[:, 0])), wall_ms_per_step=wall,
+             tokens_per_s=m / (ms * 1e-3), alg_bytes=int(nbytes), alg_flops=int(flops))
+    r.update(rates(nbytes, flops, ms))
+    return r
+
+
+def bench_rows(torch, wq, gen, timer, steps, warmup):
+    """The other workloads at their batch sizes: layer time, stage times and
+    both roofline fractions (HBM on algorithmic bytes, MFMA on algorithmic flops)."""
+    rows = []
+    for cid in (3, 5):
+        spec = gen.CONFIGS[cid]
+        act = torch.float16 if spec.act == "f16" else torch.bfloat16
+        log("bench: rows: generating and packing %s" % spec.name)
+        wts = gen.make_moe_weights(spec)
+        packed = wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2, act, spec.group_size, wts.g1, wts.g2)
+        del wts
+        for m in spec.m_sweep:
+            _, r = measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup)
+            log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
+            rows.append(dict(workload=spec.name, **rounded(r)))
+        del packed
+        torch.cuda.empty_cache()
+    spec = gen.CFG4
+    log("bench: rows: generating and packing %s" % spec.name)
+    sw = gen.make_sparse_weights(spec)
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s)
+    dev = (torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(), torch.from_numpy(sp.view(np.int16)).cuda())
+    for m in spec.m_sweep:
+        r = measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup)
+        log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
+        rows.append(dict(workload=spec.name, **rounded(r)))
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,9 +244,13 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 5])
     ap.add_argument("--m", type=int, default=None, help="batch size (default: the largest of the config's sweep)")
-    ap.add_argument("--no-sweep", action="store_true", help="time only --m")
+    ap.add_argument("--no-sweep", action="store_true", help="time only --m of the chosen workload")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a device-to-device copy of MIB MiB twice: the known-size reference that "
+                         "scales hardware byte counters (FETCH_SIZE / WRITE_SIZE) read under a profiler")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -125,6 +265,16 @@ def main(argv=None):
 
     wq.load()  # fails loudly without the HIP library
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copied %d bytes twice (counter calibration)" % n)
+        del src, dst
+    timer = Timer(torch)
     spec = gen.CONFIGS[args.config]
     M = args.m or max(spec.m_sweep)
     act = torch.float16 if spec.act == "f16" else torch.bfloat16
@@ -133,34 +283,17 @@ def main(argv=None):
     packed = wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2, act, spec.group_size, wts.g1, wts.g2)
     torch.cuda.synchronize()
 
-    def measure(m, steps, warmup):
-        toks = gen.make_tokens(spec, m)
-        x = torch.from_numpy(toks.x.view(np.int16)).cuda().view(act)
-        lg = torch.from_numpy(toks.logits).cuda()
-        runner = wq.MoERunner(packed, m, spec.topk, spec.renormalize)
-        ms, g1_ms, g2_ms = time_layer(torch, runner, x, lg, steps, warmup)
-        ids_np = runner.ids.cpu().numpy()
-        touched, g1, layer = moe_alg_counts(spec, m, ids_np, packed)
-        return toks, ids_np, dict(M=m, ms_per_step=ms, tokens_per_s=m / (ms * 1e-3), gate_up_ms=g1_ms,
-                                  down_ms=g2_ms, touched_experts=touched, block_size=runner.bs,
-                                  gate_up_alg_bytes=g1["bytes"], gate_up_alg_flops=g1["flops"],
-                                  layer_alg_bytes=layer["bytes"], layer_alg_flops=layer["flops"],
-                                  gate_up_GBps=g1["bytes"] / (g1_ms * 1e-3) / 1e9,
-                                  gate_up_TFLOPs=g1["flops"] / (g1_ms * 1e-3) / 1e12,
-                                  layer_GBps=layer["bytes"] / (ms * 1e-3) / 1e9,
-                                  layer_TFLOPs=layer["flops"] / (ms * 1e-3) / 1e12)
-
     log("bench: timing M=%d, %d steps after %d warmup" % (M, args.steps, args.warmup))
-    toks, ids_np, head = measure(M, args.steps, args.warmup)
-    log("bench: M=%d %.3f ms/step" % (M, head["ms_per_step"]))
+    toks, head = measure_moe(torch, wq, gen, timer, spec, packed, M, args.steps, args.warmup)
+    log("bench: M=%d %.4f ms/step" % (M, head["ms_per_step"]))
 
     sweep = []
     if not args.no_sweep:
         for m in spec.m_sweep:
             if m == M:
                 continue
-            _, _, r = measure(m, max(10, args.steps), args.warmup)
-            log("bench: sweep M=%d %.3f ms/step" % (m, r["ms_per_step"]))
+            _, r = measure_moe(torch, wq, gen, timer, spec, packed, m, max(10, args.steps), args.warmup)
+            log("bench: sweep M=%d %.4f ms/step" % (m, r["ms_per_step"]))
             sweep.append(r)
         sweep.append(head)
         sweep.sort(key=lambda r: r["M"])
@@ -178,17 +311,25 @@ def main(argv=None):
         achieved = head["gate_up_GBps"]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4)}
-    roof["kernel"] = "gemm_%s_kernel gate/up (W%dA16)" % ("prefill" if head["block_size"] >= 64 else "decode",
-                                                        spec.bits)
+    large = head["block_size"] >= 64
+    roof["kernel"] = "gemm_%s_kernel, gate/up stage (W%dA16)" % ("prefill" if large else "decode", spec.bits)
     roof["kernel_avg_ms"] = round(head["gate_up_ms"], 4)
     roof["alg_bytes_per_launch"] = int(head["gate_up_alg_bytes"])
     roof["alg_flops_per_launch"] = int(head["gate_up_alg_flops"])
-    roof["traffic"] = None
+    default_workload = args.config == 2 and M == 1024
+    roof["traffic"] = stored_traffic() if (default_workload and large) else None
+
+    rows = None
+    if not args.no_rows:
+        del packed, wts
+        torch.cuda.empty_cache()
+        rows = bench_rows(torch, wq, gen, timer, max(10, args.steps), args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
-        cpu = cpu_baseline(spec, wts, toks, args.cpu_seconds)
+        wts_cpu = gen.make_moe_weights(spec) if not args.no_rows else wts
+        cpu = cpu_baseline(spec, wts_cpu, toks, args.cpu_seconds)
 
     res = {
         "metric": "fused-MoE W%dA16 tokens/s" % spec.bits,
@@ -198,6 +339,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(head["ms_per_step"], 4),
+        "wall_ms_per_step": round(head["wall_ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -207,12 +349,14 @@ def main(argv=None):
                                % (spec.name, spec.E, spec.topk, spec.K, spec.N,
                                   "int8 per-column" if spec.bits == 8 else "int4 group-128", M),
                    "M": M, "E": spec.E, "topk": spec.topk, "K": spec.K, "N": spec.N, "bits": spec.bits,
-                   "block_size": head["block_size"], "touched_experts": head["touched_experts"]},
+                   "block_size": head["block_size"], "touched_experts": head["touched_experts"],
+                   "cache": "1 GiB scratch written before every step, outside the timed span"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"GBps": round(head["layer_GBps"], 1), "TFLOPs": round(head["layer_TFLOPs"], 2),
                   "alg_bytes": int(head["layer_alg_bytes"]), "alg_flops": int(head["layer_alg_flops"])},
-        "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
+        "sweep": [rounded(r) for r in sweep],
+        "rows": rows,
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -146,7 +146,8 @@ wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block
  *           vary from run to run.
  *  RAW      d_a = x [M, k_in]; d_out = fp32 [M*topk, n_out]:
  *           Z[i, r] = sum_k x[i/topk, k] * W_{expert(i)}[r, k], packed row order.
- * The workspace size comes from moe_gemm_workspace_bytes(); pass 0 / NULL if
+ * The workspace size comes from moe_gemm_workspace_bytes() with the call's
+ * stage, M, topk, E, n_out, k_in, capacity and act-order flag; pass 0 / NULL if
  * it returns 0.  Calls sharing a workspace must be stream-ordered.
  */
 typedef struct wq_moe_gemm_desc {
@@ -170,7 +171,8 @@ typedef struct wq_moe_gemm_desc {
     size_t workspace_bytes;
 } wq_moe_gemm_desc;
 
-size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int n_out, int k_in, size_t capacity, int act_order);
+size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, int k_in, size_t capacity,
+                                int act_order);
 wq_status moe_w4a16_gemm(const wq_moe_gemm_desc* d, void* stream);
 wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
 

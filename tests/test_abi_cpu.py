@@ -121,9 +121,13 @@ def test_gemm_validation(fn, kw, expect):
 
 def test_gemm_workspace_sizes():
     L = wq.load()
-    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 1024, 256, 128, 0) == 0
-    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 1024, 256, 128, 1) == 128 * 256 * 2
-    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, 4, 2, 256, 512, 128, 0) == 4 * 2 * 256 * 4
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 8, 1024, 256, 128, 0) == 0
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 8, 1024, 256, 128, 1) == 128 * 256 * 2
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, 4, 2, 8, 256, 512, 128, 0) == 4 * 2 * 256 * 4
+    # long k_in, few output tiles: the DOWN workspace holds 4 fp32 slabs (K split in 4)
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, 300, 2, 8, 256, 4096, 1024, 0) == 4 * 600 * 256 * 4
+    # a large grid is not split
+    assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, 4096, 6, 160, 5120, 1536, 1 << 16, 0) == 4096 * 6 * 5120 * 4
 
 
 def test_sparse_validation():

@@ -94,7 +94,7 @@ def test_raw_exact_integer(bits, bs, act_order):
     say("raw exact", bits, bs, act_order)
     if bits == 4:
         kpd = torch.from_numpy(kp).cuda() if kp is not None else None
-        ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_RAW, M, spec.topk, n_out, K, cap, kp is not None)
+        ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_RAW, M, spec.topk, spec.E, n_out, K, cap, kp is not None)
         work = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
         wq.moe_w4a16_gemm(wq.WQ_STAGE_RAW, xd, M, spec.topk, E, n_out, K, wd, sd, spec.group_size, kpd, st, ex, nt,
                           cap, bs, None, out, work)
@@ -111,7 +111,7 @@ def run_gate_up(spec, p, xd, ids_np, bs):
     M = xd.shape[0]
     st, ex, nt, cap = align_dev(ids_np, spec.E, bs)
     act_order = p.k_perm1 is not None
-    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, M, spec.topk, 2 * spec.N, spec.K, cap, act_order)
+    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, M, spec.topk, spec.E, 2 * spec.N, spec.K, cap, act_order)
     work = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
     h = torch.full((cap, spec.N), float("nan"), dtype=p.act, device="cuda")
     if spec.bits == 4:
@@ -192,7 +192,7 @@ def _check_down(key, bs, M):
         if i < T:
             hs[pos] = h_act[i][h_perm(spec, wts, exn[pos // bs])]
     hd = torch.from_numpy(hs).cuda().to(p.act)
-    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, M, spec.topk, spec.K, spec.N, cap, False)
+    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, M, spec.topk, spec.E, spec.K, spec.N, cap, False)
     work = torch.empty(ws, dtype=torch.uint8, device="cuda")
     out = torch.empty((M, spec.K), dtype=p.act, device="cuda")
     wd = torch.from_numpy(w).cuda()

@@ -74,7 +74,7 @@ def load():
     L.moe_align_capacity.argtypes = [i, i, i, i]
     L.moe_align_capacity.restype = sz
     L.moe_align.argtypes = [p, i, i, i, i, p, p, p, sz, p]
-    L.moe_gemm_workspace_bytes.argtypes = [i, i, i, i, i, sz, i]
+    L.moe_gemm_workspace_bytes.argtypes = [i, i, i, i, i, i, sz, i]
     L.moe_gemm_workspace_bytes.restype = sz
     L.moe_w4a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.moe_w8a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]

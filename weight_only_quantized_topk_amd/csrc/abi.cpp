@@ -184,12 +184,13 @@ wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block
 }
 
 // ---------------------------------------------------------------------------
-size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int n_out, int k_in, size_t capacity, int act_order) {
-    if (M < 0 || topk <= 0 || n_out <= 0 || k_in <= 0) return 0;
+size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, int k_in, size_t capacity,
+                                int act_order) {
+    if (M < 0 || topk <= 0 || E <= 0 || n_out <= 0 || k_in <= 0) return 0;
     size_t b = 0;
     if ((stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_RAW) && act_order) b += round256(capacity * k_in * 2);
     if (stage == WQ_STAGE_DOWN)
-        b += round256((size_t)wq::prefill_down_split(M * topk, n_out, k_in) * M * topk * n_out * sizeof(float));
+        b += round256((size_t)wq::prefill_down_split(M * topk, E, n_out, k_in) * M * topk * n_out * sizeof(float));
     return b;
 }
 
@@ -224,7 +225,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     const bool act_order = d->d_k_perm != nullptr;
     WQ_REQUIRE(!act_order || (wbits == 4 && stage != WQ_STAGE_DOWN), WQ_ERR_INVALID,
                "%s: k_perm only applies to int4 GATE_UP/RAW", who);
-    const size_t ws = moe_gemm_workspace_bytes(stage, d->M, d->topk, d->n_out, d->k_in, d->capacity, act_order);
+    const size_t ws = moe_gemm_workspace_bytes(stage, d->M, d->topk, d->E, d->n_out, d->k_in, d->capacity, act_order);
     WQ_REQUIRE(d->workspace_bytes >= ws, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who, d->workspace_bytes,
                ws);
     if (d->M == 0) return ok();

@@ -278,8 +278,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
 //   THIN   128 x 64, 4 waves of 64 x 32: blocks of 64 token rows.
 enum PrefillShape { PF_WIDE8, PF_WIDE4, PF_SQ, PF_THIN };
 
-// rough count of 128-row token tiles: T rows plus a partial tile
-static long est_mtiles(int T) { return (long)T / 128 + 1; }
+// expected count of 128-row token tiles: T rows plus, per touched expert, a
+// half-filled last tile (at most E experts are touched)
+static long est_mtiles(int T, int E) { return ((long)T + (long)std::min(T, E) * 64 + 127) / 128; }
 
 // rounds of SQ workgroups (3 per CU) needed for tiles, in units of one full-K workgroup
 static double sq_rounds(long tiles, int ks) {
@@ -287,9 +288,9 @@ static double sq_rounds(long tiles, int ks) {
     return (double)((tiles * ks + slots - 1) / slots) / ks;
 }
 
-int prefill_down_split(int T, int n_out, int k_in) {
+int prefill_down_split(int T, int E, int n_out, int k_in) {
     if (n_out % 128 != 0 || k_in % PF_BK != 0) return 1;
-    const long tiles = (long)(n_out / 128) * est_mtiles(T);
+    const long tiles = (long)(n_out / 128) * est_mtiles(T, E);
     const int steps = k_in / PF_BK;
     int best = 1;
     double best_t = sq_rounds(tiles, 1);
@@ -305,7 +306,7 @@ static PrefillShape prefill_shape(int wbits, int stage, const GemmArgs& g, int k
     if (g.block_size == 64) return PF_THIN;
     if (ksplit > 1 || g.n_out % 256 != 0) return PF_SQ;
     const int T = g.M * g.topk;
-    const long tiles256 = (long)(g.n_out / 256) * est_mtiles(T);
+    const long tiles256 = (long)(g.n_out / 256) * est_mtiles(T, g.E);
     const double pad = (double)std::min(T, g.E) * 64 / (T + (double)std::min(T, g.E) * 64);  // expected pad share
     if (wbits == 8 && stage != STAGE_DOWN && tiles256 >= 1024 && pad <= 0.25) return PF_WIDE8;
     return tiles256 >= 512 ? PF_WIDE4 : PF_SQ;
@@ -341,7 +342,7 @@ bool prefill_supported(int n_out, int k_in, int block_size) {
 
 int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s) {
     const int ksplit =
-        (stage == STAGE_DOWN && g.block_size % 128 == 0) ? prefill_down_split(g.M * g.topk, g.n_out, g.k_in) : 1;
+        (stage == STAGE_DOWN && g.block_size % 128 == 0) ? prefill_down_split(g.M * g.topk, g.E, g.n_out, g.k_in) : 1;
     if (wbits == 4) launch_prefill_s<4, false>(stage, g, ksplit, s);
     else if (bf16) launch_prefill_s<8, true>(stage, g, ksplit, s);
     else launch_prefill_s<8, false>(stage, g, ksplit, s);

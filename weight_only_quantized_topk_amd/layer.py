@@ -102,8 +102,8 @@ class MoERunner:
         self.ex = torch.empty(max(self.cap // self.bs, 1), dtype=torch.int32, device=dev)
         self.nt = torch.empty(4, dtype=torch.int32, device=dev)
         act_order = p.k_perm1 is not None
-        ws1 = ops.moe_gemm_workspace_bytes(WQ_STAGE_GATE_UP, M, topk, 2 * p.N, p.K, self.cap, act_order)
-        ws2 = ops.moe_gemm_workspace_bytes(WQ_STAGE_DOWN, M, topk, p.K, p.N, self.cap, False)
+        ws1 = ops.moe_gemm_workspace_bytes(WQ_STAGE_GATE_UP, M, topk, p.E, 2 * p.N, p.K, self.cap, act_order)
+        ws2 = ops.moe_gemm_workspace_bytes(WQ_STAGE_DOWN, M, topk, p.E, p.K, p.N, self.cap, False)
         self.work1 = torch.empty(ws1, dtype=torch.uint8, device=dev) if ws1 else None
         self.work2 = torch.empty(ws2, dtype=torch.uint8, device=dev) if ws2 else None
         self.h = torch.empty((max(self.cap, 1), p.N), dtype=p.act, device=dev)

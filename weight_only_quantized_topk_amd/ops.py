@@ -89,9 +89,9 @@ def moe_align(topk_ids, E: int, block_size: int, capacity: Optional[int] = None,
     return sorted_token_ids, expert_ids, num_tokens_post_padded
 
 
-def moe_gemm_workspace_bytes(stage: int, M: int, topk: int, n_out: int, k_in: int, capacity: int,
+def moe_gemm_workspace_bytes(stage: int, M: int, topk: int, E: int, n_out: int, k_in: int, capacity: int,
                              act_order: bool) -> int:
-    return int(load().moe_gemm_workspace_bytes(stage, M, topk, n_out, k_in, capacity, int(bool(act_order))))
+    return int(load().moe_gemm_workspace_bytes(stage, M, topk, E, n_out, k_in, capacity, int(bool(act_order))))
 
 
 def _gemm(fn_name: str, stage: int, a, M: int, topk: int, E: int, n_out: int, k_in: int, w_packed, scales,
