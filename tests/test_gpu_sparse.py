@@ -48,6 +48,34 @@ def test_sparse_float(M):
     assert_close_fp(y, ref, "sparse M=%d" % M)
 
 
+@pytest.mark.parametrize("M", [1, 16, 40, 100, 200])
+def test_sparse_float_long_k(M):
+    """K = 2304 (9 chunks of 256: a full block of 8 in flight plus a tail) and
+    N = 512, through each batch-size kernel (16/32/64-token streaming, 256 x
+    64 tiles)."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=2304, N=512)
+    sw = gen.make_sparse_weights(spec, seed_config=313)
+    x = gen.make_sparse_x(spec, M, seed_config=313)
+    say("sparse long-k", M)
+    y = run_sparse(sw, x, spec.N)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128)
+    assert_close_fp(y, ref, "sparse K=2304 M=%d" % M)
+
+
+def test_sparse_large_batch_narrow_n():
+    """M > 128 with N not a multiple of 256: the streaming kernel, with a
+    partial last workgroup of row tiles."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=512, N=112)
+    sw = gen.make_sparse_weights(spec, seed_config=314)
+    x = gen.make_sparse_x(spec, 150, seed_config=314)
+    say("sparse narrow-n")
+    y = run_sparse(sw, x, spec.N)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128)
+    assert_close_fp(y, ref, "sparse N=112 M=150")
+
+
 def test_sparse_matches_dense_with_zeros_on_gpu():
     """The 2:4 kernel and the dense int4 kernel (RAW stage, one expert, top-1)
     agree on the same weights with zeros at the pruned positions."""

@@ -320,7 +320,7 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
         WQ_REQUIRE(group_size == 128, WQ_ERR_UNSUPPORTED, "sparse24: group_size %d (128 only)", group_size);
         WQ_REQUIRE(K % 256 == 0, WQ_ERR_UNSUPPORTED, "sparse24: K %d not a multiple of 256", K);
         WQ_REQUIRE(N % 16 == 0, WQ_ERR_UNSUPPORTED, "sparse24: N %d not a multiple of 16", N);
-        WQ_REQUIRE(N / 16 <= 0x7fffffff && (M + 63) / 64 <= 65535, WQ_ERR_UNSUPPORTED, "sparse24: M too large");
+        WQ_REQUIRE((M + 15) / 16 <= 65535, WQ_ERR_UNSUPPORTED, "sparse24: M too large");
         if (M == 0) return ok();
         WQ_TRY(check_ptr(d_x, "x"));
         WQ_TRY(check_ptr(d_vals, "vals"));

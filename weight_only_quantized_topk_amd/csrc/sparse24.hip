@@ -10,120 +10,296 @@
 // order of the dense int4 format) and one 8-byte piece of 2-bit position
 // metadata per lane, already in the instruction's index format, so the
 // metadata decode is a register move: two instructions share one index dword
-// through ABID 0/1.  Group scales are folded in fp32 per 128 dense channels.
+// through ABID 0/1.
 //
-// One workgroup: 16 output rows x up to 64 tokens, the 4 waves split K and
-// meet in LDS.
+// Two kernels:
+//  - small and medium batches (M <= 128): one workgroup per 64 output rows
+//    (one 16-row tile per wave) and 16, 32 or 64 tokens; all waves walk the
+//    same 256-channel chunks, whose token tile is staged once in LDS and
+//    shared; each wave keeps the weights of 8 chunks in flight in registers;
+//  - large batches: one workgroup per 256 output rows and 64 tokens; the token
+//    tile of each chunk is staged once in LDS and shared by the 4 waves, each
+//    of which multiplies its own 64 weight rows, read straight from the packed
+//    layout into registers one chunk ahead.
+// Token rows are 512-byte LDS rows of 16-byte pieces stored at
+// piece ^ (row & 15), so the B-operand reads of 16 rows hit distinct banks.
+// Weights are scaled in fp16 (q * s rounded once) before the multiply.
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace wq {
+
+// calls f(std::integral_constant<int, i>) for i in [B, E), unrolled
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 constexpr int SP_WAVES = 4;
 constexpr int SP_THREADS = 64 * SP_WAVES;
 constexpr int SP_KCHUNK = 256;  // dense input channels per packed piece
-constexpr int SP_RMAX = 4;      // 16-row token blocks per workgroup
+constexpr int SPT_ROWB_S = SP_KCHUNK * 2;  // LDS bytes of one token row of a chunk
 
-__global__ __launch_bounds__(SP_THREADS) void sparse24_kernel(const uint16_t* __restrict__ x, int M, int K, int N,
-                                                              const uint8_t* __restrict__ vals,
-                                                              const uint8_t* __restrict__ meta,
-                                                              const uint16_t* __restrict__ scales,
-                                                              uint16_t* __restrict__ y) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int tile = blockIdx.x;
-    const int tok0 = blockIdx.y * 16 * SP_RMAX;
-    const int R = min(SP_RMAX, (M - tok0 + 15) / 16);
+// ------------------------------------------------- streaming (small batches)
+// One workgroup: NWV waves, wave w multiplies 16-row tile NWV*blockIdx.x + w by
+// the 16*R tokens of blockIdx.y; all waves walk the same 256-channel chunks.
+// The token tile of a chunk is staged in LDS (two slots), its global loads
+// issued XP chunks ahead; each wave keeps the weights of PF chunks of its tile
+// in flight in registers.  Chunk slots are static: the chunk loop is unrolled
+// by PF.
+template <int R, int PF, int NWV>
+__global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                     int N, const uint8_t* __restrict__ vals,
+                                                                     const uint8_t* __restrict__ meta,
+                                                                     const uint16_t* __restrict__ scales,
+                                                                     uint16_t* __restrict__ y) {
+    constexpr int XP = R == 1 ? 4 : 2;              // token chunks in flight
+    constexpr int ROWS = 16 * R;                    // tokens per workgroup
+    constexpr int NT = NWV * 64;
+    constexpr int XPIECES = ROWS * 32 / NT;         // 16-byte token pieces per thread per chunk
+    constexpr int SPS_PF = PF;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * SPT_ROWB_S];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ntiles = N / 16;
+    const int t_raw = NWV * blockIdx.x + wave;
+    const bool tvalid = t_raw < ntiles;
+    const int t = tvalid ? t_raw : ntiles - 1;
+    const int m0 = blockIdx.y * ROWS;
     const int C = K / SP_KCHUNK;
-    const int rowq = 4 * (lane >> 4);
+    const int nrow = lane & 15;
 
-    const uint8_t* vt = vals + (size_t)tile * C * 1024 + lane * 16;
-    const uint8_t* mt = meta + (size_t)tile * C * 512 + lane * 8;
-    const uint16_t* st = scales + tile * 16 + rowq;
-
-    const uint16_t* xr[SP_RMAX];
-    bool xv_ok[SP_RMAX];
+    const uint8_t* vt = vals + (size_t)t * C * 1024 + lane * 16;
+    const uint8_t* mt = meta + (size_t)t * C * 512 + lane * 8;
+    const uint16_t* sn = scales + 16 * t + nrow;
+    // the two scale halves stay apart until used, so no wait follows their loads
+    u32x4 wv[SPS_PF];
+    u32x2 wm[SPS_PF];
+    uint32_t ws0[SPS_PF], ws1[SPS_PF];
+    auto wload = [&](int c, int slot) {
+        wv[slot] = ldg128_stream(vt + (size_t)c * 1024);
+        wm[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
+        ws0[slot] = sn[(size_t)(2 * c) * N];
+        ws1[slot] = sn[(size_t)(2 * c + 1) * N];
+    };
+    const uint16_t* xcol = x + (tid & 31) * 8;
+    const int xrow0 = m0 + (tid >> 5);
+    u32x4 xv[XP][XPIECES];
+    auto xload = [&](int c, int slot) {
 #pragma unroll
-    for (int r = 0; r < SP_RMAX; ++r) {
-        const int m = tok0 + 16 * r + (lane & 15);
-        xv_ok[r] = (r < R) && (m < M);
-        xr[r] = x + (size_t)(xv_ok[r] ? m : 0) * K + 8 * (lane >> 4);
-    }
-
-    f32x4 acc[SP_RMAX];
+        for (int i = 0; i < XPIECES; ++i)
+            xv[slot][i] = ldg128(xcol + (size_t)min(xrow0 + (NT / 32) * i, M - 1) * K + c * SP_KCHUNK);
+    };
+    auto xstore = [&](int slot, int buf) {
 #pragma unroll
-    for (int r = 0; r < SP_RMAX; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = wave; c < C; c += SP_WAVES) {
-        const u32x4 v = ldg128_stream(vt + (size_t)c * 1024);
-        const u32x2 md = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
-        u32x8 b[SP_RMAX][4];
+        for (int i = 0; i < XPIECES; ++i) {
+            const int id = tid + NT * i;
+            const int row = id >> 5, piece = id & 31;
+            *reinterpret_cast<u32x4*>(&xs[buf][row * SPT_ROWB_S + ((piece ^ (row & 15)) << 4)]) = xv[slot][i];
+        }
+    };
+    f32x4 acc[R];
 #pragma unroll
-        for (int r = 0; r < SP_RMAX; ++r)
+    for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int slot, int buf) {
+        const uint8_t* xb = xs[buf];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-                if (xv_ok[r]) {
-                    lo = ldg128(xr[r] + c * SP_KCHUNK + 64 * s);
-                    hi = ldg128(xr[r] + c * SP_KCHUNK + 64 * s + 32);
-                }
-                b[r][s] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-        const u32x2 s01 = *reinterpret_cast<const u32x2*>(st + (size_t)(2 * c) * N);
-        const u32x2 s23 = *reinterpret_cast<const u32x2*>(st + (size_t)(2 * c + 1) * N);
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t sv = (s < 2) ? ws0[slot] : ws1[slot];
+            const u32x4 a = dequant_w4_f16_scaled(wv[slot][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+            const int idx = (int)wm[slot][s >> 1];
+            const int plo = 8 * s + (lane >> 4), phi = plo + 4;
 #pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
-            f32x4 part[SP_RMAX];
-#pragma unroll
-            for (int r = 0; r < SP_RMAX; ++r) part[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const u32x4 a0 = dequant_w4_f16(v[2 * grp]);
-            const u32x4 a1 = dequant_w4_f16(v[2 * grp + 1]);
-            const int idx = (int)md[grp];
-#pragma unroll
-            for (int r = 0; r < SP_RMAX; ++r) {
-                if (r < R) {
-                    part[r] = smfmac16x16x64<0>(a0, b[r][2 * grp], idx, part[r]);
-                    part[r] = smfmac16x16x64<1>(a1, b[r][2 * grp + 1], idx, part[r]);
-                }
-            }
-            const u32x2 sp = grp ? s23 : s01;
-            const float f0 = f16_to_f32((uint16_t)(sp[0] & 0xffffu));
-            const float f1 = f16_to_f32((uint16_t)(sp[0] >> 16));
-            const float f2 = f16_to_f32((uint16_t)(sp[1] & 0xffffu));
-            const float f3 = f16_to_f32((uint16_t)(sp[1] >> 16));
-#pragma unroll
-            for (int r = 0; r < SP_RMAX; ++r) {
-                acc[r][0] += part[r][0] * f0;
-                acc[r][1] += part[r][1] * f1;
-                acc[r][2] += part[r][2] * f2;
-                acc[r][3] += part[r][3] * f3;
+            for (int r = 0; r < R; ++r) {
+                const int row = 16 * r + nrow;
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(xb + row * SPT_ROWB_S + ((plo ^ nrow) << 4));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(xb + row * SPT_ROWB_S + ((phi ^ nrow) << 4));
+                const u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                if (s & 1) acc[r] = smfmac16x16x64<1>(a, b, idx, acc[r]);
+                else acc[r] = smfmac16x16x64<0>(a, b, idx, acc[r]);
             }
         }
-    }
+    };
 
-    __shared__ f32x4 red[SP_WAVES][SP_RMAX][64];
+    // every load is unconditional (chunk indices clamped to the last chunk, which
+    // the tail then reads again from cache): loads under a branch would make the
+    // compiler wait for all of them before the LDS stores
+    auto body = [&](int c, auto U) {
+        constexpr int u = decltype(U)::value;
+        xstore(u % XP, u & 1);
+        xload(min(c + XP, C - 1), u % XP);
+        __syncthreads();
+        compute(u, u & 1);
+        wload(min(c + SPS_PF, C - 1), u);
+    };
 #pragma unroll
-    for (int r = 0; r < SP_RMAX; ++r) red[wave][r][lane] = acc[r];
-    __syncthreads();
-    if (wave < R) {
-        const int r = wave;
-        f32x4 o = red[0][r][lane];
+    for (int p = 0; p < SPS_PF; ++p) wload(min(p, C - 1), p);
 #pragma unroll
-        for (int w = 1; w < SP_WAVES; ++w) o += red[w][r][lane];
-        const int m = tok0 + 16 * r + (lane & 15);
-        if (m < M) {
-            u32x2 stv;
-            stv[0] = (uint32_t)f32_to_f16(o[0]) | ((uint32_t)f32_to_f16(o[1]) << 16);
-            stv[1] = (uint32_t)f32_to_f16(o[2]) | ((uint32_t)f32_to_f16(o[3]) << 16);
-            *reinterpret_cast<u32x2*>(y + (size_t)m * N + tile * 16 + rowq) = stv;
+    for (int q = 0; q < XP; ++q) xload(min(q, C - 1), q);
+    int c0 = 0;
+    for (; c0 + SPS_PF <= C; c0 += SPS_PF)
+        static_for<0, SPS_PF>([&](auto U) { body(c0 + decltype(U)::value, U); });
+    // tail of fewer than PF chunks (the guard is uniform over the workgroup)
+    static_for<0, SPS_PF - 1>([&](auto U) {
+        if (c0 + decltype(U)::value < C) body(c0 + decltype(U)::value, U);
+    });
+
+    if (tvalid) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int m = m0 + 16 * r + nrow;
+            if (m < M) {
+                u32x2 stv;
+                stv[0] = (uint32_t)f32_to_f16(acc[r][0]) | ((uint32_t)f32_to_f16(acc[r][1]) << 16);
+                stv[1] = (uint32_t)f32_to_f16(acc[r][2]) | ((uint32_t)f32_to_f16(acc[r][3]) << 16);
+                *reinterpret_cast<u32x2*>(y + (size_t)m * N + 16 * t + 4 * (lane >> 4)) = stv;
+            }
         }
     }
 }
 
+// ------------------------------------------------------------ large batches
+constexpr int SPT_BN = 256;  // weight rows per workgroup (4 waves x 4 tiles of 16)
+constexpr int SPT_BM = 64;   // tokens per workgroup (4 B tiles of 16)
+constexpr int SPT_ROWB = SP_KCHUNK * 2;
+constexpr int SPT_XPIECES = SPT_BM * (SPT_ROWB / 16) / SP_THREADS;  // 16-byte token pieces per thread per chunk
+
+__device__ __forceinline__ int spt_off(int row, int piece) { return row * SPT_ROWB + ((piece ^ (row & 15)) << 4); }
+
+template <int OCC>
+__global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                      int N, const uint8_t* __restrict__ vals,
+                                                                      const uint8_t* __restrict__ meta,
+                                                                      const uint16_t* __restrict__ scales,
+                                                                      uint16_t* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[SPT_BM * SPT_ROWB];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m0 = blockIdx.y * SPT_BM;
+    const int C = K / SP_KCHUNK;
+    const int t0 = blockIdx.x * (SPT_BN / 16) + 4 * wave;  // first 16-row tile of this wave
+    const int nrow = lane & 15;
+
+    // token pieces: row id/32 = tid/32 + 8i, piece id%32 = tid%32 (rows past M read row M-1; their
+    // outputs are not stored)
+    const uint16_t* xcol = x + (tid & 31) * 8;
+    const int xrow0 = m0 + (tid >> 5);
+    u32x4 xv[SPT_XPIECES];
+    u32x4 v[4], vn[4];
+    u32x2 md[4], mdn[4];
+    uint32_t sc0[4], sc1[4], scn0[4], scn1[4];  // scales of groups 2c and 2c+1 of this lane's row
+    auto gload = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < SPT_XPIECES; ++i)
+            xv[i] = ldg128(xcol + (size_t)min(xrow0 + 8 * i, M - 1) * K + c * SP_KCHUNK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t pc = ((size_t)(t0 + i) * C + c) * 64 + lane;
+            vn[i] = ldg128_stream(vals + pc * 16);
+            mdn[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(meta + pc * 8));
+            const int n = 16 * (t0 + i) + nrow;
+            scn0[i] = scales[(size_t)(2 * c) * N + n];
+            scn1[i] = scales[(size_t)(2 * c + 1) * N + n];
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int boff[4];  // LDS row offsets of this lane's B columns (token tiles j)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) boff[j] = (16 * j + nrow) * SPT_ROWB;
+    const int bsw = nrow;  // row & 15 of every B row this lane reads
+
+    auto step = [&](auto ST) {
+        constexpr int s = decltype(ST)::value;  // 64-channel step within the chunk
+        u32x4 a[4];
+        int idx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t sv = (s < 2) ? sc0[i] : sc1[i];
+            a[i] = dequant_w4_f16_scaled(v[i][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+            idx[i] = (int)md[i][s >> 1];
+        }
+        const int plo = 8 * s + (lane >> 4), phi = plo + 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(xs + boff[j] + ((plo ^ bsw) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(xs + boff[j] + ((phi ^ bsw) << 4));
+            const u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][j] = smfmac16x16x64<s & 1>(a[i], b, idx[i], acc[i][j]);
+        }
+    };
+
+    gload(0);
+    for (int c = 0; c < C; ++c) {
+#pragma unroll
+        for (int i = 0; i < SPT_XPIECES; ++i) {
+            const int id = tid + SP_THREADS * i;
+            *reinterpret_cast<u32x4*>(xs + spt_off(id >> 5, id & 31)) = xv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = vn[i];
+            md[i] = mdn[i];
+            sc0[i] = scn0[i];
+            sc1[i] = scn1[i];
+        }
+        __syncthreads();
+        gload(min(c + 1, C - 1));  // the last chunk is loaded twice, keeping the loop branch-free
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+        __syncthreads();
+    }
+
+    // D[row 4*(lane/16) + r][col lane%16]: rows are weight rows, columns tokens
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = m0 + 16 * j + nrow;
+        if (m < M) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x2 stv;
+                stv[0] = (uint32_t)f32_to_f16(acc[i][j][0]) | ((uint32_t)f32_to_f16(acc[i][j][1]) << 16);
+                stv[1] = (uint32_t)f32_to_f16(acc[i][j][2]) | ((uint32_t)f32_to_f16(acc[i][j][3]) << 16);
+                *reinterpret_cast<u32x2*>(y + (size_t)m * N + 16 * (t0 + i) + 4 * (lane >> 4)) = stv;
+            }
+        }
+    }
+}
+
+template <int R>
+static void launch_stream(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+                          const uint16_t* scales, uint16_t* y, hipStream_t s) {
+    const dim3 grid((N / 16 + 3) / 4, (M + 16 * R - 1) / (16 * R));
+    hipLaunchKernelGGL((sparse24_stream_kernel<R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales, y);
+}
+
+// batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480
 void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                      const uint16_t* scales, uint16_t* y, hipStream_t s) {
-    const dim3 grid(N / 16, (M + 16 * SP_RMAX - 1) / (16 * SP_RMAX));
-    hipLaunchKernelGGL(sparse24_kernel, grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta, scales, y);
+    if (M > 128 && N % SPT_BN == 0) {
+        const dim3 grid(N / SPT_BN, (M + SPT_BM - 1) / SPT_BM);
+        hipLaunchKernelGGL(sparse24_tile_kernel<2>, grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta, scales, y);
+    } else if (M <= 16) {
+        launch_stream<1>(x, M, K, N, vals, meta, scales, y, s);
+    } else if (M <= 64) {
+        launch_stream<2>(x, M, K, N, vals, meta, scales, y, s);
+    } else {
+        launch_stream<4>(x, M, K, N, vals, meta, scales, y, s);
+    }
 }
 
 }  // namespace wq
