@@ -22,6 +22,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace wq {
 
 // Kernel shape: NP weight-row tiles per workgroup (pairs of gate+up tiles for
@@ -32,8 +34,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;  // 16-row tiles per workgroup
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     constexpr int KSTEPS = KCHUNK / 32;
-    constexpr int ITEMS = NP * RMAX;  // epilogue items (tile or tile pair, token block)
     static_assert(NW * NT * RMAX * 1024 <= 64 * 1024, "LDS reduction buffer");
+    static_assert(RMAX == 1 || RMAX == 2 || RMAX == 4, "passes of RMAX, then 2 and/or 1 blocks");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -65,48 +67,52 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
 
     __shared__ f32x4 red[NW][NT][RMAX][64];
 
-    for (int s0 = 0; s0 < S; s0 += RMAX) {
-        const int R = min(RMAX, S - s0);
-        const uint16_t* arow[RMAX];
-        bool avalid[RMAX];
+    // one pass multiplies R token blocks (a compile-time count: full passes take
+    // RMAX, the remainder one pass of 2 and/or 1), so no load depends on R
+    auto pass = [&](const int s0, auto RC) {
+        constexpr int R = decltype(RC)::value;
+        constexpr int ITEMS_R = NP * R;  // epilogue items (tile or tile pair, token block)
+        const uint16_t* arow[R];
+        bool avalid[R];
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r) {
-            avalid[r] = false;
-            arow[r] = g.a;
-            if (r < R) {
-                const int p = (sb_first + s0 + r) * 16 + (lane & 15);
-                const int pair = g.sorted[p];
-                avalid[r] = pair < T;
-                const int row = g.a_direct ? p : (avalid[r] ? pair / g.topk : 0);
-                arow[r] = g.a + (size_t)row * g.k_in + 8 * (lane >> 4);
-            }
+        for (int r = 0; r < R; ++r) {
+            // pad rows read the block's first row, a real one (same address as
+            // lane 0: one fetch; their H rows are written as 0, their other
+            // outputs dropped), so every load below is unconditional
+            const int p_first = (sb_first + s0 + r) * 16;
+            const int p = p_first + (lane & 15);
+            const int pair = g.sorted[p];
+            avalid[r] = pair < T;
+            const int pl = avalid[r] ? p : p_first;
+            const int row = g.a_direct ? pl : g.sorted[pl] / g.topk;
+            arow[r] = g.a + (size_t)row * g.k_in + 8 * (lane >> 4);
         }
 
-        f32x4 acc[NT][RMAX];
+        f32x4 acc[NT][R];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < R; ++r) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // DEPTH rotating buffers of one chunk each
         u32x4 wv[DEPTH][NT];
-        u32x4 xv[DEPTH][RMAX][KSTEPS];
+        u32x4 xv[DEPTH][R][KSTEPS];
         u32x2 sv[DEPTH][NT];
 
+        // no load sits under a branch: a branch would make the compiler wait for
+        // every load in flight before the next multiply
         auto load = [&](int c, int d) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) wv[d][t] = ldg128_stream(wt[t] + (size_t)c * CHUNK_BYTES);
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r)
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s)
-                    xv[d][r][s] =
-                        (r < R && avalid[r]) ? ldg128(arow[r] + c * KCHUNK + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-            if (grouped) {
+                for (int s = 0; s < KSTEPS; ++s) xv[d][r][s] = ldg128(arow[r] + c * KCHUNK + 32 * s);
+            if constexpr (WBITS == 4) {
+                const size_t gc = grouped ? (size_t)c : 0;  // per-column scales: a harmless reread of group 0
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    sv[d][t] = *reinterpret_cast<const u32x2*>(se + (size_t)c * g.n_out +
-                                                               (NT * unit + t) * TILE_ROWS + rowq);
+                    sv[d][t] = *reinterpret_cast<const u32x2*>(se + gc * g.n_out + (NT * unit + t) * TILE_ROWS + rowq);
             }
         };
 
@@ -114,15 +120,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if constexpr (WBITS == 4) {
-                    f32x4 part[RMAX];
+                    f32x4 part[R];
 #pragma unroll
-                    for (int r = 0; r < RMAX; ++r) part[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < R; ++r) part[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KSTEPS; ++s) {
                         const u32x4 a = dequant_w4_f16(wv[d][t][s]);
 #pragma unroll
-                        for (int r = 0; r < RMAX; ++r)
-                            if (r < R) part[r] = mfma16x16x32<false>(a, xv[d][r][s], part[r]);
+                        for (int r = 0; r < R; ++r) part[r] = mfma16x16x32<false>(a, xv[d][r][s], part[r]);
                     }
                     if (grouped) {
                         const uint32_t lo = sv[d][t][0], hi = sv[d][t][1];
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
                         const float s2f = f16_to_f32((uint16_t)(hi & 0xffffu));
                         const float s3f = f16_to_f32((uint16_t)(hi >> 16));
 #pragma unroll
-                        for (int r = 0; r < RMAX; ++r) {
+                        for (int r = 0; r < R; ++r) {
                             acc[t][r][0] += part[r][0] * s0f;
                             acc[t][r][1] += part[r][1] * s1f;
                             acc[t][r][2] += part[r][2] * s2f;
@@ -139,30 +144,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
                         }
                     } else {
 #pragma unroll
-                        for (int r = 0; r < RMAX; ++r) acc[t][r] += part[r];
+                        for (int r = 0; r < R; ++r) acc[t][r] += part[r];
                     }
                 } else {
 #pragma unroll
                     for (int s = 0; s < KSTEPS; ++s) {
                         const u32x4 a = dequant_w8x8<BF16>(wv[d][t][2 * s], wv[d][t][2 * s + 1]);
 #pragma unroll
-                        for (int r = 0; r < RMAX; ++r)
-                            if (r < R) acc[t][r] = mfma16x16x32<BF16>(a, xv[d][r][s], acc[t][r]);
+                        for (int r = 0; r < R; ++r) acc[t][r] = mfma16x16x32<BF16>(a, xv[d][r][s], acc[t][r]);
                     }
                 }
             }
         };
 
-        // split-K over the waves; DEPTH - 1 chunks in flight while one is multiplied
+        // split-K over the waves; DEPTH - 1 chunks in flight while one is
+        // multiplied.  Chunk indices past the end are clamped to this wave's
+        // last chunk (a cache hit), keeping every load unconditional.
+        // (a wave without chunks, C <= wave, loads chunk C - 1 and multiplies nothing)
+        const int clast = wave < C ? wave + ((C - 1 - wave) / NW) * NW : C - 1;
 #pragma unroll
-        for (int i = 0; i < DEPTH - 1; ++i)
-            if (wave + i * NW < C) load(wave + i * NW, i);
+        for (int i = 0; i < DEPTH - 1; ++i) load(min(wave + i * NW, clast), i);
         for (int base = wave; base < C; base += DEPTH * NW) {
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
                 const int c = base + d * NW;
-                const int cl = c + (DEPTH - 1) * NW;
-                if (cl < C) load(cl, (d + DEPTH - 1) % DEPTH);
+                load(min(c + (DEPTH - 1) * NW, clast), (d + DEPTH - 1) % DEPTH);
                 if (c < C) compute(d);
             }
         }
@@ -170,13 +176,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r) red[wave][t][r][lane] = acc[t][r];
+            for (int r = 0; r < R; ++r) red[wave][t][r][lane] = acc[t][r];
         __syncthreads();
 
-        for (int item = wave; item < ITEMS; item += NW) {
-            const int pp = item / RMAX;  // tile (or gate/up tile pair) within the workgroup
-            const int r = item % RMAX;
-            if (r >= R) continue;
+        for (int item = wave; item < ITEMS_R; item += NW) {
+            const int pp = item / R;  // tile (or gate/up tile pair) within the workgroup
+            const int r = item % R;
             const int p = (sb_first + s0 + r) * 16 + (lane & 15);
             const int pair = g.sorted[p];
             if constexpr (STAGE == STAGE_GATE_UP) {
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
                         gt *= act_to_f32<BF16>(se[(NT * unit + tg) * TILE_ROWS + rowq + i]);
                         up *= act_to_f32<BF16>(se[(NT * unit + tu) * TILE_ROWS + rowq + i]);
                     }
-                    h[i] = silu_f32(gt) * up;
+                    h[i] = pair < T ? silu_f32(gt) * up : 0.0f;
                 }
                 u32x2 st;
                 st[0] = (uint32_t)f32_to_act<BF16>(h[0]) | ((uint32_t)f32_to_act<BF16>(h[1]) << 16);
@@ -219,6 +224,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
             }
         }
         __syncthreads();
+    };
+    int s0 = 0;
+    for (; s0 + RMAX <= S; s0 += RMAX) pass(s0, std::integral_constant<int, RMAX>{});
+    if constexpr (RMAX >= 4) {
+        if (s0 + 2 <= S) {
+            pass(s0, std::integral_constant<int, 2>{});
+            s0 += 2;
+        }
+    }
+    if constexpr (RMAX >= 2) {
+        if (s0 < S) pass(s0, std::integral_constant<int, 1>{});
     }
 
     if constexpr (STAGE == STAGE_GATE_UP) {
@@ -241,29 +257,37 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH>), grid, dim3(64 * NW), 0, s, g);
 }
 
-// Shapes by batch (measured on MI355X with the cfg2 Mixtral shapes): one
-// token block per pass when the experts are thin (each wave then keeps one
-// chunk in flight while it multiplies one; the down stage, with half as many
-// weight rows, takes two row tiles per workgroup, 8 waves and two chunks in
-// flight), two blocks and two row tiles when experts average up to ~24 rows,
-// four blocks beyond.  Token blocks an expert has beyond RMAX cost another
-// pass over its weights.
+// Shapes by batch, measured on MI355X (Mixtral-shaped int8 and int4 layers,
+// and the 160-expert int8 layer with skewed routing).  One token block per
+// pass when experts are thin, two up to ~24 rows per expert, four beyond
+// (larger batches normally take the large-batch kernel).  The waves of a
+// workgroup split the input channels, so their count follows the number of
+// 1 KiB chunks per weight row tile C: a short reduction (C <= 32) keeps 2
+// waves with 2 or 4 row tiles, a long one 8 waves for int8 and 4 for int4,
+// whose dequantisation costs more instructions per chunk.
 template <int WBITS, bool BF16, int STAGE>
 static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
-    constexpr int NT1 = (STAGE == STAGE_GATE_UP) ? 2 : 1;
+    constexpr bool GU = STAGE == STAGE_GATE_UP;
+    constexpr int NT1 = GU ? 2 : 1;
     const int T = g.M * g.topk;
     const int touched = T < g.E ? T : g.E;
     const int rows = (T + touched - 1) / touched;  // expected rows per touched expert
     const bool np2_ok = (g.n_out % (TILE_ROWS * NT1 * 2)) == 0;
+    const bool np4_ok = (g.n_out % (TILE_ROWS * NT1 * 4)) == 0;
+    const bool short_k = g.k_in / WFmt<WBITS>::KCHUNK <= 32;
     if (T <= 16 || rows <= 8) {
-        if (STAGE == STAGE_GATE_UP) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
-        else if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 8, 3>(g, s);
-        else launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 8, 4>(g, s);
+        if (GU) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
+        else if (!np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 8, 4>(g, s);
+        else if (short_k) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 2, 3>(g, s);
+        else if (WBITS == 8) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 8, 3>(g, s);
+        else launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 3>(g, s);
     } else if (rows <= 24) {
-        if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);
+        if (!GU && short_k && np4_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 4, 2, 2>(g, s);
+        else if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);
         else launch_decode_cfg<WBITS, BF16, STAGE, 2, 1, 4, 2>(g, s);
     } else {
-        launch_decode_cfg<WBITS, BF16, STAGE, 4, 1, 4, 2>(g, s);
+        if (!GU && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 4, 2, 4, 2>(g, s);
+        else launch_decode_cfg<WBITS, BF16, STAGE, 4, 1, 4, 2>(g, s);
     }
 }
 

@@ -19,6 +19,7 @@ from ._lib import WQ_STAGE_DOWN, WQ_STAGE_GATE_UP
 
 DECODE_BLOCK = 16    # token block of the small-batch kernel
 PREFILL_BLOCK = 128  # token block of the large-batch kernel
+PREFILL_BLOCK_THIN = 64
 
 
 @dataclass
@@ -73,15 +74,18 @@ def pack_moe(bits: int, w1q: np.ndarray, s1_bits: np.ndarray, w2q: np.ndarray, s
 
 
 def choose_block_size(M: int, topk: int, E: int, bits: int = 8) -> int:
-    """Batch-size heuristic: expected rows per touched expert decides between the
-    small-batch kernel (block 16) and the large-batch kernel (block 128; its
-    64-row tiles were slower than 128-row tiles with their extra padding at
-    every measured shape, so block 64 is left to explicit callers)."""
+    """Batch-size heuristic on the expected rows per touched expert: up to 24
+    the small-batch kernel (block 16: it rereads the token rows from L2 for
+    every weight tile, cheap only while they are few), up to 96 the
+    large-batch kernel with 64-row token tiles (less padding), beyond that its
+    128-row tiles."""
     T = M * topk
     if T == 0:
         return DECODE_BLOCK
     rows_per_expert = T / min(E, T)
-    return DECODE_BLOCK if rows_per_expert <= 64 else PREFILL_BLOCK
+    if rows_per_expert <= 24:
+        return DECODE_BLOCK
+    return PREFILL_BLOCK_THIN if rows_per_expert <= 96 else PREFILL_BLOCK
 
 
 class MoERunner:
