@@ -263,8 +263,9 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
 // (larger batches normally take the large-batch kernel).  The waves of a
 // workgroup split the input channels, so their count follows the number of
 // 1 KiB chunks per weight row tile C: a short reduction (C <= 32) keeps 2
-// waves with 2 or 4 row tiles, a long one 8 waves for int8 and 4 for int4,
-// whose dequantisation costs more instructions per chunk.
+// waves with 2 or 4 row tiles, a long one 8 waves; int4 (half the bytes per
+// weight, so half the work per wave) takes two gate/up tile pairs per
+// workgroup, and four row tiles in DOWN once that grid still fills the GPU.
 template <int WBITS, bool BF16, int STAGE>
 static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
     constexpr bool GU = STAGE == STAGE_GATE_UP;
@@ -275,12 +276,15 @@ static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
     const bool np2_ok = (g.n_out % (TILE_ROWS * NT1 * 2)) == 0;
     const bool np4_ok = (g.n_out % (TILE_ROWS * NT1 * 4)) == 0;
     const bool short_k = g.k_in / WFmt<WBITS>::KCHUNK <= 32;
+    // workgroups of a 4-tile DOWN grid over the touched experts
+    const long wg4 = (long)touched * (g.n_out / (TILE_ROWS * 4));
     if (T <= 16 || rows <= 8) {
-        if (GU) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
+        if (GU && WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 2>(g, s);
+        else if (GU) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
         else if (!np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 8, 4>(g, s);
         else if (short_k) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 2, 3>(g, s);
-        else if (WBITS == 8) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 8, 3>(g, s);
-        else launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 3>(g, s);
+        else if (WBITS == 4 && np4_ok && wg4 >= 512) launch_decode_cfg<WBITS, BF16, STAGE, 1, 4, 4, 2>(g, s);
+        else launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 8, 3>(g, s);
     } else if (rows <= 24) {
         if (!GU && short_k && np4_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 4, 2, 2>(g, s);
         else if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);

@@ -149,6 +149,28 @@ class MoERunner:
             marks[2].record()
         return self.out
 
+    def capture(self, x, logits):
+        """Record one call (route -> align -> GATE_UP -> DOWN -> combine) into a
+        HIP graph that reads x and logits from these tensors' memory and writes
+        the runner's buffers; replay() reruns it after the caller updates the
+        inputs in place.  The launches are validated once, here."""
+        import torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self(x, logits)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self(x, logits)
+        self.graph, self._graph_inputs = g, (x, logits)
+        return g
+
+    def replay(self):
+        self.graph.replay()
+        return self.out
+
     def aux(self):
         return {"topk_weights": self.w, "topk_ids": self.ids, "sorted_token_ids": self.st, "expert_ids": self.ex,
                 "num_tokens_post_padded": self.nt, "h": self.h, "y": self.work2, "block_size": self.bs,
