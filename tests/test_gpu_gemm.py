@@ -175,6 +175,40 @@ def test_down_split_k(key, M):
     assert ws >= 4 * M * spec.topk * spec.K * 4
 
 
+def test_down_split_wide_grid_w4():
+    """int4, 4096 outputs, k_in 4096, M = 1024 (2048 pairs): the DOWN grid of
+    256-row tiles has fewer than 1024 workgroups, so K is split in 4 slices on
+    the 256 x 128 four-wave shape (the workspace holds 4 fp32 slabs); the
+    output of sampled tokens against the oracle."""
+    need_gpu()
+    spec = W4.with_(name="w4-split-wide", K=4096, N=4096)
+    wts = gen.make_moe_weights(spec, seed_config=508)
+    p = _pack(spec, wts)
+    M, bs = 1024, 128
+    toks, w, ids = routed(spec, M, seed=760)
+    T = M * spec.topk
+    h_act = act_round(np.random.default_rng(761).standard_normal((T, spec.N)), spec.act)
+    st, ex, nt, cap = align_dev(ids, spec.E, bs)
+    stn, ntn = st.cpu().numpy(), int(nt.cpu()[0])
+    hs = np.zeros((cap, spec.N), np.float32)
+    live = stn[:ntn] < T
+    hs[:ntn][live] = h_act[stn[:ntn][live]]
+    hd = torch.from_numpy(hs).cuda().to(p.act)
+    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, M, spec.topk, spec.E, spec.K, spec.N, cap, False)
+    assert ws >= 4 * T * spec.K * 4
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, spec.K), dtype=p.act, device="cuda")
+    say("down split wide w4")
+    wq.moe_w4a16_gemm(wq.WQ_STAGE_DOWN, hd, M, spec.topk, spec.E, spec.K, spec.N, p.w2, p.s2, spec.group_size,
+                      None, st, ex, nt, cap, bs, torch.from_numpy(w).cuda(), out, work)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 100, 511, 777, M - 1])
+    h_rows = h_act.reshape(M, spec.topk, spec.N)[rows].reshape(-1, spec.N)
+    y_ref = oracle.moe_down(h_rows, ids, wts.w2q, wts.s2_f32(), wts.g2, rows=rows)
+    out_ref = oracle.moe_combine(y_ref, w, rows=rows)
+    assert_close_fp(host_f32(out)[rows], out_ref, "split-K DOWN, sampled tokens")
+
+
 def _check_down(key, bs, M):
     need_gpu()
     spec, wts, p = setup(key)
