@@ -7,6 +7,7 @@
  * host synchronisation, no device-to-host read):
  *   moe_route             router softmax + top-k
  *   moe_align             token sort and pad per expert
+ *   moe_route_align       both in one call (one kernel for small batches)
  *   moe_w4a16_gemm        grouped GEMM, int4 GPTQ-style weights, fp16 activations
  *   moe_w8a16_gemm        grouped GEMM, int8 per-column weights, bf16/fp16 activations
  *   sparse24_w4a16_gemm   2:4-sparse int4 dense linear layer, fp16 activations
@@ -110,6 +111,21 @@ size_t moe_align_capacity(int M, int topk, int E, int block_size);
 wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block_size,
                     int32_t* d_sorted_token_ids, int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded,
                     size_t capacity, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_route_align                                                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * moe_route followed by moe_align in one call, with the same arguments and the
+ * same outputs bit for bit.  Batches of at most 16 tokens (and 1024 pairs) run
+ * as a single kernel that keeps the expert ids on chip between the two steps
+ * (one launch instead of two on the latency-bound small-batch path); larger
+ * batches run the two kernels.  Limits: those of both calls.
+ */
+wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int renormalize, int block_size,
+                          float* d_topk_weights, int32_t* d_topk_ids, int32_t* d_sorted_token_ids,
+                          int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded, size_t capacity,
+                          void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Grouped GEMMs                                                             */

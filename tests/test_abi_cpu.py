@@ -76,6 +76,23 @@ def test_align_validation():
     assert _status("moe_align", p, 4, 2, 8, 16, None, p, p, 1024, None)[0] == wq.WQ_ERR_INVALID
 
 
+def test_route_align_validation():
+    """The fused call rejects what either of its two parts rejects, before any
+    device work (the ids check against device memory is never reached)."""
+    p = C.c_void_p(FAKE)
+    args = lambda **k: [k.get("logits", p), k.get("M", 4), k.get("E", 8), k.get("topk", 2), 1, k.get("bs", 16),
+                        p, p, k.get("st", p), p, p, k.get("cap", 1024), None]
+    assert _status("moe_route_align", *args(topk=9))[0] == wq.WQ_ERR_INVALID            # topk > E
+    assert _status("moe_route_align", *args(E=2000, topk=2))[0] == wq.WQ_ERR_UNSUPPORTED
+    assert _status("moe_route_align", *args(topk=17, E=32))[0] == wq.WQ_ERR_UNSUPPORTED  # topk > 16
+    assert _status("moe_route_align", *args(bs=24))[0] == wq.WQ_ERR_UNSUPPORTED         # block size
+    assert _status("moe_route_align", *args(cap=16))[0] == wq.WQ_ERR_INVALID            # capacity
+    assert _status("moe_route_align", *args(cap=136))[0] == wq.WQ_ERR_INVALID           # not a multiple
+    assert _status("moe_route_align", *args(logits=None))[0] == wq.WQ_ERR_INVALID
+    assert _status("moe_route_align", *args(st=None))[0] == wq.WQ_ERR_INVALID
+    assert _status("moe_route_align", *args(M=-1))[0] == wq.WQ_ERR_INVALID
+
+
 def _desc(**kw):
     d = _lib.WqMoeGemmDesc()
     d.struct_size = C.sizeof(_lib.WqMoeGemmDesc)

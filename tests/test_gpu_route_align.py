@@ -101,3 +101,33 @@ def test_align_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("M,E,topk", [(1, 8, 2), (7, 8, 2), (16, 160, 6), (17, 160, 6), (64, 8, 2), (300, 160, 6),
+                                      (12, 1024, 8), (33, 1024, 8), (16, 2, 2)])
+@pytest.mark.parametrize("bs", [16, 64, 128])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_align_fused_equals_two_calls(M, E, topk, bs, renorm):
+    """moe_route_align (one kernel up to 16 tokens, two above) gives exactly
+    the outputs of moe_route followed by moe_align."""
+    need_gpu()
+    rng = np.random.default_rng(1000 + M + E + bs)
+    logits = rng.standard_normal((M, E)).astype(np.float32)
+    logits[:, : E // 2] += np.float32(0.5)  # skew: some experts get many tokens
+    lg = torch.from_numpy(logits).cuda()
+    say("route_align", M, E, topk, bs, renorm)
+    w1, i1 = wq.moe_route(lg, topk, renorm)
+    cap = wq.moe_align_capacity(M, topk, E, bs)
+    st1, ex1, nt1 = wq.moe_align(i1, E, bs, cap)
+    w2 = torch.full((M, topk), -1.0, dtype=torch.float32, device="cuda")
+    i2 = torch.full((M, topk), -7, dtype=torch.int32, device="cuda")
+    st2 = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    ex2 = torch.full((cap // bs,), -7, dtype=torch.int32, device="cuda")
+    nt2 = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    wq.moe_route_align(lg, topk, renorm, bs, w2, i2, st2, ex2, nt2, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(i1, i2)
+    assert int(nt1[0]) == int(nt2[0])
+    assert torch.equal(st1[:cap], st2)
+    assert torch.equal(ex1[: cap // bs], ex2)

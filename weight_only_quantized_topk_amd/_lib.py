@@ -16,7 +16,7 @@ WQ_PACK_INTERLEAVE_GATE_UP = 1
 
 EXPORTS = (
     "wq_version", "wq_status_string", "wq_last_error",
-    "moe_route", "moe_align_capacity", "moe_align",
+    "moe_route", "moe_align_capacity", "moe_align", "moe_route_align",
     "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
     "sparse24_w4a16_gemm",
     "wq_pack_w4_bytes", "wq_pack_w8_bytes", "wq_pack_w4", "wq_pack_w8",
@@ -74,6 +74,7 @@ def load():
     L.moe_align_capacity.argtypes = [i, i, i, i]
     L.moe_align_capacity.restype = sz
     L.moe_align.argtypes = [p, i, i, i, i, p, p, p, sz, p]
+    L.moe_route_align.argtypes = [p, i, i, i, i, i, p, p, p, p, p, sz, p]
     L.moe_gemm_workspace_bytes.argtypes = [i, i, i, i, i, i, sz, i]
     L.moe_gemm_workspace_bytes.restype = sz
     L.moe_w4a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
@@ -90,7 +91,7 @@ def load():
     L.wq_pack_sparse24_meta_bytes.argtypes = [i, i]
     L.wq_pack_sparse24_meta_bytes.restype = sz
     L.wq_pack_sparse24.argtypes = [i, i, p, p, p, p, p, p]
-    for f in ("moe_route", "moe_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm", "wq_pack_w4",
+    for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm", "wq_pack_w4",
               "wq_pack_w8", "wq_pack_sparse24"):
         getattr(L, f).restype = i
     _lib = L

@@ -183,6 +183,56 @@ wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block
     }
 }
 
+wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int renormalize, int block_size,
+                          float* d_topk_weights, int32_t* d_topk_ids, int32_t* d_sorted_token_ids,
+                          int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded, size_t capacity, void* stream) {
+    try {
+        WQ_REQUIRE(M >= 0, WQ_ERR_INVALID, "M = %d < 0", M);
+        WQ_REQUIRE(E >= 1 && topk >= 1 && topk <= E, WQ_ERR_INVALID, "need 1 <= topk <= E (topk %d, E %d)", topk, E);
+        WQ_REQUIRE(E <= 1024, WQ_ERR_UNSUPPORTED, "E = %d > 1024", E);
+        WQ_REQUIRE(topk <= 16, WQ_ERR_UNSUPPORTED, "topk = %d > 16", topk);
+        WQ_REQUIRE(valid_block_size(block_size), WQ_ERR_UNSUPPORTED, "block_size %d not in {16,32,64,128,256}",
+                   block_size);
+        WQ_REQUIRE((int64_t)M * topk <= MAX_PAIRS, WQ_ERR_UNSUPPORTED, "M*topk > 2^24");
+        const size_t need = moe_align_capacity(M, topk, E, block_size);
+        WQ_REQUIRE(capacity >= need, WQ_ERR_INVALID, "capacity %zu < required %zu", capacity, need);
+        WQ_REQUIRE(capacity % (size_t)block_size == 0, WQ_ERR_INVALID, "capacity not a multiple of block_size");
+        WQ_REQUIRE(capacity <= (size_t)0x7fffffff, WQ_ERR_UNSUPPORTED, "capacity too large");
+        if (M > 0) {
+            WQ_TRY(check_ptr(d_logits, "logits"));
+            WQ_TRY(check_ptr(d_topk_weights, "topk_weights"));
+            WQ_TRY(check_ptr(d_topk_ids, "topk_ids"));
+        }
+        WQ_TRY(check_ptr(d_sorted_token_ids, "sorted_token_ids"));
+        WQ_TRY(check_ptr(d_expert_ids, "expert_ids"));
+        WQ_TRY(check_ptr(d_num_tokens_post_padded, "num_tokens_post_padded"));
+        if (M > 0) {
+            WQ_TRY(check_dev(d_logits, "logits"));
+            WQ_TRY(check_dev(d_topk_weights, "topk_weights"));
+            WQ_TRY(check_dev(d_topk_ids, "topk_ids"));
+        }
+        WQ_TRY(check_dev(d_sorted_token_ids, "sorted_token_ids"));
+        WQ_TRY(check_dev(d_expert_ids, "expert_ids"));
+        WQ_TRY(check_dev(d_num_tokens_post_padded, "num_tokens_post_padded"));
+        hipStream_t s = (hipStream_t)stream;
+        const int rn = renormalize ? 1 : 0;
+        if (M > 0 && wq::route_align_fused(M, topk)) {
+            wq::launch_route_align(d_logits, M, E, topk, rn, d_topk_weights, d_topk_ids, block_size,
+                                   d_sorted_token_ids, d_expert_ids, d_num_tokens_post_padded, (int)capacity, s);
+        } else {
+            if (M > 0) {
+                wq::launch_route(d_logits, M, E, topk, rn, d_topk_weights, d_topk_ids, s);
+                WQ_TRY(after_launch("moe_route_align"));
+            }
+            wq::launch_align(d_topk_ids, M * topk, E, block_size, d_sorted_token_ids, d_expert_ids,
+                             d_num_tokens_post_padded, (int)capacity, s);
+        }
+        return after_launch("moe_route_align");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_route_align: unexpected exception");
+    }
+}
+
 // ---------------------------------------------------------------------------
 size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, int k_in, size_t capacity,
                                 int act_order) {

@@ -25,6 +25,10 @@ void launch_route(const float* logits, int M, int E, int topk, int renormalize, 
                   hipStream_t s);
 void launch_align(const int32_t* ids, int T, int E, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp,
                   int cap, hipStream_t s);
+// route + align in one kernel (batches of at most 16 tokens and 1024 pairs)
+bool route_align_fused(int M, int topk);
+void launch_route_align(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids, int BS,
+                        int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, int cap, hipStream_t s);
 
 struct GemmArgs {
     const uint16_t* a;        // activations (x, gathered x, or H), 16-bit

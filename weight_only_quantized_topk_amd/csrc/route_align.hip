@@ -15,6 +15,9 @@
 // popcount of the lower lanes; across the 16 waves, per-wave counts in LDS give
 // each wave its offset.  No LDS atomic decides an order, so the output is the
 // unique stable one.
+// moe_route_align: for batches up to 16 tokens one 1024-thread workgroup does
+// both, the expert ids staying in LDS between the two (one launch instead of
+// two, the same outputs).
 // (The token sort is the moe_align_block_size step of "Marlin moe integration",
 // nm-vllm PR 266, review thread on its kernel and its block size of 16.)
 #include "common.hpp"
@@ -28,13 +31,11 @@ __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
     return va > vb || (va == vb && ea < eb);
 }
 
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int M, int E, int topk,
-                                                    int renormalize, float* __restrict__ w_out,
-                                                    int32_t* __restrict__ ids_out) {
-    const int lane = threadIdx.x & 63;
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;
-    const float* l = logits + (size_t)m * E;
+// routes token row `l` (E logits) with one wave; lane j < topk writes slot j's
+// weight and expert to w_row[j] / ids_row[j] (and to lds_ids[j] if given)
+__device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int topk, int renormalize, int lane,
+                                            float* __restrict__ w_row, int32_t* __restrict__ ids_row,
+                                            int* lds_ids) {
     float v[ROUTE_MAX_PER_LANE];
     uint32_t avail = 0;  // bit i: slot i of this lane holds a not-yet-chosen expert
 #pragma unroll
@@ -90,9 +91,20 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         denom = part;
     }
     if (lane < topk) {
-        w_out[(size_t)m * topk + lane] = (float)(ex / denom);
-        ids_out[(size_t)m * topk + lane] = sel_e;
+        w_row[lane] = (float)(ex / denom);
+        ids_row[lane] = sel_e;
+        if (lds_ids) lds_ids[lane] = sel_e;
     }
+}
+
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int M, int E, int topk,
+                                                    int renormalize, float* __restrict__ w_out,
+                                                    int32_t* __restrict__ ids_out) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    route_token(logits + (size_t)m * E, E, topk, renormalize, lane, w_out + (size_t)m * topk,
+                ids_out + (size_t)m * topk, nullptr);
 }
 
 void launch_route(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids,
@@ -103,12 +115,17 @@ void launch_route(const float* logits, int M, int E, int topk, int renormalize, 
 // ---------------------------------------------------------------------------
 constexpr int ALIGN_THREADS = 1024;
 constexpr int ALIGN_WAVES = ALIGN_THREADS / 64;
+// the fused route + align kernel serves batches up to 16 tokens (one per wave:
+// routing a token is a chain of dependent latencies, and 4 tokens per wave made
+// the fused kernel slower than the two separate ones)
+constexpr int ROUTE_ALIGN_MAX_M = 16;
+constexpr int ROUTE_ALIGN_MAX_T = 1024;
 
-__global__ __launch_bounds__(ALIGN_THREADS) void align_kernel(const int32_t* __restrict__ ids, int T, int E, int BS,
-                                                              int nbits, int32_t* __restrict__ sorted,
-                                                              int32_t* __restrict__ expert_ids,
-                                                              int32_t* __restrict__ ntpp, int cap) {
-    extern __shared__ int smem[];
+// the align steps for one 1024-thread workgroup; ids may point to global or
+// LDS memory; smem holds E * (1 + ALIGN_WAVES) ints
+__device__ __forceinline__ void align_body(const int32_t* ids, int T, int E, int BS, int nbits,
+                                           int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
+                                           int32_t* __restrict__ ntpp, int cap, int* smem) {
     int* cnt = smem;            // [E]   counts, later the running write position
     int* wcnt = smem + E;       // [ALIGN_WAVES][E] per-wave counts of the current chunk
     __shared__ int wsum[ALIGN_WAVES];
@@ -183,16 +200,60 @@ __global__ __launch_bounds__(ALIGN_THREADS) void align_kernel(const int32_t* __r
     }
 }
 
-void launch_align(const int32_t* ids, int T, int E, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp,
-                  int cap, hipStream_t s) {
+__global__ __launch_bounds__(ALIGN_THREADS) void align_kernel(const int32_t* __restrict__ ids, int T, int E, int BS,
+                                                              int nbits, int32_t* __restrict__ sorted,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ ntpp, int cap) {
+    extern __shared__ int smem[];
+    align_body(ids, T, E, BS, nbits, sorted, expert_ids, ntpp, cap, smem);
+}
+
+// moe_route + moe_align for small batches in one workgroup: its 16 waves route
+// the tokens (one wave per token), the expert ids stay in LDS for the align steps
+__global__ __launch_bounds__(ALIGN_THREADS) void route_align_kernel(const float* __restrict__ logits, int M, int E,
+                                                                    int topk, int renormalize,
+                                                                    float* __restrict__ w_out,
+                                                                    int32_t* __restrict__ ids_out, int BS, int nbits,
+                                                                    int32_t* __restrict__ sorted,
+                                                                    int32_t* __restrict__ expert_ids,
+                                                                    int32_t* __restrict__ ntpp, int cap) {
+    extern __shared__ int smem[];
+    int* sids = smem + E * (1 + ALIGN_WAVES);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int m = wave; m < M; m += ALIGN_WAVES)
+        route_token(logits + (size_t)m * E, E, topk, renormalize, lane, w_out + (size_t)m * topk,
+                    ids_out + (size_t)m * topk, sids + m * topk);
+    __syncthreads();
+    align_body(sids, M * topk, E, BS, nbits, sorted, expert_ids, ntpp, cap, smem);
+}
+
+static int id_bits(int E) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
+    return nbits;
+}
+
+void launch_align(const int32_t* ids, int T, int E, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp,
+                  int cap, hipStream_t s) {
     const size_t lds = sizeof(int) * (size_t)E * (1 + ALIGN_WAVES);
     if (lds > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&align_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(ALIGN_THREADS), lds, s, ids, T, E, BS, nbits, sorted, expert_ids,
-                       ntpp, cap);
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(ALIGN_THREADS), lds, s, ids, T, E, BS, id_bits(E), sorted,
+                       expert_ids, ntpp, cap);
+}
+
+bool route_align_fused(int M, int topk) { return M <= ROUTE_ALIGN_MAX_M && M * topk <= ROUTE_ALIGN_MAX_T; }
+
+void launch_route_align(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids, int BS,
+                        int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, int cap, hipStream_t s) {
+    const size_t lds = sizeof(int) * ((size_t)E * (1 + ALIGN_WAVES) + (size_t)M * topk);
+    if (lds > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_align_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(route_align_kernel, dim3(1), dim3(ALIGN_THREADS), lds, s, logits, M, E, topk, renormalize, w,
+                       ids, BS, id_bits(E), sorted, expert_ids, ntpp, cap);
 }
 
 }  // namespace wq

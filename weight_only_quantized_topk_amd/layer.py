@@ -114,8 +114,8 @@ class MoERunner:
         self.out = torch.empty((M, p.K), dtype=p.act, device=dev)
 
     def route_align(self, logits, stream=None):
-        ops.moe_route(logits, self.topk, self.renormalize, self.w, self.ids, stream=stream)
-        ops.moe_align(self.ids, self.p.E, self.bs, self.cap, self.st, self.ex, self.nt, stream=stream)
+        ops.moe_route_align(logits, self.topk, self.renormalize, self.bs, self.w, self.ids, self.st, self.ex,
+                            self.nt, self.cap, stream=stream)
 
     def gate_up(self, x, stream=None):
         p = self

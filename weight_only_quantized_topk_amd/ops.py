@@ -17,7 +17,7 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
                    WqMoeGemmDesc, check, load)
 
 __all__ = [
-    "moe_route", "moe_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
+    "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
     "sparse24_w4a16_gemm", "pack_w4", "pack_w8", "pack_sparse24", "act_code",
 ]
 
@@ -65,6 +65,17 @@ def moe_route(logits, topk: int, renormalize: bool = True, topk_weights=None, to
     check(load().moe_route(_ptr(logits), M, E, topk, int(bool(renormalize)), _ptr(topk_weights), _ptr(topk_ids),
                            _stream(stream)), "moe_route")
     return topk_weights, topk_ids
+
+
+def moe_route_align(logits, topk: int, renormalize: bool, block_size: int, topk_weights, topk_ids,
+                    sorted_token_ids, expert_ids, num_tokens_post_padded, capacity: int, stream=None):
+    """moe_route then moe_align in one call (one kernel for batches up to 16
+    tokens); every output buffer is the caller's."""
+    M, E = logits.shape
+    check(load().moe_route_align(_ptr(logits), M, E, topk, int(bool(renormalize)), block_size, _ptr(topk_weights),
+                                 _ptr(topk_ids), _ptr(sorted_token_ids), _ptr(expert_ids),
+                                 _ptr(num_tokens_post_padded), capacity, _stream(stream)), "moe_route_align")
+    return topk_weights, topk_ids, sorted_token_ids, expert_ids, num_tokens_post_padded
 
 
 def moe_align_capacity(M: int, topk: int, E: int, block_size: int) -> int:
