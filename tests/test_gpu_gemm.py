@@ -26,7 +26,8 @@ W4AO = W4.with_(name="w4ao-small", act_order=True)
 W4PC = W4.with_(name="w4-percol-small", group_size=-1)
 W8 = gen.CFG2.with_(name="w8-small", E=8, topk=2, K=512, N=384)
 W8E = gen.CFG5.with_(name="w8-many-small", E=40, topk=6, K=256, N=256, zipf_s=1.1)
-# long k_in, narrow output: the large-batch DOWN splits K into 4 slices
+# long k_in, narrow output: the large-batch DOWN splits K into 4 slices; their
+# GATE_UP (8192 outputs) takes the 512-row shape
 W4K = W4.with_(name="w4-longk", K=256, N=4096)
 W8K = W8.with_(name="w8-longk", K=256, N=4096)
 SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E, "w4k": W4K, "w8k": W8K}
@@ -130,7 +131,7 @@ def h_perm(spec, wts, e):
     return np.arange(spec.N)
 
 
-@pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e"])
+@pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e", "w4k", "w8k"])
 @pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_gate_up(key, bs, M):
@@ -166,20 +167,22 @@ def test_down(key, bs, M):
 
 
 @pytest.mark.parametrize("key", ["w4k", "w8k"])
+@pytest.mark.parametrize("bs", [64, 128])
 @pytest.mark.parametrize("M", [37, 300])
-def test_down_split_k(key, M):
-    """k_in = 4096 with 256 outputs: the large-batch DOWN writes 4 fp32 slabs
-    of partial sums (its workspace says so) that the combine adds."""
+def test_down_split_k(key, bs, M):
+    """k_in = 4096 with 256 outputs: the large-batch DOWN (blocks of 64 or
+    128 rows) writes 4 fp32 slabs of partial sums (its workspace says so)
+    that the combine adds."""
     spec = SPECS[key]
-    ws = _check_down(key, 128, M)
+    ws = _check_down(key, bs, M)
     assert ws >= 4 * M * spec.topk * spec.K * 4
 
 
 def test_down_split_wide_grid_w4():
     """int4, 4096 outputs, k_in 4096, M = 1024 (2048 pairs): the DOWN grid of
-    256-row tiles has fewer than 1024 workgroups, so K is split in 4 slices on
-    the 256 x 128 four-wave shape (the workspace holds 4 fp32 slabs); the
-    output of sampled tokens against the oracle."""
+    512-row tiles is smaller than one round of resident workgroups, so K is
+    split in 4 slices on the 512 x 128 eight-wave shape (the workspace holds 4
+    fp32 slabs); the output of sampled tokens against the oracle."""
     need_gpu()
     spec = W4.with_(name="w4-split-wide", K=4096, N=4096)
     wts = gen.make_moe_weights(spec, seed_config=508)

@@ -240,7 +240,7 @@ size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, in
     size_t b = 0;
     if ((stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_RAW) && act_order) b += round256(capacity * k_in * 2);
     if (stage == WQ_STAGE_DOWN)
-        b += round256((size_t)wq::prefill_down_split(M * topk, E, n_out, k_in) * M * topk * n_out * sizeof(float));
+        b += round256((size_t)wq::prefill_down_split_max(M * topk, E, n_out, k_in) * M * topk * n_out * sizeof(float));
     return b;
 }
 

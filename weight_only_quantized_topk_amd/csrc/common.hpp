@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace wq {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -191,6 +193,15 @@ __device__ __forceinline__ u32x4 dequant_w8x8(uint32_t d0, uint32_t d1) {
 // ---------------------------------------------------------------------------
 // misc
 // ---------------------------------------------------------------------------
+// calls f(std::integral_constant<int, i>) for i in [B, E), unrolled
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 __device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 ldg128_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

@@ -49,11 +49,14 @@ struct GemmArgs {
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
 void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
-// large-batch path: 256 or 128 weight rows x 128 (or 64) token rows through LDS
+// large-batch path: 512, 256 or 128 weight rows (dequantized in registers) x
+// 128 (or 64) token rows (staged in LDS)
 bool prefill_supported(int n_out, int k_in, int block_size);
-// K slices of the large-batch DOWN stage for T = M*topk rows over E experts
-// (1, 2 or 4); the DOWN workspace holds that many fp32 slabs of T x n_out
-int prefill_down_split(int T, int E, int n_out, int k_in);
+// K slices of the large-batch DOWN stage for T = M*topk rows over E experts in
+// blocks of block_size rows (1, 2 or 4); the DOWN workspace holds that many
+// fp32 slabs of T x n_out.  _max: the largest over the supported block sizes
+int prefill_down_split(int T, int E, int n_out, int k_in, int block_size);
+int prefill_down_split_max(int T, int E, int n_out, int k_in);
 // returns the number of K slices (Y slabs) it wrote
 int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
 

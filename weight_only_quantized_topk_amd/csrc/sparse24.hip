@@ -27,18 +27,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-#include <type_traits>
-
 namespace wq {
-
-// calls f(std::integral_constant<int, i>) for i in [B, E), unrolled
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
 
 constexpr int SP_WAVES = 4;
 constexpr int SP_THREADS = 64 * SP_WAVES;
