@@ -12,7 +12,9 @@
 //    v_mfma_f32_16x16x32 instructions; each wave loads its own tiles with
 //    coalesced 128-bit (int8) or 64-bit (int4) loads two K steps ahead and
 //    dequantizes them in registers (int8 exact; int4: q * group scale rounded
-//    once to fp16).
+//    once to fp16).  int8 weights are streamed past the caches; int4 weights
+//    are cached, which measured 9-13 % faster (an expert's weight tile is
+//    re-read by every token tile of the expert, about 8 at M = 4096).
 //  - The BM token rows of a K step (gathered through sorted_token_ids, or read
 //    directly for H and the act-order-permuted activations) are staged in one
 //    of two LDS buffers: step s + 1 is stored while step s is multiplied, so a
@@ -95,9 +97,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
         } else {
             const int c = step >> 1, half = step & 1;  // a 128-channel chunk spans two K steps
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
-                w4[sl][t] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x2*>(wsrc + t * tile_stride + (size_t)c * CHUNK_BYTES + 8 * half));
+            for (int t = 0; t < RT; ++t)  // cached: the many token tiles of an expert re-read them
+                w4[sl][t] = *reinterpret_cast<const u32x2*>(wsrc + t * tile_stride + (size_t)c * CHUNK_BYTES + 8 * half);
             const int grp = g.groups > 1 ? c : 0;
 #pragma unroll
             for (int t = 0; t < RT; ++t) sc[sl][t] = ssrc[(size_t)grp * g.n_out + t * TILE_ROWS];
