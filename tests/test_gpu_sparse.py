@@ -63,6 +63,52 @@ def test_sparse_float_long_k(M):
     assert_close_fp(y, ref, "sparse K=2304 M=%d" % M)
 
 
+@pytest.mark.parametrize("N", [512, 112])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_sparse_decode_kernel(M, N):
+    """M <= 4: the decode kernel (token rows staged in LDS, waves splitting the
+    9 chunks of K = 2304 with a tail, two row tiles per workgroup; N = 112 has
+    an odd tile count, so the last workgroup holds one valid tile)."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=2304, N=N)
+    sw = gen.make_sparse_weights(spec, seed_config=315)
+    x = gen.make_sparse_x(spec, M, seed_config=316 + M)
+    say("sparse decode", M, N)
+    y = run_sparse(sw, x, spec.N)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128)
+    assert_close_fp(y, ref, "sparse decode M=%d N=%d" % (M, N))
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_sparse_exact_integer_decode(M):
+    """Exact-integer case through the decode kernel: unit scales, x in
+    {-1, 0, 1}, so every output is an integer the fp16 result holds exactly."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=512, N=96)
+    sw = gen.make_sparse_weights(spec, seed_config=317)
+    x = np.random.default_rng(M).integers(-1, 2, size=(M, spec.K)).astype(np.float32)
+    ones = np.ones((spec.K // 128, spec.N), np.float32)
+    sw.s = gen.round_to("f16", ones)
+    say("sparse exact decode", M)
+    y = run_sparse(sw, gen.round_to("f16", x), spec.N)
+    ref = oracle.sparse24(x, sw.vals, sw.idx, ones, 128)
+    assert np.abs(ref).max() < 2048
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_sparse_decode_too_long_for_lds():
+    """M = 4 with K = 16384: the token rows (128 KiB) do not fit the decode
+    kernel's LDS, so the streaming kernel runs; same result contract."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=16384, N=64)
+    sw = gen.make_sparse_weights(spec, seed_config=318)
+    x = gen.make_sparse_x(spec, 4, seed_config=318)
+    say("sparse long row")
+    y = run_sparse(sw, x, spec.N)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128)
+    assert_close_fp(y, ref, "sparse K=16384 M=4")
+
+
 def test_sparse_large_batch_narrow_n():
     """M > 128 with N not a multiple of 256: the streaming kernel, with a
     partial last workgroup of row tiles."""

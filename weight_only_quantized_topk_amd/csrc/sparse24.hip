@@ -153,6 +153,104 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
     }
 }
 
+// ------------------------------------------------- decode (few tokens)
+// One workgroup per TPW 16-row weight tiles, NW waves per tile splitting its
+// 256-channel chunks (wave w takes chunks w, w + NW, ...), each keeping DEPTH
+// chunks of its weights in flight in registers.  The token rows (M * K fp16, at most
+// 64 KiB) are staged in LDS once, before the chunk loop, rows padded by 16
+// bytes so the 16 column lanes of the B operand hit distinct banks; columns
+// at or beyond M read row M - 1.  So the loop's only global loads are the
+// weight stream: a token load among them would make every wait for it also
+// wait for the weight loads issued before it (the wait counter is in order),
+// shortening the prefetch.  The NW partial sums are added in LDS in wave
+// order.  Loads sit outside branches except in the guarded tail of fewer than
+// DEPTH chunks.
+template <int NW, int DEPTH, int TPW>
+__global__ __launch_bounds__(NW * TPW * 64) void sparse24_decode_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                    int N, const uint8_t* __restrict__ vals,
+                                                                    const uint8_t* __restrict__ meta,
+                                                                    const uint16_t* __restrict__ scales,
+                                                                    uint16_t* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs_dyn[];
+    __shared__ f32x4 red[TPW][NW][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = (tid >> 6) % NW;  // K slice of this wave
+    const int tw = (tid >> 6) / NW;    // tile of this wave within the workgroup
+    const int t = min(TPW * (int)blockIdx.x + tw, N / 16 - 1);
+    const bool tvalid = TPW * (int)blockIdx.x + tw < N / 16;
+    const int C = K / SP_KCHUNK;
+    const int nrow = lane & 15;
+    const int xrow_b = 2 * K + 16;  // LDS bytes per token row
+
+    // weights first, so their loads are in flight during the token staging
+    const int nw = wave < C ? (C - 1 - wave) / NW + 1 : 0;
+    const int clast = wave < C ? wave + (nw - 1) * NW : C - 1;  // chunk C - 1 for a wave without chunks
+    const uint8_t* vt = vals + (size_t)t * C * 1024 + lane * 16;
+    const uint8_t* mt = meta + (size_t)t * C * 512 + lane * 8;
+    const uint16_t* sn = scales + 16 * t + nrow;
+    u32x4 wv[DEPTH];
+    u32x2 wm[DEPTH];
+    uint32_t ws0[DEPTH], ws1[DEPTH];
+    auto wload = [&](int i, int slot) {
+        const int c = min(wave + NW * i, clast);
+        wv[slot] = ldg128_stream(vt + (size_t)c * 1024);
+        wm[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
+        ws0[slot] = sn[(size_t)(2 * c) * N];
+        ws1[slot] = sn[(size_t)(2 * c + 1) * N];
+    };
+#pragma unroll
+    for (int p = 0; p < DEPTH; ++p) wload(p, p);
+
+    const int pieces = M * (K / 8);  // 16-byte token pieces
+    for (int q = tid; q < pieces; q += NW * TPW * 64) {
+        const int row = q / (K / 8), pc = q - row * (K / 8);
+        *reinterpret_cast<u32x4*>(xs_dyn + row * xrow_b + 16 * pc) = ldg128(x + (size_t)row * K + 8 * pc);
+    }
+    __syncthreads();
+
+    const uint8_t* xl = xs_dyn + min(nrow, M - 1) * xrow_b + 16 * (lane >> 4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto body = [&](int i, auto U) {
+        constexpr int u = decltype(U)::value;
+        const uint8_t* xc = xl + (size_t)min(wave + NW * i, clast) * (2 * SP_KCHUNK);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t sv = (s < 2) ? ws0[u] : ws1[u];
+            const u32x4 a = dequant_w4_f16_scaled(wv[u][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+            const int idx = (int)wm[u][s >> 1];
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(xc + 128 * s);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(xc + 128 * s + 64);
+            const u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            if (s & 1) acc = smfmac16x16x64<1>(a, b, idx, acc);
+            else acc = smfmac16x16x64<0>(a, b, idx, acc);
+        }
+        wload(i + DEPTH, u);
+    };
+    int i0 = 0;
+    for (; i0 + DEPTH <= nw; i0 += DEPTH) static_for<0, DEPTH>([&](auto U) { body(i0 + decltype(U)::value, U); });
+    static_for<0, DEPTH - 1>([&](auto U) {
+        if (i0 + decltype(U)::value < nw) body(i0 + decltype(U)::value, U);
+    });
+
+    red[tw][wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 1; w < NW; ++w) acc += red[tw][w][lane];
+        if (tvalid && nrow < M) {
+            u32x2 stv;
+            stv[0] = (uint32_t)f32_to_f16(acc[0]) | ((uint32_t)f32_to_f16(acc[1]) << 16);
+            stv[1] = (uint32_t)f32_to_f16(acc[2]) | ((uint32_t)f32_to_f16(acc[3]) << 16);
+            *reinterpret_cast<u32x2*>(y + (size_t)nrow * N + 16 * t + 4 * (lane >> 4)) = stv;
+        }
+    }
+}
+
+// LDS bytes of the decode kernel's token rows, and the most it takes
+static size_t sparse24_decode_lds(int M, int K) { return (size_t)M * (2 * (size_t)K + 16); }
+constexpr size_t SP_DECODE_LDS_MAX = 96 * 1024;
+
 // ------------------------------------------------------------ large batches
 constexpr int SPT_BN = 256;  // weight rows per workgroup (4 waves x 4 tiles of 16)
 constexpr int SPT_BM = 64;   // tokens per workgroup (4 B tiles of 16)
@@ -276,10 +374,26 @@ static void launch_stream(const uint16_t* x, int M, int K, int N, const uint8_t*
     hipLaunchKernelGGL((sparse24_stream_kernel<R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales, y);
 }
 
-// batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480
+template <int NW, int TPW>
+static void launch_decode(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+                          const uint16_t* scales, uint16_t* y, hipStream_t s) {
+    const size_t lds = sparse24_decode_lds(M, K);
+    auto kern = sparse24_decode_kernel<NW, 4, TPW>;
+    if (lds + sizeof(f32x4) * 64 * NW * TPW > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+    hipLaunchKernelGGL(kern, dim3((N / 16 + TPW - 1) / TPW), dim3(NW * TPW * 64), lds, s, x, M, K, N, vals, meta,
+                       scales, y);
+}
+
+// batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480:
+// M = 1, 2: 18 -> 13 us; M = 4: 18.6 -> 17.0 us with the decode kernel
 void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                      const uint16_t* scales, uint16_t* y, hipStream_t s) {
-    if (M > 128 && N % SPT_BN == 0) {
+    if (M <= 4 && sparse24_decode_lds(M, K) <= SP_DECODE_LDS_MAX) {
+        if (M <= 2) launch_decode<2, 2>(x, M, K, N, vals, meta, scales, y, s);
+        else launch_decode<4, 2>(x, M, K, N, vals, meta, scales, y, s);
+    } else if (M > 128 && N % SPT_BN == 0) {
         const dim3 grid(N / SPT_BN, (M + SPT_BM - 1) / SPT_BM);
         hipLaunchKernelGGL(sparse24_tile_kernel<2>, grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta, scales, y);
     } else if (M <= 16) {
