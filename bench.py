@@ -11,7 +11,8 @@ prompt length of the end-to-end latency workload in "[Kernel] W8A16 Int8
 inside FusedMoE" (vLLM PR 7415, latency table).  The other batch sizes of that
 layer's sweep are timed too and reported under "sweep"; the other workloads
 (int4 act-order Mixtral, the 2:4-sparse int4 linear layer, the DeepSeek-V2
-shaped int8 layer) under "rows".
+shaped int8 layer) under "rows", with the ExpertsInt8 load-time quantizer on
+Mixtral's w1 (HBM GB/s).
 
 Timing: before every step (warm-up and timed) 1 GiB of scratch memory is
 written, outside the timed span, so the weights come from HBM and not from
@@ -250,7 +251,38 @@ def bench_rows(torch, wq, gen, timer, steps, warmup):
         r = measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup)
         log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
         rows.append(dict(workload=spec.name, **rounded(r)))
+    del dev
+    rows.append(dict(workload="experts-int8-quantize-mixtral-w1", **rounded(measure_quant(torch, wq, timer, steps,
+                                                                                         warmup))))
+    log("bench: rows: quantizer %.4f ms" % rows[-1]["ms_per_step"])
     return rows
+
+
+def measure_quant(torch, wq, timer, steps, warmup):
+    """The ExpertsInt8 load-time quantizer on Mixtral-8x7B's w1 (8 experts x
+    28672 output columns x 4096 bf16 weights, seeded normal x 0.02): HBM-bound,
+    2 bytes read and 1 written per weight."""
+    E, n_out, k = 8, 2 * 14336, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20240807)
+    w = (torch.randn((E, n_out, k), generator=g, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    q = torch.empty(w.shape, dtype=torch.int8, device="cuda")
+    sc = torch.empty(w.shape[:-1], dtype=torch.bfloat16, device="cuda")
+
+    def step(marks):
+        wq.quantize_w8(w, q, sc)
+        if marks:
+            marks[0].record()
+
+    spans, wall = timer.run(step, steps, warmup, 1)
+    ms = float(spans[:, 0].mean())
+    nbytes = E * n_out * k * 3 + E * n_out * 2
+    r = dict(M=0, ms_per_step=ms, ms_per_step_median=float(np.median(spans[:, 0])), wall_ms_per_step=wall,
+             alg_bytes=int(nbytes), alg_flops=0, shape=[E, n_out, k])
+    r.update(rates(nbytes, 0, ms))
+    del w, q, sc
+    torch.cuda.empty_cache()
+    return r
 
 
 def main(argv=None):

@@ -208,6 +208,30 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
                               const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* ExpertsInt8 quantization at load time                                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * Produces the int8 weights and per-column scales of the W8A16 path from the
+ * 16-bit checkpoint on the GPU ("[Kernel] W8A16 Int8 inside FusedMoE", vLLM
+ * PR 7415, opening description: symmetric per-column per-expert int8 with
+ * scales extracted at startup; its "How to convert models to ExpertsInt8?"
+ * answer: quantization on the fly).  For each of `rows` rows of k weights
+ * (row = one expert's output column, rows = E * n_out):
+ *   s = round_to_dtype(max_k |w| / 127)      float32 division, nearest-even
+ *   q = clamp(round_half_even(w / s), -127, 127), float32 division; q = 0
+ *       where s == 0
+ *   d_w      [rows, k] 16-bit (dtype: WQ_BF16 or WQ_F16), 16-byte aligned
+ *   d_q      int8 [rows, k], 8-byte aligned: the canonical codes wq_pack_w8
+ *            takes (copied to host)
+ *   d_scales uint16 [rows]: the dtype's bit patterns, i.e. the [E, 1, n_out]
+ *            scales wq_pack_w8 takes
+ * Limits: k % 8 == 0; finite inputs (NaN or infinity give unspecified codes).
+ * Device memory, all of it owned by the caller; asynchronous on `stream`.
+ */
+wq_status wq_quantize_w8(const void* d_w, int64_t rows, int k, int dtype, int8_t* d_q, uint16_t* d_scales,
+                         void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Offline packers (host memory; not on the hot path)                        */
 /* ------------------------------------------------------------------------ */
 /*

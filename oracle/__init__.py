@@ -52,8 +52,9 @@ def lib():
         L.orc_moe_layer.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, p, i32, p, p, p, i32, p, i64,
                                     p, p, p, p]
         L.orc_sparse24.argtypes = [i64, i32, i32, p, p, p, p, i32, p, i64, p]
+        L.orc_quant_w8.argtypes = [i64, i32, p, i32, p, p]
         for f in ("orc_route", "orc_align", "orc_moe_up", "orc_moe_down", "orc_moe_combine", "orc_moe_layer",
-                  "orc_sparse24"):
+                  "orc_sparse24", "orc_quant_w8"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -194,3 +195,17 @@ def sparse24(x, vals, idx, s, group_size, rows=None):
     _check(lib().orc_sparse24(M, K, N, _ptr(x), _ptr(_c(vals, np.int8)), _ptr(_c(idx, np.uint8)),
                               _ptr(_c(s, np.float32)), gs, _ptr(rows_a), R, _ptr(y)), "sparse24")
     return y
+
+
+def quant_w8(w, bf16: bool):
+    """ExpertsInt8 load-time quantization of 16-bit weights w [..., k] (given as
+    the float32 values that hold them): per row s = max|w| / 127 rounded to the
+    16-bit type, q = w / s rounded half-to-even, clamped to +-127.  Returns
+    (q int8 [..., k], s float32 [...]: the stored 16-bit scales' values)."""
+    w = _c(w, np.float32)
+    k = w.shape[-1]
+    rows = w.size // k
+    q = np.empty(w.shape, np.int8)
+    s = np.empty(w.shape[:-1], np.float32)
+    _check(lib().orc_quant_w8(rows, k, _ptr(w), int(bool(bf16)), _ptr(q), _ptr(s)), "quant_w8")
+    return q, s

@@ -24,6 +24,10 @@
  *    act-order; the token sort that pads each expert's tokens to blocks of 16.
  *  - "Add GPTQ Marlin 2:4 sparse structured support" (vLLM PR 4790), opening
  *    description: 2:4 structured sparsity, 4-bit values, group size 128.
+ *  - "[Kernel] W8A16 Int8 inside FusedMoE", opening description and its
+ *    "How to convert models to ExpertsInt8?" answer: the int8 weights and
+ *    their scales are produced from the 16-bit checkpoint when the model loads
+ *    (orc_quant_w8).
  * The router (softmax + top-k), SiLU-and-mul between the two projections and
  * the top-k-weighted sum are the standard fused-MoE steps those threads plug
  * their kernels into; the pages name them only through the fused_moe
@@ -343,6 +347,65 @@ ORC_EXPORT int orc_sparse24(int64_t M, int K, int N, const float* x,
                 }
             }
             y[rr * N + n] = acc;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* ExpertsInt8 quantization at load time ("[Kernel] W8A16 Int8 inside        */
+/* FusedMoE", opening description: symmetric per-column per-expert int8,     */
+/* scales extracted at startup).  The pages state no formula or rounding;     */
+/* the plain reading: per row (one expert's output column) of k weights,      */
+/*   s32 = max_k |w| / 127           (float32, one correctly rounded divide)  */
+/*   s   = s32 rounded to the 16-bit activation type, nearest-even (stored)   */
+/*   q_k = w_k / s (float32 divide) rounded half-to-even, clamped to +-127    */
+/* so that q * s, the weight the GEMM uses, is the nearest int8 multiple of   */
+/* the stored scale; a row whose stored scale is 0 gets q = 0.                */
+/* ------------------------------------------------------------------------ */
+
+/* nearest value with p significant bits and minimum exponent emin (the
+ * subnormal step is 2^(emin - p + 1)), ties to even; |x| beyond the largest
+ * finite value of the format becomes infinite.  Double arithmetic is exact
+ * here: x is a float32, the step a power of two. */
+static double round_sig(double x, int p, int emin, double maxv)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e = ilogb(x);
+    if (e < emin) e = emin;
+    const double step = ldexp(1.0, e - (p - 1));
+    double r = nearbyint(x / step) * step; /* default rounding mode: nearest-even */
+    if (fabs(r) > maxv) r = copysign(INFINITY, x);
+    return r;
+}
+static float round_bf16(float x) { return (float)round_sig(x, 8, -126, 0x1.fep127); }
+static float round_f16(float x) { return (float)round_sig(x, 11, -14, 65504.0); }
+
+ORC_EXPORT int orc_quant_w8(int64_t rows, int k, const float* w, int bf16, int8_t* q, float* s)
+{
+    if (rows < 0 || k <= 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* wr = w + r * k;
+        float mx = 0.0f;
+        for (int i = 0; i < k; ++i) {
+            if (!isfinite(wr[i])) { SET_BAD(bad); }
+            const float a = fabsf(wr[i]);
+            if (a > mx) mx = a;
+        }
+        const float s32 = mx / 127.0f;
+        const float sr = bf16 ? round_bf16(s32) : round_f16(s32);
+        s[r] = sr;
+        for (int i = 0; i < k; ++i) {
+            int v = 0;
+            if (sr != 0.0f) {
+                const float t = wr[i] / sr;
+                v = (int)nearbyintf(t);
+                if (v > 127) v = 127;
+                if (v < -127) v = -127;
+            }
+            q[r * k + i] = (int8_t)v;
         }
     }
     return bad ? -1 : 0;

@@ -93,6 +93,22 @@ def test_route_align_validation():
     assert _status("moe_route_align", *args(M=-1))[0] == wq.WQ_ERR_INVALID
 
 
+def test_quantize_w8_validation():
+    """The load-time quantizer rejects bad sizes, dtypes and pointers before any
+    device work; zero rows is a no-op."""
+    p = C.c_void_p(FAKE)
+    args = lambda **k: [k.get("w", p), k.get("rows", 16), k.get("k", 64), k.get("dt", wq.WQ_BF16), k.get("q", p),
+                        k.get("s", p), None]
+    assert _status("wq_quantize_w8", *args(k=0))[0] == wq.WQ_ERR_INVALID
+    assert _status("wq_quantize_w8", *args(rows=-1))[0] == wq.WQ_ERR_INVALID
+    assert _status("wq_quantize_w8", *args(dt=7))[0] == wq.WQ_ERR_INVALID
+    assert _status("wq_quantize_w8", *args(k=60))[0] == wq.WQ_ERR_UNSUPPORTED        # k % 8
+    assert _status("wq_quantize_w8", *args(w=None))[0] == wq.WQ_ERR_INVALID
+    assert _status("wq_quantize_w8", *args(q=None))[0] == wq.WQ_ERR_INVALID
+    assert _status("wq_quantize_w8", *args(s=None))[0] == wq.WQ_ERR_INVALID
+    assert _status("wq_quantize_w8", *args(rows=0))[0] == wq.WQ_OK
+
+
 def _desc(**kw):
     d = _lib.WqMoeGemmDesc()
     d.struct_size = C.sizeof(_lib.WqMoeGemmDesc)

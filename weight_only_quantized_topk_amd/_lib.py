@@ -18,7 +18,7 @@ EXPORTS = (
     "wq_version", "wq_status_string", "wq_last_error",
     "moe_route", "moe_align_capacity", "moe_align", "moe_route_align",
     "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
-    "sparse24_w4a16_gemm",
+    "sparse24_w4a16_gemm", "wq_quantize_w8",
     "wq_pack_w4_bytes", "wq_pack_w8_bytes", "wq_pack_w4", "wq_pack_w8",
     "wq_pack_sparse24_vals_bytes", "wq_pack_sparse24_meta_bytes", "wq_pack_sparse24",
 )
@@ -80,6 +80,7 @@ def load():
     L.moe_w4a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.moe_w8a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.sparse24_w4a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
+    L.wq_quantize_w8.argtypes = [p, C.c_int64, i, i, p, p, p]
     L.wq_pack_w4_bytes.argtypes = [i, i, i]
     L.wq_pack_w4_bytes.restype = sz
     L.wq_pack_w8_bytes.argtypes = [i, i, i]
@@ -91,7 +92,8 @@ def load():
     L.wq_pack_sparse24_meta_bytes.argtypes = [i, i]
     L.wq_pack_sparse24_meta_bytes.restype = sz
     L.wq_pack_sparse24.argtypes = [i, i, p, p, p, p, p, p]
-    for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm", "wq_pack_w4",
+    for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm",
+              "wq_quantize_w8", "wq_pack_w4",
               "wq_pack_w8", "wq_pack_sparse24"):
         getattr(L, f).restype = i
     _lib = L

@@ -392,6 +392,31 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
 }
 
 // ---------------------------------------------------------------------------
+wq_status wq_quantize_w8(const void* d_w, int64_t rows, int k, int dtype, int8_t* d_q, uint16_t* d_scales,
+                         void* stream) {
+    try {
+        WQ_REQUIRE(rows >= 0 && k > 0, WQ_ERR_INVALID, "quantize_w8: bad sizes rows %lld k %d", (long long)rows, k);
+        WQ_REQUIRE(dtype == WQ_F16 || dtype == WQ_BF16, WQ_ERR_INVALID, "quantize_w8: bad dtype %d", dtype);
+        WQ_REQUIRE(k % 8 == 0, WQ_ERR_UNSUPPORTED, "quantize_w8: k %d not a multiple of 8", k);
+        WQ_REQUIRE((rows + 3) / 4 <= 0x7fffffffLL, WQ_ERR_UNSUPPORTED, "quantize_w8: too many rows");
+        if (rows == 0) return ok();
+        WQ_TRY(check_ptr(d_w, "w"));
+        WQ_TRY(check_ptr(d_q, "q"));
+        WQ_TRY(check_ptr(d_scales, "scales"));
+        WQ_TRY(check_dev(d_w, "w"));
+        WQ_TRY(check_dev(d_q, "q"));
+        WQ_TRY(check_dev(d_scales, "scales"));
+        WQ_REQUIRE(reinterpret_cast<uintptr_t>(d_w) % 16 == 0 && reinterpret_cast<uintptr_t>(d_q) % 8 == 0,
+                   WQ_ERR_INVALID, "quantize_w8: w must be 16-byte and q 8-byte aligned");
+        wq::launch_quant_w8(static_cast<const uint16_t*>(d_w), rows, k, dtype == WQ_BF16, d_q, d_scales,
+                            (hipStream_t)stream);
+        return after_launch("wq_quantize_w8");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "quantize_w8: unexpected exception");
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Offline packers
 // ---------------------------------------------------------------------------
 size_t wq_pack_w4_bytes(int E, int n_out, int k_in) {

@@ -71,4 +71,8 @@ void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf1
 void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                      const uint16_t* scales, uint16_t* y, hipStream_t s);
 
+// ExpertsInt8 load-time quantizer: rows of k 16-bit weights -> int8 codes and
+// one 16-bit scale per row
+void launch_quant_w8(const uint16_t* w, int64_t rows, int k, bool bf16, int8_t* q, uint16_t* s, hipStream_t st);
+
 }  // namespace wq

@@ -18,7 +18,7 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
 
 __all__ = [
     "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
-    "sparse24_w4a16_gemm", "pack_w4", "pack_w8", "pack_sparse24", "act_code",
+    "sparse24_w4a16_gemm", "quantize_w8", "pack_w4", "pack_w8", "pack_sparse24", "act_code",
 ]
 
 
@@ -156,6 +156,25 @@ def sparse24_w4a16_gemm(x, vals, meta, scales, N: int, out=None, group_size: int
     check(load().sparse24_w4a16_gemm(_ptr(x), M, K, N, _ptr(vals), _ptr(meta), _ptr(scales), group_size, _ptr(out),
                                      act_code(x.dtype), _stream(stream)), "sparse24_w4a16_gemm")
     return out
+
+
+def quantize_w8(w, q=None, scales=None, stream=None):
+    """ExpertsInt8 load-time quantization on the device: w [..., k] bf16/fp16
+    (the 16-bit checkpoint; leading dims = experts x output columns) ->
+    (q int8 [..., k], scales [...] in w's dtype), one scale per row."""
+    torch = _torch()
+    if w.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("quantize_w8 takes bf16 or fp16 weights, got %s" % w.dtype)
+    w = w.contiguous()
+    k = w.shape[-1]
+    rows = w.numel() // k if k else 0
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    if scales is None:
+        scales = torch.empty(w.shape[:-1], dtype=w.dtype, device=w.device)
+    check(load().wq_quantize_w8(_ptr(w), rows, k, act_code(w.dtype), _ptr(q), _ptr(scales), _stream(stream)),
+          "wq_quantize_w8")
+    return q, scales
 
 
 # ----------------------------------------------------------------------------
