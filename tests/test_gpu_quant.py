@@ -2,7 +2,8 @@
 the oracle: codes and scales bit for bit (the rounding decisions are taken in
 float32 on both sides), on ragged shapes (row counts not a multiple of the 4
 rows per workgroup, k not a multiple of a wave's 512 channels), zero rows and
-a Mixtral-sized expert; then the quantized weights through the packer and the
+a Mixtral-sized expert (rows held in registers up to 16384 weights, longer
+rows in two passes); then the quantized weights through the packer and the
 int8 GEMM against the oracle on the same codes."""
 import numpy as np
 import pytest
@@ -32,7 +33,7 @@ def _run(act, bits):
 
 
 @pytest.mark.parametrize("act", ["bf16", "f16"])
-@pytest.mark.parametrize("shape", [(1, 1, 8), (3, 33, 1000), (2, 48, 4096), (1, 7, 14336)])
+@pytest.mark.parametrize("shape", [(1, 1, 8), (3, 33, 1000), (2, 48, 4096), (1, 7, 14336), (1, 5, 16392)])
 def test_quant_matches_oracle(act, shape):
     need_gpu()
     bits, w = _weights(act, shape, 600 + shape[-1] + shape[1])

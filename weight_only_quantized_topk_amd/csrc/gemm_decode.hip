@@ -353,6 +353,8 @@ void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* s
 // (Y already carries the routed weight; z runs over the K slices of a split
 // DOWN stage), ascending j then z in fp32, one rounding to act
 // ---------------------------------------------------------------------------
+constexpr int COMBINE_MAXT = 16;  // terms loaded together (topk * K slices)
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int M, int topk, int n, int ksplit,
                                                       uint16_t* __restrict__ out) {
@@ -363,8 +365,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int c = (int)(q * 4 % n);
     const size_t slab = (size_t)M * topk * n;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < topk; ++j)
-        for (int z = 0; z < ksplit; ++z) acc += *reinterpret_cast<const f32x4*>(y + z * slab + (m * topk + j) * n + c);
+    const int cnt = topk * ksplit;  // terms, in summation order i = j * ksplit + z
+    if (cnt <= COMBINE_MAXT) {
+        // every load issued before the first add: all terms in flight at once
+        f32x4 v[COMBINE_MAXT];
+        int j = 0, z = 0;
+#pragma unroll
+        for (int i = 0; i < COMBINE_MAXT; ++i) {
+            if (i < cnt) v[i] = *reinterpret_cast<const f32x4*>(y + z * slab + (m * topk + j) * n + c);
+            if (++z == ksplit) z = 0, ++j;
+        }
+#pragma unroll
+        for (int i = 0; i < COMBINE_MAXT; ++i)
+            if (i < cnt) acc += v[i];
+    } else {
+        for (int j = 0; j < topk; ++j)
+            for (int z = 0; z < ksplit; ++z) acc += *reinterpret_cast<const f32x4*>(y + z * slab + (m * topk + j) * n + c);
+    }
     u32x2 st;
     st[0] = (uint32_t)f32_to_act<BF16>(acc[0]) | ((uint32_t)f32_to_act<BF16>(acc[1]) << 16);
     st[1] = (uint32_t)f32_to_act<BF16>(acc[2]) | ((uint32_t)f32_to_act<BF16>(acc[3]) << 16);
