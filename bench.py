@@ -11,8 +11,9 @@ prompt length of the end-to-end latency workload in "[Kernel] W8A16 Int8
 inside FusedMoE" (vLLM PR 7415, latency table).  The other batch sizes of that
 layer's sweep are timed too and reported under "sweep"; the other workloads
 (int4 act-order Mixtral, the 2:4-sparse int4 linear layer, the DeepSeek-V2
-shaped int8 layer) under "rows", with the ExpertsInt8 load-time quantizer on
-Mixtral's w1 (HBM GB/s).
+shaped int8 layer, and the dense int4 linear layer of the 2:4 layer's shape)
+under "rows", with the ExpertsInt8 load-time quantizer on Mixtral's w1 (HBM
+GB/s).
 
 Timing: before every step (warm-up and timed) 1 GiB of scratch memory is
 written, outside the timed span, so the weights come from HBM and not from
@@ -252,10 +253,50 @@ def bench_rows(torch, wq, gen, timer, steps, warmup):
         log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
         rows.append(dict(workload=spec.name, **rounded(r)))
     del dev
+    log("bench: rows: generating and packing the dense int4 layer")
+    ddev = dense_weights(torch, wq, spec)
+    for m in spec.m_sweep:
+        r = measure_dense(torch, wq, gen, timer, spec, ddev, m, steps, warmup)
+        log("bench: rows: dense M=%d %.4f ms/step" % (m, r["ms_per_step"]))
+        rows.append(dict(workload="yi34b-mlp-dense-w4a16", **rounded(r)))
+    del ddev
     rows.append(dict(workload="experts-int8-quantize-mixtral-w1", **rounded(measure_quant(torch, wq, timer, steps,
                                                                                          warmup))))
     log("bench: rows: quantizer %.4f ms" % rows[-1]["ms_per_step"])
     return rows
+
+
+def dense_weights(torch, wq, spec):
+    """Dense int4 weights of the 2:4 layer's shape (N x K, group-128 fp16
+    scales), seeded uniform codes in [-8, 7] and scales in [0.005, 0.02]."""
+    rng = np.random.default_rng([20240807, spec.K, spec.N])
+    q = rng.integers(-8, 8, size=(1, spec.N, spec.K), dtype=np.int8)
+    s = rng.uniform(0.005, 0.02, size=(1, spec.K // 128, spec.N)).astype(np.float16).view(np.uint16)
+    packed, sp, _ = wq.pack_w4(q, s, 128)
+    return torch.from_numpy(packed).cuda(), torch.from_numpy(sp.view(np.int16)).cuda()
+
+
+def measure_dense(torch, wq, gen, timer, spec, dev, m, steps, warmup):
+    """The dense int4 linear layer of the same shape as the 2:4 one (the pages
+    set Marlin-24 beside dense Marlin): bytes = packed weights + scales + x + y."""
+    wd, sd = dev
+    x = torch.from_numpy(gen.make_sparse_x(spec, m).view(np.int16)).cuda().view(torch.float16)
+    y = torch.empty((m, spec.N), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(1, wq.dense_gemm_workspace_bytes(m, spec.K, spec.N)), dtype=torch.uint8, device="cuda")
+
+    def step(marks):
+        wq.dense_w4a16_gemm(x, spec.N, wd, sd, 128, out=y, workspace=ws)
+        if marks:
+            marks[0].record()
+
+    spans, wall = timer.run(step, steps, warmup, 1)
+    ms = float(spans[:, 0].mean())
+    nbytes = wd.numel() + sd.numel() * 2 + m * spec.K * 2 + m * spec.N * 2
+    flops = 2 * m * spec.N * spec.K
+    r = dict(M=m, ms_per_step=ms, ms_per_step_median=float(np.median(spans[:, 0])), wall_ms_per_step=wall,
+             tokens_per_s=m / (ms * 1e-3), alg_bytes=int(nbytes), alg_flops=int(flops))
+    r.update(rates(nbytes, flops, ms))
+    return r
 
 
 def measure_quant(torch, wq, timer, steps, warmup):

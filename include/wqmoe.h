@@ -208,6 +208,36 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
                               const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Dense single-expert W4A16 / W8A16 linear layer                            */
+/* ------------------------------------------------------------------------ */
+/*
+ * y[m, n] = sum_k x[m, k] W[n, k] for one weight matrix W [N, K] (the dense
+ * GPTQ-Marlin case the MoE kernel was derived from -- "Marlin moe
+ * integration", nm-vllm PR 266, review thread: the MoE file compared against
+ * csrc/quantization/gptq_marlin/gptq_marlin.cu -- and the GEMV/GEMM mix picked
+ * by batch-size heuristics of "[WIP] AWQ Faster Kernels", vLLM issue 3289).
+ * It runs the grouped GEMM of this library with one expert and top-1: up to
+ * 24 rows the small-batch (GEMV-like) kernel, up to 96 the large-batch kernel
+ * with 64-row tiles, above that 128-row tiles; fp32 accumulation, rounded once
+ * to the activation type.
+ *   d_x [M, K] act dtype; d_y [M, N] act dtype
+ *   d_w_packed, d_scales: wq_pack_w4 / wq_pack_w8 output for E = 1, n_out = N,
+ *     k_in = K (no gate/up interleave); int4 group_size 128 or -1, int8 -1
+ *   d_k_perm: int4 act-order permutation from wq_pack_w4 ([1, K]) or NULL
+ *   d_workspace: dense_gemm_workspace_bytes(M, K, N, act_order) bytes, 256-byte
+ *     aligned (the routing arrays, the act-order gather, fp32 partial sums)
+ * Limits: int4 K % 128 == 0 and fp16 activations; int8 K % 64 == 0; N % 16 ==
+ * 0.  Asynchronous on `stream`; calls sharing a workspace must be
+ * stream-ordered.
+ */
+size_t dense_gemm_workspace_bytes(int M, int K, int N, int act_order);
+wq_status dense_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_w_packed, const void* d_scales,
+                           int group_size, const int32_t* d_k_perm, void* d_y, int act_dtype, void* d_workspace,
+                           size_t workspace_bytes, void* stream);
+wq_status dense_w8a16_gemm(const void* d_x, int M, int K, int N, const void* d_w_packed, const void* d_scales,
+                           void* d_y, int act_dtype, void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* ExpertsInt8 quantization at load time                                     */
 /* ------------------------------------------------------------------------ */
 /*

@@ -109,6 +109,31 @@ def test_quantize_w8_validation():
     assert _status("wq_quantize_w8", *args(rows=0))[0] == wq.WQ_OK
 
 
+def test_dense_validation_and_workspace():
+    """The dense linear rejects bad sizes, formats and short workspaces before
+    any device work; its workspace holds the routing arrays and, for a split
+    long K, the fp32 slabs."""
+    L = wq.load()
+    p = C.c_void_p(FAKE)
+    ws = L.dense_gemm_workspace_bytes(1, 4096, 4096, 0)
+    assert ws >= 4096 * 4                                    # at least the fp32 result row
+    assert L.dense_gemm_workspace_bytes(300, 4096, 256, 0) >= 4 * 300 * 256 * 4   # K split in 4
+    assert L.dense_gemm_workspace_bytes(300, 4096, 256, 1) > L.dense_gemm_workspace_bytes(300, 4096, 256, 0)
+    assert L.dense_gemm_workspace_bytes(0, 4096, 256, 0) == 0
+    a4 = lambda **k: [k.get("x", p), k.get("M", 4), k.get("K", 512), k.get("N", 256), p, p, k.get("gs", 128), None,
+                      k.get("y", p), k.get("dt", wq.WQ_F16), p, k.get("ws", 1 << 30), None]
+    assert _status("dense_w4a16_gemm", *a4(K=500))[0] == wq.WQ_ERR_UNSUPPORTED      # K % 128
+    assert _status("dense_w4a16_gemm", *a4(N=200))[0] == wq.WQ_ERR_UNSUPPORTED      # N % 16
+    assert _status("dense_w4a16_gemm", *a4(gs=64))[0] == wq.WQ_ERR_UNSUPPORTED
+    assert _status("dense_w4a16_gemm", *a4(dt=wq.WQ_BF16))[0] == wq.WQ_ERR_UNSUPPORTED
+    assert _status("dense_w4a16_gemm", *a4(ws=16))[0] == wq.WQ_ERR_INVALID         # workspace too small
+    assert _status("dense_w4a16_gemm", *a4(M=-1))[0] == wq.WQ_ERR_INVALID
+    assert _status("dense_w4a16_gemm", *a4(x=None))[0] == wq.WQ_ERR_INVALID
+    assert _status("dense_w4a16_gemm", *a4(M=0, ws=0))[0] == wq.WQ_OK
+    a8 = lambda **k: [p, 4, k.get("K", 512), 256, p, p, p, wq.WQ_BF16, p, 1 << 30, None]
+    assert _status("dense_w8a16_gemm", *a8(K=96))[0] == wq.WQ_ERR_UNSUPPORTED       # K % 64
+
+
 def _desc(**kw):
     d = _lib.WqMoeGemmDesc()
     d.struct_size = C.sizeof(_lib.WqMoeGemmDesc)

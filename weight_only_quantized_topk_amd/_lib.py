@@ -19,6 +19,7 @@ EXPORTS = (
     "moe_route", "moe_align_capacity", "moe_align", "moe_route_align",
     "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
     "sparse24_w4a16_gemm", "wq_quantize_w8",
+    "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "wq_pack_w4_bytes", "wq_pack_w8_bytes", "wq_pack_w4", "wq_pack_w8",
     "wq_pack_sparse24_vals_bytes", "wq_pack_sparse24_meta_bytes", "wq_pack_sparse24",
 )
@@ -81,6 +82,10 @@ def load():
     L.moe_w8a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.sparse24_w4a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
     L.wq_quantize_w8.argtypes = [p, C.c_int64, i, i, p, p, p]
+    L.dense_gemm_workspace_bytes.argtypes = [i, i, i, i]
+    L.dense_gemm_workspace_bytes.restype = sz
+    L.dense_w4a16_gemm.argtypes = [p, i, i, i, p, p, i, p, p, i, p, sz, p]
+    L.dense_w8a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, sz, p]
     L.wq_pack_w4_bytes.argtypes = [i, i, i]
     L.wq_pack_w4_bytes.restype = sz
     L.wq_pack_w8_bytes.argtypes = [i, i, i]
@@ -93,7 +98,7 @@ def load():
     L.wq_pack_sparse24_meta_bytes.restype = sz
     L.wq_pack_sparse24.argtypes = [i, i, p, p, p, p, p, p]
     for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm",
-              "wq_quantize_w8", "wq_pack_w4",
+              "wq_quantize_w8", "dense_w4a16_gemm", "dense_w8a16_gemm", "wq_pack_w4",
               "wq_pack_w8", "wq_pack_sparse24"):
         getattr(L, f).restype = i
     _lib = L

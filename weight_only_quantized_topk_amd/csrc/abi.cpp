@@ -392,6 +392,150 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
 }
 
 // ---------------------------------------------------------------------------
+// Dense single-expert linear: the grouped kernels with E = 1 and top-1 on
+// identity routing written into the workspace, the DOWN stage with unit routed
+// weights (rows gathered by token, not by sorted position: x has M rows), the
+// combine rounding the fp32 result to the activation type.
+// ---------------------------------------------------------------------------
+namespace {
+struct DenseLayout {
+    int bs, ks;
+    size_t cap, off_sorted, off_eids, off_ntpp, off_w, off_a1, off_y, total;
+};
+
+// batch-size dispatch: the small-batch kernel (blocks of 16 rows) up to 24
+// rows, the large-batch kernel with 64-row tiles up to 96, 128-row tiles above
+int dense_block_size(int M, int N, int K) {
+    const int bs = M <= 24 ? 16 : (M <= 96 ? 64 : 128);
+    return (bs == 16 || wq::prefill_supported(N, K, bs)) ? bs : 16;
+}
+
+DenseLayout dense_layout(int M, int K, int N, bool act_order) {
+    DenseLayout L{};
+    L.bs = dense_block_size(M, N, K);
+    L.cap = moe_align_capacity(M, 1, 1, L.bs);
+    L.ks = (L.bs == 16) ? 1 : wq::prefill_down_split(M, 1, N, K, L.bs);
+    size_t o = 0;
+    L.off_sorted = o;
+    o += round256(L.cap * 4);
+    L.off_eids = o;
+    o += round256(L.cap / L.bs * 4);
+    L.off_ntpp = o;
+    o += 256;
+    L.off_w = o;
+    o += round256((size_t)M * 4);
+    L.off_a1 = o;
+    if (act_order) o += round256(L.cap * (size_t)K * 2);
+    L.off_y = o;
+    o += round256((size_t)L.ks * M * N * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+wq_status dense_gemm(int wbits, const void* d_x, int M, int K, int N, const void* d_w, const void* d_scales,
+                     int group_size, const int32_t* d_k_perm, void* d_y, int act_dtype, void* d_ws, size_t ws_bytes,
+                     void* stream, const char* who) {
+    WQ_REQUIRE(M >= 0 && K > 0 && N > 0, WQ_ERR_INVALID, "%s: bad sizes M %d K %d N %d", who, M, K, N);
+    WQ_REQUIRE(M <= MAX_PAIRS, WQ_ERR_UNSUPPORTED, "%s: M > 2^24", who);
+    WQ_REQUIRE(act_dtype == WQ_F16 || act_dtype == WQ_BF16, WQ_ERR_INVALID, "%s: bad act dtype", who);
+    if (wbits == 4) WQ_REQUIRE(act_dtype == WQ_F16, WQ_ERR_UNSUPPORTED, "%s: int4 path takes fp16 activations", who);
+    const int kchunk = wbits == 4 ? wq::WFmt<4>::KCHUNK : wq::WFmt<8>::KCHUNK;
+    WQ_REQUIRE(K % kchunk == 0, WQ_ERR_UNSUPPORTED, "%s: K %d not a multiple of %d", who, K, kchunk);
+    WQ_REQUIRE(N % 16 == 0, WQ_ERR_UNSUPPORTED, "%s: N %d not a multiple of 16", who, N);
+    if (wbits == 4)
+        WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "%s: group_size %d", who, group_size);
+    const bool act_order = d_k_perm != nullptr;
+    const size_t need = dense_gemm_workspace_bytes(M, K, N, act_order);
+    WQ_REQUIRE(ws_bytes >= need, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who, ws_bytes, need);
+    if (M == 0) return ok();
+    WQ_TRY(check_ptr(d_x, "x"));
+    WQ_TRY(check_ptr(d_w, "w_packed"));
+    WQ_TRY(check_ptr(d_scales, "scales"));
+    WQ_TRY(check_ptr(d_y, "y"));
+    WQ_TRY(check_ptr(d_ws, "workspace"));
+    WQ_TRY(check_dev(d_x, "x"));
+    WQ_TRY(check_dev(d_w, "w_packed"));
+    WQ_TRY(check_dev(d_scales, "scales"));
+    WQ_TRY(check_dev(d_y, "y"));
+    WQ_TRY(check_dev(d_ws, "workspace"));
+    if (act_order) WQ_TRY(check_dev(d_k_perm, "k_perm"));
+    WQ_REQUIRE(reinterpret_cast<uintptr_t>(d_ws) % 256 == 0, WQ_ERR_INVALID, "%s: workspace not 256-byte aligned",
+               who);
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = act_dtype == WQ_BF16;
+    const DenseLayout L = dense_layout(M, K, N, act_order);
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
+    int32_t* eids = reinterpret_cast<int32_t*>(ws + L.off_eids);
+    int32_t* ntpp = reinterpret_cast<int32_t*>(ws + L.off_ntpp);
+    float* tw = reinterpret_cast<float*>(ws + L.off_w);
+    float* y = reinterpret_cast<float*>(ws + L.off_y);
+    wq::launch_identity_route(M, (int)L.cap, L.bs, sorted, eids, ntpp, tw, s);
+    WQ_TRY(after_launch(who));
+
+    wq::GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(d_x);
+    g.w = static_cast<const uint8_t*>(d_w);
+    g.s = static_cast<const uint16_t*>(d_scales);
+    g.sorted = sorted;
+    g.expert_ids = eids;
+    g.ntpp = ntpp;
+    g.topk_w = tw;
+    g.out = y;
+    g.M = M;
+    g.topk = 1;
+    g.E = 1;
+    g.n_out = N;
+    g.k_in = K;
+    g.block_size = L.bs;
+    g.groups = (wbits == 4 && group_size == 128) ? K / 128 : 1;
+    g.a_direct = 0;  // x row = token of the pair (x has M rows, no pad rows)
+    g.cap = (int)L.cap;
+    if (act_order) {
+        uint16_t* a1 = reinterpret_cast<uint16_t*>(ws + L.off_a1);
+        wq::launch_gather_perm(g.a, d_k_perm, sorted, eids, ntpp, M, 1, K, L.bs, g.cap, a1, s);
+        WQ_TRY(after_launch(who));
+        g.a = a1;
+        g.a_direct = 1;
+    }
+    int ks = 1;
+    if (L.bs != 16) ks = wq::launch_gemm_prefill(wbits, bf16, wq::STAGE_DOWN, g, s);
+    else wq::launch_gemm_decode(wbits, bf16, wq::STAGE_DOWN, g, s);
+    WQ_TRY(after_launch(who));
+    wq::launch_combine(y, M, 1, N, ks, bf16, static_cast<uint16_t*>(d_y), s);
+    return after_launch(who);
+}
+}  // namespace
+
+size_t dense_gemm_workspace_bytes(int M, int K, int N, int act_order) {
+    if (M < 0 || K <= 0 || N <= 0 || M > MAX_PAIRS) return 0;
+    if (M == 0) return 0;
+    return dense_layout(M, K, N, act_order != 0).total;
+}
+
+wq_status dense_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_w_packed, const void* d_scales,
+                           int group_size, const int32_t* d_k_perm, void* d_y, int act_dtype, void* d_workspace,
+                           size_t workspace_bytes, void* stream) {
+    try {
+        return dense_gemm(4, d_x, M, K, N, d_w_packed, d_scales, group_size, d_k_perm, d_y, act_dtype, d_workspace,
+                          workspace_bytes, stream, "dense_w4a16_gemm");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "dense_w4a16_gemm: unexpected exception");
+    }
+}
+
+wq_status dense_w8a16_gemm(const void* d_x, int M, int K, int N, const void* d_w_packed, const void* d_scales,
+                           void* d_y, int act_dtype, void* d_workspace, size_t workspace_bytes, void* stream) {
+    try {
+        return dense_gemm(8, d_x, M, K, N, d_w_packed, d_scales, -1, nullptr, d_y, act_dtype, d_workspace,
+                          workspace_bytes, stream, "dense_w8a16_gemm");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "dense_w8a16_gemm: unexpected exception");
+    }
+}
+
+// ---------------------------------------------------------------------------
 wq_status wq_quantize_w8(const void* d_w, int64_t rows, int k, int dtype, int8_t* d_q, uint16_t* d_scales,
                          void* stream) {
     try {

@@ -60,6 +60,11 @@ int prefill_down_split_max(int T, int E, int n_out, int k_in);
 // returns the number of K slices (Y slabs) it wrote
 int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
 
+// the routing arrays of a dense layer (E = 1, top-1): sorted = 0..M-1 then pad
+// ids M up to cap, expert 0 per block, ntpp = M rounded up to BS, weights 1
+void launch_identity_route(int M, int cap, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, float* w,
+                           hipStream_t s);
+
 // act-order: A1[p, k'] = x[token(p), perm[expert(p), k']] for sorted rows p
 void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* sorted, const int32_t* expert_ids,
                         const int32_t* ntpp, int M, int topk, int k_in, int block_size, int cap, uint16_t* a1,

@@ -23,6 +23,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace wq {
 
 constexpr int ROUTE_MAX_PER_LANE = 16;  // E <= 1024
@@ -242,6 +244,28 @@ void launch_align(const int32_t* ids, int T, int E, int BS, int32_t* sorted, int
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(ALIGN_THREADS), lds, s, ids, T, E, BS, id_bits(E), sorted,
                        expert_ids, ntpp, cap);
+}
+
+// ---------------------------------------------------------------------------
+// Routing of a dense layer (one expert, top-1): what moe_align produces for
+// topk_ids = 0 -- the rows in order, pads (id M) up to the capacity, expert 0
+// for every block, M rounded up to the block size -- and unit routed weights.
+__global__ __launch_bounds__(256) void identity_route_kernel(int M, int cap, int BS, int32_t* __restrict__ sorted,
+                                                             int32_t* __restrict__ expert_ids,
+                                                             int32_t* __restrict__ ntpp, float* __restrict__ w) {
+    const int stride = (int)(gridDim.x * blockDim.x);
+    for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < cap; i += stride) {
+        sorted[i] = i < M ? i : M;
+        if (i < M) w[i] = 1.0f;
+        if (i % BS == 0) expert_ids[i / BS] = 0;
+        if (i == 0) *ntpp = (M + BS - 1) / BS * BS;
+    }
+}
+
+void launch_identity_route(int M, int cap, int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, float* w,
+                           hipStream_t s) {
+    const int blocks = std::max(1, std::min(1024, (cap + 255) / 256));
+    hipLaunchKernelGGL(identity_route_kernel, dim3(blocks), dim3(256), 0, s, M, cap, BS, sorted, expert_ids, ntpp, w);
 }
 
 bool route_align_fused(int M, int topk) { return M <= ROUTE_ALIGN_MAX_M && M * topk <= ROUTE_ALIGN_MAX_T; }

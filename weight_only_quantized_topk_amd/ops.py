@@ -18,7 +18,8 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
 
 __all__ = [
     "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
-    "sparse24_w4a16_gemm", "quantize_w8", "pack_w4", "pack_w8", "pack_sparse24", "act_code",
+    "sparse24_w4a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
+    "pack_w4", "pack_w8", "pack_sparse24", "act_code",
 ]
 
 
@@ -156,6 +157,37 @@ def sparse24_w4a16_gemm(x, vals, meta, scales, N: int, out=None, group_size: int
     check(load().sparse24_w4a16_gemm(_ptr(x), M, K, N, _ptr(vals), _ptr(meta), _ptr(scales), group_size, _ptr(out),
                                      act_code(x.dtype), _stream(stream)), "sparse24_w4a16_gemm")
     return out
+
+
+def dense_gemm_workspace_bytes(M: int, K: int, N: int, act_order: bool = False) -> int:
+    return int(load().dense_gemm_workspace_bytes(M, K, N, int(bool(act_order))))
+
+
+def _dense(fn, x, N, w_packed, scales, extra, out, workspace, stream, act_order):
+    torch = _torch()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        nb = dense_gemm_workspace_bytes(M, K, N, act_order)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
+    check(fn(_ptr(x), M, K, N, _ptr(w_packed), _ptr(scales), *extra, _ptr(out), act_code(x.dtype), _ptr(workspace),
+             workspace.numel(), _stream(stream)), fn.__name__)
+    return out
+
+
+def dense_w4a16_gemm(x, N: int, w_packed, scales, group_size: int = 128, k_perm=None, out=None, workspace=None,
+                     stream=None):
+    """Dense int4 linear: x [M, K] fp16 (device) -> y [M, N] fp16, weights
+    packed by pack_w4 with E = 1."""
+    return _dense(load().dense_w4a16_gemm, x, N, w_packed, scales, (group_size, _ptr(k_perm)), out, workspace,
+                  stream, k_perm is not None)
+
+
+def dense_w8a16_gemm(x, N: int, w_packed, scales, out=None, workspace=None, stream=None):
+    """Dense int8 linear: x [M, K] bf16/fp16 (device) -> y [M, N], weights
+    packed by pack_w8 with E = 1."""
+    return _dense(load().dense_w8a16_gemm, x, N, w_packed, scales, (), out, workspace, stream, False)
 
 
 def quantize_w8(w, q=None, scales=None, stream=None):
