@@ -11,6 +11,9 @@
  *   moe_w4a16_gemm        grouped GEMM, int4 GPTQ-style weights, fp16 activations
  *   moe_w8a16_gemm        grouped GEMM, int8 per-column weights, bf16/fp16 activations
  *   sparse24_w4a16_gemm   2:4-sparse int4 dense linear layer, fp16 activations
+ * Beside them: dense_w4a16_gemm / dense_w8a16_gemm (one quantized weight
+ * matrix, the same kernels with one expert) and wq_quantize_w8 (the int8
+ * weights and scales from a 16-bit checkpoint on the device, at load time).
  * Off the hot path (host memory in and out): the packers that turn canonical
  * quantized tensors into the device layout these kernels read.
  *
@@ -198,11 +201,12 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
 /*
  * y[m, n] = sum_k x[m, k] W[n, k] with W [N, K] keeping 2 of every 4
  * consecutive input channels, int4 codes in [-8, 7] and one fp16 scale per
- * group of 128 input channels ("Add GPTQ Marlin 2:4 sparse structured
- * support", vLLM PR 4790, opening description: group size 128, 4-bit).
+ * group of 128 input channels, or per output column with group_size = -1
+ * ("Add GPTQ Marlin 2:4 sparse structured support", vLLM PR 4790, opening
+ * description: group size 128 or -1 (channel-wise), 4-bit).
  *   d_x [M, K] fp16, d_y [M, N] fp16 (fp32 accumulation, rounded once)
- *   d_vals, d_meta, d_scales: from wq_pack_sparse24
- * Limits: K % 256 == 0, N % 16 == 0, group_size == 128, act_dtype == WQ_F16.
+ *   d_vals, d_meta, d_scales: from wq_pack_sparse24 with the same group_size
+ * Limits: K % 256 == 0, N % 16 == 0, group_size 128 or -1, act_dtype == WQ_F16.
  */
 wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
                               const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream);
@@ -301,13 +305,14 @@ wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t
  * 2:4 sparse canonical input: vals int8 [N, K/2] (kept codes in [-8, 7], two
  * per group of 4 along K, ascending position), idx uint8 [N, K/2] (their
  * positions 0..3 inside the group, strictly ascending per pair), scales uint16
- * [K/128, N].  Outputs: vals_packed (wq_pack_sparse24_vals_bytes),
- * meta_packed (wq_pack_sparse24_meta_bytes), scales_packed uint16 [K/128, N].
+ * [G, N] with G = K/128 (group_size 128) or 1 (group_size -1).  Outputs:
+ * vals_packed (wq_pack_sparse24_vals_bytes), meta_packed
+ * (wq_pack_sparse24_meta_bytes), scales_packed uint16 [G, N].
  */
 size_t wq_pack_sparse24_vals_bytes(int N, int K);
 size_t wq_pack_sparse24_meta_bytes(int N, int K);
-wq_status wq_pack_sparse24(int N, int K, const int8_t* vals, const uint8_t* idx, const uint16_t* scales,
-                           void* vals_packed, void* meta_packed, uint16_t* scales_packed);
+wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, const uint8_t* idx,
+                           const uint16_t* scales, void* vals_packed, void* meta_packed, uint16_t* scales_packed);
 
 #ifdef __cplusplus
 }

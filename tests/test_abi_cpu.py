@@ -192,6 +192,7 @@ def test_sparse_validation():
     p = C.c_void_p(FAKE)
     L = wq.load()
     assert L.sparse24_w4a16_gemm(p, 4, 7168, 20480, p, p, p, 64, p, wq.WQ_F16, None) == wq.WQ_ERR_UNSUPPORTED
+    assert L.sparse24_w4a16_gemm(p, 0, 7168, 20480, p, p, p, -1, p, wq.WQ_F16, None) == wq.WQ_OK   # channel-wise
     assert L.sparse24_w4a16_gemm(p, 4, 7000, 20480, p, p, p, 128, p, wq.WQ_F16, None) == wq.WQ_ERR_UNSUPPORTED
     assert L.sparse24_w4a16_gemm(p, 4, 7168, 20480, p, p, p, 128, p, wq.WQ_BF16, None) == wq.WQ_ERR_UNSUPPORTED
     assert L.sparse24_w4a16_gemm(None, 4, 7168, 20480, p, p, p, 128, p, wq.WQ_F16, None) == wq.WQ_ERR_INVALID
@@ -244,6 +245,23 @@ def test_pack_sparse24_layout():
     assert np.array_equal(v, sw.vals) and np.array_equal(i, sw.idx)
     assert np.array_equal(sp, sw.s)
     assert vp.nbytes == spec.N * spec.K // 4 and mp.nbytes == spec.N * spec.K // 8
+
+
+def test_pack_sparse24_per_column():
+    """group_size -1: one scale row [1, N], copied as is; the values and
+    metadata layout does not depend on the group size; other group sizes and
+    wrongly shaped scales are rejected."""
+    spec = gen.CFG4.with_(K=512, N=32, group_size=-1)
+    sw = gen.make_sparse_weights(spec, seed_config=406)
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, -1)
+    assert sp.shape == (1, spec.N) and np.array_equal(sp, sw.s)
+    vp2, mp2, _ = wq.pack_sparse24(sw.vals, sw.idx, np.ones((spec.K // 128, spec.N), np.uint16), 128)
+    assert np.array_equal(vp, vp2) and np.array_equal(mp, mp2)
+    with pytest.raises(ValueError):
+        wq.pack_sparse24(sw.vals, sw.idx, sw.s, 128)
+    L = wq.load()
+    p = C.c_void_p(FAKE)
+    assert L.wq_pack_sparse24(32, 512, 64, p, p, p, p, p, p) == wq.WQ_ERR_UNSUPPORTED
 
 
 def test_sparse24_metadata_roundtrip_all_patterns():

@@ -13,10 +13,10 @@ from tests.helpers import assert_close_fp
 pytestmark = pytest.mark.gpu
 
 
-def run_sparse(sw, x_bits, N):
-    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s)
+def run_sparse(sw, x_bits, N, group_size=128):
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, group_size)
     y = wq.sparse24_w4a16_gemm(dev_u16(x_bits, "f16"), torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(),
-                               torch.from_numpy(sp.view(np.int16)).cuda(), N)
+                               torch.from_numpy(sp.view(np.int16)).cuda(), N, group_size=group_size)
     torch.cuda.synchronize()
     return host_f32(y)
 
@@ -107,6 +107,22 @@ def test_sparse_decode_too_long_for_lds():
     y = run_sparse(sw, x, spec.N)
     ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128)
     assert_close_fp(y, ref, "sparse K=16384 M=4")
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 100, 200])
+def test_sparse_per_column_scales(M):
+    """group_size -1 (one scale per output column, the pages' channel-wise
+    variant) through each batch-size kernel: decode (M <= 4), streaming,
+    256 x 64 tiles."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=2304, N=512, group_size=-1)
+    sw = gen.make_sparse_weights(spec, seed_config=319)
+    assert sw.s.shape == (1, spec.N)
+    x = gen.make_sparse_x(spec, M, seed_config=319)
+    say("sparse per-column", M)
+    y = run_sparse(sw, x, spec.N, group_size=-1)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), -1)
+    assert_close_fp(y, ref, "sparse per-column M=%d" % M)
 
 
 def test_sparse_large_batch_narrow_n():

@@ -96,7 +96,7 @@ def load():
     L.wq_pack_sparse24_vals_bytes.restype = sz
     L.wq_pack_sparse24_meta_bytes.argtypes = [i, i]
     L.wq_pack_sparse24_meta_bytes.restype = sz
-    L.wq_pack_sparse24.argtypes = [i, i, p, p, p, p, p, p]
+    L.wq_pack_sparse24.argtypes = [i, i, i, p, p, p, p, p, p]
     for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm",
               "wq_quantize_w8", "dense_w4a16_gemm", "dense_w8a16_gemm", "wq_pack_w4",
               "wq_pack_w8", "wq_pack_sparse24"):

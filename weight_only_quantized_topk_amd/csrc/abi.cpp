@@ -367,7 +367,8 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
     try {
         WQ_REQUIRE(M >= 0 && K > 0 && N > 0, WQ_ERR_INVALID, "sparse24: bad sizes M %d K %d N %d", M, K, N);
         WQ_REQUIRE(act_dtype == WQ_F16, WQ_ERR_UNSUPPORTED, "sparse24: fp16 activations only");
-        WQ_REQUIRE(group_size == 128, WQ_ERR_UNSUPPORTED, "sparse24: group_size %d (128 only)", group_size);
+        WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "sparse24: group_size %d (128 or -1)",
+                   group_size);
         WQ_REQUIRE(K % 256 == 0, WQ_ERR_UNSUPPORTED, "sparse24: K %d not a multiple of 256", K);
         WQ_REQUIRE(N % 16 == 0, WQ_ERR_UNSUPPORTED, "sparse24: N %d not a multiple of 16", N);
         WQ_REQUIRE((M + 15) / 16 <= 65535, WQ_ERR_UNSUPPORTED, "sparse24: M too large");
@@ -383,7 +384,7 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
         WQ_TRY(check_dev(d_scales, "scales"));
         WQ_TRY(check_dev(d_y, "y"));
         wq::launch_sparse24(static_cast<const uint16_t*>(d_x), M, K, N, static_cast<const uint8_t*>(d_vals),
-                            static_cast<const uint8_t*>(d_meta), static_cast<const uint16_t*>(d_scales),
+                            static_cast<const uint8_t*>(d_meta), static_cast<const uint16_t*>(d_scales), group_size,
                             static_cast<uint16_t*>(d_y), (hipStream_t)stream);
         return after_launch("sparse24_w4a16_gemm");
     } catch (...) {
@@ -723,10 +724,12 @@ size_t wq_pack_sparse24_meta_bytes(int N, int K) {
     return (size_t)N * K / 8;
 }
 
-wq_status wq_pack_sparse24(int N, int K, const int8_t* vals, const uint8_t* idx, const uint16_t* scales,
-                           void* vals_packed, void* meta_packed, uint16_t* scales_packed) {
+wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, const uint8_t* idx,
+                           const uint16_t* scales, void* vals_packed, void* meta_packed, uint16_t* scales_packed) {
     try {
         WQ_REQUIRE(N > 0 && K > 0, WQ_ERR_INVALID, "pack_sparse24: bad sizes");
+        WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "pack_sparse24: group_size %d",
+                   group_size);
         WQ_REQUIRE(N % 16 == 0 && K % 256 == 0, WQ_ERR_UNSUPPORTED, "pack_sparse24: need N %% 16 == 0, K %% 256 == 0");
         WQ_REQUIRE(vals && idx && scales && vals_packed && meta_packed && scales_packed, WQ_ERR_INVALID,
                    "pack_sparse24: NULL buffer");
@@ -766,7 +769,7 @@ wq_status wq_pack_sparse24(int N, int K, const int8_t* vals, const uint8_t* idx,
                 }
             }
         });
-        std::memcpy(scales_packed, scales, sizeof(uint16_t) * (size_t)(K / 128) * N);
+        std::memcpy(scales_packed, scales, sizeof(uint16_t) * (size_t)(group_size == -1 ? 1 : K / 128) * N);
         return ok();
     } catch (...) {
         return fail(WQ_ERR_INVALID, "pack_sparse24: unexpected exception");

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
                                                                      int N, const uint8_t* __restrict__ vals,
                                                                      const uint8_t* __restrict__ meta,
                                                                      const uint16_t* __restrict__ scales,
-                                                                     uint16_t* __restrict__ y) {
+                                                                     int sstride, uint16_t* __restrict__ y) {
     constexpr int XP = R == 1 ? 4 : 2;              // token chunks in flight
     constexpr int ROWS = 16 * R;                    // tokens per workgroup
     constexpr int NT = NWV * 64;
@@ -74,8 +74,8 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
     auto wload = [&](int c, int slot) {
         wv[slot] = ldg128_stream(vt + (size_t)c * 1024);
         wm[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
-        ws0[slot] = sn[(size_t)(2 * c) * N];
-        ws1[slot] = sn[(size_t)(2 * c + 1) * N];
+        ws0[slot] = sn[(size_t)(2 * c) * sstride];
+        ws1[slot] = sn[(size_t)(2 * c + 1) * sstride];
     };
     const uint16_t* xcol = x + (tid & 31) * 8;
     const int xrow0 = m0 + (tid >> 5);
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NW * TPW * 64) void sparse24_decode_kernel(const ui
                                                                     int N, const uint8_t* __restrict__ vals,
                                                                     const uint8_t* __restrict__ meta,
                                                                     const uint16_t* __restrict__ scales,
-                                                                    uint16_t* __restrict__ y) {
+                                                                    int sstride, uint16_t* __restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs_dyn[];
     __shared__ f32x4 red[TPW][NW][64];
     const int tid = threadIdx.x;
@@ -196,8 +196,8 @@ __global__ __launch_bounds__(NW * TPW * 64) void sparse24_decode_kernel(const ui
         const int c = min(wave + NW * i, clast);
         wv[slot] = ldg128_stream(vt + (size_t)c * 1024);
         wm[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
-        ws0[slot] = sn[(size_t)(2 * c) * N];
-        ws1[slot] = sn[(size_t)(2 * c + 1) * N];
+        ws0[slot] = sn[(size_t)(2 * c) * sstride];
+        ws1[slot] = sn[(size_t)(2 * c + 1) * sstride];
     };
 #pragma unroll
     for (int p = 0; p < DEPTH; ++p) wload(p, p);
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
                                                                       int N, const uint8_t* __restrict__ vals,
                                                                       const uint8_t* __restrict__ meta,
                                                                       const uint16_t* __restrict__ scales,
-                                                                      uint16_t* __restrict__ y) {
+                                                                      int sstride, uint16_t* __restrict__ y) {
     __shared__ __attribute__((aligned(16))) uint8_t xs[SPT_BM * SPT_ROWB];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -292,8 +292,8 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
             vn[i] = ldg128_stream(vals + pc * 16);
             mdn[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(meta + pc * 8));
             const int n = 16 * (t0 + i) + nrow;
-            scn0[i] = scales[(size_t)(2 * c) * N + n];
-            scn1[i] = scales[(size_t)(2 * c + 1) * N + n];
+            scn0[i] = scales[(size_t)(2 * c) * sstride + n];
+            scn1[i] = scales[(size_t)(2 * c + 1) * sstride + n];
         }
     };
     f32x4 acc[4][4];
@@ -369,39 +369,42 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
 
 template <int R>
 static void launch_stream(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
-                          const uint16_t* scales, uint16_t* y, hipStream_t s) {
+                          const uint16_t* scales, int sstride, uint16_t* y, hipStream_t s) {
     const dim3 grid((N / 16 + 3) / 4, (M + 16 * R - 1) / (16 * R));
-    hipLaunchKernelGGL((sparse24_stream_kernel<R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales, y);
+    hipLaunchKernelGGL((sparse24_stream_kernel<R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales,
+                       sstride, y);
 }
 
 template <int NW, int TPW>
 static void launch_decode(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
-                          const uint16_t* scales, uint16_t* y, hipStream_t s) {
+                          const uint16_t* scales, int sstride, uint16_t* y, hipStream_t s) {
     const size_t lds = sparse24_decode_lds(M, K);
     auto kern = sparse24_decode_kernel<NW, 4, TPW>;
     if (lds + sizeof(f32x4) * 64 * NW * TPW > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
     hipLaunchKernelGGL(kern, dim3((N / 16 + TPW - 1) / TPW), dim3(NW * TPW * 64), lds, s, x, M, K, N, vals, meta,
-                       scales, y);
+                       scales, sstride, y);
 }
 
 // batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480:
 // M = 1, 2: 18 -> 13 us; M = 4: 18.6 -> 17.0 us with the decode kernel
 void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
-                     const uint16_t* scales, uint16_t* y, hipStream_t s) {
+                     const uint16_t* scales, int group_size, uint16_t* y, hipStream_t s) {
+    const int ss = group_size == -1 ? 0 : N;  // scale row stride: per-column scales reread row 0
     if (M <= 4 && sparse24_decode_lds(M, K) <= SP_DECODE_LDS_MAX) {
-        if (M <= 2) launch_decode<2, 2>(x, M, K, N, vals, meta, scales, y, s);
-        else launch_decode<4, 2>(x, M, K, N, vals, meta, scales, y, s);
+        if (M <= 2) launch_decode<2, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
+        else launch_decode<4, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else if (M > 128 && N % SPT_BN == 0) {
         const dim3 grid(N / SPT_BN, (M + SPT_BM - 1) / SPT_BM);
-        hipLaunchKernelGGL(sparse24_tile_kernel<2>, grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta, scales, y);
+        hipLaunchKernelGGL(sparse24_tile_kernel<2>, grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta, scales, ss,
+                           y);
     } else if (M <= 16) {
-        launch_stream<1>(x, M, K, N, vals, meta, scales, y, s);
+        launch_stream<1>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else if (M <= 64) {
-        launch_stream<2>(x, M, K, N, vals, meta, scales, y, s);
+        launch_stream<2>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else {
-        launch_stream<4>(x, M, K, N, vals, meta, scales, y, s);
+        launch_stream<4>(x, M, K, N, vals, meta, scales, ss, y, s);
     }
 }
 

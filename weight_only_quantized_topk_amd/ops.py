@@ -253,8 +253,9 @@ def pack_w8(q: np.ndarray, scales_bits: np.ndarray, row_perm: Optional[np.ndarra
     return packed, sp
 
 
-def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray):
-    """vals int8 [N, K/2], idx uint8 [N, K/2], scales uint16 [K/128, N] -> (vals, meta, scales) packed."""
+def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray, group_size: int = 128):
+    """vals int8 [N, K/2], idx uint8 [N, K/2], scales uint16 [K/128, N] (group
+    128) or [1, N] (group -1) -> (vals, meta, scales) packed."""
     vals = np.ascontiguousarray(vals, dtype=np.int8)
     idx = np.ascontiguousarray(idx, dtype=np.uint8)
     s = np.ascontiguousarray(scales_bits, dtype=np.uint16)
@@ -268,8 +269,11 @@ def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray):
     vp = np.empty(vb, np.uint8)
     mp = np.empty(mb, np.uint8)
     sp = np.empty_like(s)
-    check(L.wq_pack_sparse24(N, K, _np_ptr(vals), _np_ptr(idx), _np_ptr(s), _np_ptr(vp), _np_ptr(mp), _np_ptr(sp)),
-          "wq_pack_sparse24")
+    G = 1 if group_size == -1 else K // 128
+    if s.shape != (G, N):
+        raise ValueError("scales must be [%d, %d] for group_size %d, got %s" % (G, N, group_size, s.shape))
+    check(L.wq_pack_sparse24(N, K, group_size, _np_ptr(vals), _np_ptr(idx), _np_ptr(s), _np_ptr(vp), _np_ptr(mp),
+                             _np_ptr(sp)), "wq_pack_sparse24")
     return vp, mp, sp
 
 
