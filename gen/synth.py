@@ -130,6 +130,7 @@ class SparseSpec:
     scale_lo: float = 0.005
     scale_hi: float = 0.02
     m_sweep: Tuple[int, ...] = field(default_factory=tuple)
+    bits: int = 4                     # kept codes: 4-bit [-8, 7] or 8-bit [-128, 127]
 
     def with_(self, **kw) -> "SparseSpec":
         return replace(self, **kw)
@@ -274,7 +275,8 @@ def make_sparse_weights(spec: SparseSpec, seed_config: Optional[int] = None) -> 
     N, K = spec.N, spec.K
     choice = rng.integers(0, 6, size=(N, K // 4), dtype=np.int8)
     idx = _KEEP_PAIRS[choice].reshape(N, K // 2)
-    vals = rng.integers(-8, 8, size=(N, K // 2), dtype=np.int8)
+    lim = 8 if spec.bits == 4 else 128
+    vals = rng.integers(-lim, lim, size=(N, K // 2), dtype=np.int8)
     G = 1 if spec.group_size == -1 else K // spec.group_size
     s = _draw_scales(rng, (G, N), spec.scale_lo, spec.scale_hi, spec.act)
     return SparseWeights(spec, vals, np.ascontiguousarray(idx), s)

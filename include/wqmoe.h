@@ -11,6 +11,7 @@
  *   moe_w4a16_gemm        grouped GEMM, int4 GPTQ-style weights, fp16 activations
  *   moe_w8a16_gemm        grouped GEMM, int8 per-column weights, bf16/fp16 activations
  *   sparse24_w4a16_gemm   2:4-sparse int4 dense linear layer, fp16 activations
+ *   sparse24_w8a16_gemm   the same with 8-bit kept codes
  * Beside them: dense_w4a16_gemm / dense_w8a16_gemm (one quantized weight
  * matrix, the same kernels with one expert) and wq_quantize_w8 (the int8
  * weights and scales from a 16-bit checkpoint on the device, at load time).
@@ -207,7 +208,11 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
  *   d_x [M, K] fp16, d_y [M, N] fp16 (fp32 accumulation, rounded once)
  *   d_vals, d_meta, d_scales: from wq_pack_sparse24 with the same group_size
  * Limits: K % 256 == 0, N % 16 == 0, group_size 128 or -1, act_dtype == WQ_F16.
+ * sparse24_w8a16_gemm: the same with 8-bit kept codes in [-128, 127] (the
+ * pages' 8-bit variant of the 2:4 support), packed with bits = 8.
  */
+wq_status sparse24_w8a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
+                              const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream);
 wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
                               const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream);
 
@@ -302,16 +307,17 @@ wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t
                      const int32_t* row_perm, int flags, void* packed, uint16_t* scales_packed);
 
 /*
- * 2:4 sparse canonical input: vals int8 [N, K/2] (kept codes in [-8, 7], two
- * per group of 4 along K, ascending position), idx uint8 [N, K/2] (their
- * positions 0..3 inside the group, strictly ascending per pair), scales uint16
- * [G, N] with G = K/128 (group_size 128) or 1 (group_size -1).  Outputs:
- * vals_packed (wq_pack_sparse24_vals_bytes), meta_packed
- * (wq_pack_sparse24_meta_bytes), scales_packed uint16 [G, N].
+ * 2:4 sparse canonical input: vals int8 [N, K/2] (kept codes, in [-8, 7] for
+ * bits = 4, any int8 for bits = 8; two per group of 4 along K, ascending
+ * position), idx uint8 [N, K/2] (their positions 0..3 inside the group,
+ * strictly ascending per pair), scales uint16 [G, N] with G = K/128
+ * (group_size 128) or 1 (group_size -1).  Outputs: vals_packed
+ * (wq_pack_sparse24_vals_bytes: N*K/4 bytes for 4-bit, N*K/2 for 8-bit),
+ * meta_packed (wq_pack_sparse24_meta_bytes), scales_packed uint16 [G, N].
  */
-size_t wq_pack_sparse24_vals_bytes(int N, int K);
+size_t wq_pack_sparse24_vals_bytes(int N, int K, int bits);
 size_t wq_pack_sparse24_meta_bytes(int N, int K);
-wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, const uint8_t* idx,
+wq_status wq_pack_sparse24(int N, int K, int bits, int group_size, const int8_t* vals, const uint8_t* idx,
                            const uint16_t* scales, void* vals_packed, void* meta_packed, uint16_t* scales_packed);
 
 #ifdef __cplusplus

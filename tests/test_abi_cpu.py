@@ -261,7 +261,32 @@ def test_pack_sparse24_per_column():
         wq.pack_sparse24(sw.vals, sw.idx, sw.s, 128)
     L = wq.load()
     p = C.c_void_p(FAKE)
-    assert L.wq_pack_sparse24(32, 512, 64, p, p, p, p, p, p) == wq.WQ_ERR_UNSUPPORTED
+    assert L.wq_pack_sparse24(32, 512, 4, 64, p, p, p, p, p, p) == wq.WQ_ERR_UNSUPPORTED   # group size
+    assert L.wq_pack_sparse24(32, 512, 6, 128, p, p, p, p, p, p) == wq.WQ_ERR_UNSUPPORTED  # bits
+    assert L.wq_pack_sparse24_vals_bytes(32, 512, 8) == 2 * L.wq_pack_sparse24_vals_bytes(32, 512, 4)
+
+
+def test_pack_sparse24_8bit_layout():
+    """8-bit kept codes: lane l of 16-row tile t, chunk c holds 32 bytes, 8 per
+    64-channel step, the step's 8 kept codes of row 16t + l%16 in natural order
+    (two's complement); the metadata equals the 4-bit packing's."""
+    spec = gen.CFG4.with_(K=512, N=32)
+    sw = gen.make_sparse_weights(spec, seed_config=407)
+    rng = np.random.default_rng(407)
+    v8 = rng.integers(-128, 128, size=sw.vals.shape, dtype=np.int8)
+    vp, mp, _ = wq.pack_sparse24(v8, sw.idx, sw.s, 128, bits=8)
+    _, mp4, _ = wq.pack_sparse24(sw.vals, sw.idx, sw.s, 128, bits=4)
+    assert np.array_equal(mp, mp4)
+    assert vp.nbytes == spec.N * spec.K // 2
+    C = spec.K // 256
+    lanes = vp.view(np.int8).reshape(spec.N // 16, C, 64, 4, 8)      # [tile, chunk, lane, step, value]
+    for t in range(spec.N // 16):
+        for c in range(C):
+            for l in range(64):
+                n = 16 * t + (l & 15)
+                for st in range(4):
+                    first = (256 * c + 64 * st + 16 * (l >> 4)) // 2   # first kept index of the lane's 4 groups
+                    assert np.array_equal(lanes[t, c, l, st], v8[n, first:first + 8])
 
 
 def test_sparse24_metadata_roundtrip_all_patterns():

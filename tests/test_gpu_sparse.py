@@ -13,10 +13,11 @@ from tests.helpers import assert_close_fp
 pytestmark = pytest.mark.gpu
 
 
-def run_sparse(sw, x_bits, N, group_size=128):
-    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, group_size)
-    y = wq.sparse24_w4a16_gemm(dev_u16(x_bits, "f16"), torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(),
-                               torch.from_numpy(sp.view(np.int16)).cuda(), N, group_size=group_size)
+def run_sparse(sw, x_bits, N, group_size=128, bits=4):
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, group_size, bits=bits)
+    fn = wq.sparse24_w4a16_gemm if bits == 4 else wq.sparse24_w8a16_gemm
+    y = fn(dev_u16(x_bits, "f16"), torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(),
+           torch.from_numpy(sp.view(np.int16)).cuda(), N, group_size=group_size)
     torch.cuda.synchronize()
     return host_f32(y)
 
@@ -123,6 +124,41 @@ def test_sparse_per_column_scales(M):
     y = run_sparse(sw, x, spec.N, group_size=-1)
     ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), -1)
     assert_close_fp(y, ref, "sparse per-column M=%d" % M)
+
+
+@pytest.mark.parametrize("gs", [128, -1])
+@pytest.mark.parametrize("M", [1, 3, 16, 100, 200])
+def test_sparse_8bit(M, gs):
+    """8-bit kept codes (the pages' 8-bit variant of the 2:4 support), group
+    128 and channel-wise, through each batch-size kernel."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=2304, N=512, bits=8, group_size=gs)
+    sw = gen.make_sparse_weights(spec, seed_config=320)
+    assert sw.vals.min() < -8 and sw.vals.max() > 7
+    x = gen.make_sparse_x(spec, M, seed_config=320)
+    say("sparse 8-bit", M, gs)
+    y = run_sparse(sw, x, spec.N, group_size=gs, bits=8)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), gs)
+    assert_close_fp(y, ref, "sparse 8-bit M=%d gs=%d" % (M, gs))
+
+
+@pytest.mark.parametrize("M", [2, 37])
+def test_sparse_8bit_exact_integer(M):
+    """Exact-integer case for 8-bit codes: unit scales, x in {-1, 0, 1} with
+    one nonzero channel in 16, codes in [-128, 127]: every output is an integer
+    below 2048 in magnitude, held exactly by fp16."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=512, N=96, bits=8)
+    sw = gen.make_sparse_weights(spec, seed_config=321)
+    rng = np.random.default_rng(M)
+    x = rng.integers(-1, 2, size=(M, spec.K)).astype(np.float32) * (rng.random((M, spec.K)) < 1 / 16)
+    ones = np.ones((spec.K // 128, spec.N), np.float32)
+    sw.s = gen.round_to("f16", ones)
+    say("sparse 8-bit exact", M)
+    y = run_sparse(sw, gen.round_to("f16", x), spec.N, bits=8)
+    ref = oracle.sparse24(x, sw.vals, sw.idx, ones, 128)
+    assert np.abs(ref).max() < 2048
+    assert np.array_equal(y.astype(np.float64), ref)
 
 
 def test_sparse_large_batch_narrow_n():

@@ -41,6 +41,24 @@ def test_exact_integer_equals_dense_with_zeros():
     assert ((D.reshape(spec.N, -1, 4) != 0).sum(-1) <= 2).all()
 
 
+def test_exact_integer_8bit_and_per_column():
+    """8-bit kept codes and channel-wise scales (group -1): exact integers vs
+    the int64 matmul of the dense-with-zeros matrix, and per-column scales
+    equal one group spanning all of K."""
+    spec = gen.CFG4.with_(K=512, N=48, bits=8, group_size=-1)
+    sw = gen.make_sparse_weights(spec, seed_config=305)
+    assert sw.vals.min() < -8 and sw.s.shape == (1, spec.N)
+    rng = np.random.default_rng(1)
+    x = rng.integers(-1, 2, size=(4, spec.K)).astype(np.float32)
+    y = oracle.sparse24(x, sw.vals, sw.idx, np.ones((1, spec.N), np.float32), -1)
+    D = dense_codes(sw.vals, sw.idx)
+    assert np.array_equal(y, (x.astype(np.int64) @ D.T).astype(np.float64))
+    s = sw.s_f32()
+    y1 = oracle.sparse24(x, sw.vals, sw.idx, s, -1)
+    y2 = oracle.sparse24(x, sw.vals, sw.idx, np.repeat(s, spec.K // 128, axis=0), 128)
+    assert np.array_equal(y1, y2)
+
+
 def test_float_equals_dense_with_zeros():
     spec = gen.CFG4.with_(K=1024, N=64)
     sw = gen.make_sparse_weights(spec, seed_config=302)

@@ -18,7 +18,7 @@ EXPORTS = (
     "wq_version", "wq_status_string", "wq_last_error",
     "moe_route", "moe_align_capacity", "moe_align", "moe_route_align",
     "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
-    "sparse24_w4a16_gemm", "wq_quantize_w8",
+    "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "wq_quantize_w8",
     "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "wq_pack_w4_bytes", "wq_pack_w8_bytes", "wq_pack_w4", "wq_pack_w8",
     "wq_pack_sparse24_vals_bytes", "wq_pack_sparse24_meta_bytes", "wq_pack_sparse24",
@@ -81,6 +81,7 @@ def load():
     L.moe_w4a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.moe_w8a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.sparse24_w4a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
+    L.sparse24_w8a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
     L.wq_quantize_w8.argtypes = [p, C.c_int64, i, i, p, p, p]
     L.dense_gemm_workspace_bytes.argtypes = [i, i, i, i]
     L.dense_gemm_workspace_bytes.restype = sz
@@ -92,12 +93,13 @@ def load():
     L.wq_pack_w8_bytes.restype = sz
     L.wq_pack_w4.argtypes = [i, i, i, p, p, i, p, p, i, p, p, p]
     L.wq_pack_w8.argtypes = [i, i, i, p, p, p, i, p, p]
-    L.wq_pack_sparse24_vals_bytes.argtypes = [i, i]
+    L.wq_pack_sparse24_vals_bytes.argtypes = [i, i, i]
     L.wq_pack_sparse24_vals_bytes.restype = sz
     L.wq_pack_sparse24_meta_bytes.argtypes = [i, i]
     L.wq_pack_sparse24_meta_bytes.restype = sz
-    L.wq_pack_sparse24.argtypes = [i, i, i, p, p, p, p, p, p]
+    L.wq_pack_sparse24.argtypes = [i, i, i, i, p, p, p, p, p, p]
     for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm",
+              "sparse24_w8a16_gemm",
               "wq_quantize_w8", "dense_w4a16_gemm", "dense_w8a16_gemm", "wq_pack_w4",
               "wq_pack_w8", "wq_pack_sparse24"):
         getattr(L, f).restype = i

@@ -362,33 +362,50 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream) {
     }
 }
 
+static wq_status sparse24_gemm(int bits, const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
+                               const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream,
+                               const char* who) {
+    WQ_REQUIRE(M >= 0 && K > 0 && N > 0, WQ_ERR_INVALID, "%s: bad sizes M %d K %d N %d", who, M, K, N);
+    WQ_REQUIRE(act_dtype == WQ_F16, WQ_ERR_UNSUPPORTED, "%s: fp16 activations only", who);
+    WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "%s: group_size %d (128 or -1)", who,
+               group_size);
+    WQ_REQUIRE(K % 256 == 0, WQ_ERR_UNSUPPORTED, "%s: K %d not a multiple of 256", who, K);
+    WQ_REQUIRE(N % 16 == 0, WQ_ERR_UNSUPPORTED, "%s: N %d not a multiple of 16", who, N);
+    WQ_REQUIRE((M + 15) / 16 <= 65535, WQ_ERR_UNSUPPORTED, "%s: M too large", who);
+    if (M == 0) return ok();
+    WQ_TRY(check_ptr(d_x, "x"));
+    WQ_TRY(check_ptr(d_vals, "vals"));
+    WQ_TRY(check_ptr(d_meta, "meta"));
+    WQ_TRY(check_ptr(d_scales, "scales"));
+    WQ_TRY(check_ptr(d_y, "y"));
+    WQ_TRY(check_dev(d_x, "x"));
+    WQ_TRY(check_dev(d_vals, "vals"));
+    WQ_TRY(check_dev(d_meta, "meta"));
+    WQ_TRY(check_dev(d_scales, "scales"));
+    WQ_TRY(check_dev(d_y, "y"));
+    wq::launch_sparse24(bits, static_cast<const uint16_t*>(d_x), M, K, N, static_cast<const uint8_t*>(d_vals),
+                        static_cast<const uint8_t*>(d_meta), static_cast<const uint16_t*>(d_scales), group_size,
+                        static_cast<uint16_t*>(d_y), (hipStream_t)stream);
+    return after_launch(who);
+}
+
 wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
                               const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream) {
     try {
-        WQ_REQUIRE(M >= 0 && K > 0 && N > 0, WQ_ERR_INVALID, "sparse24: bad sizes M %d K %d N %d", M, K, N);
-        WQ_REQUIRE(act_dtype == WQ_F16, WQ_ERR_UNSUPPORTED, "sparse24: fp16 activations only");
-        WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "sparse24: group_size %d (128 or -1)",
-                   group_size);
-        WQ_REQUIRE(K % 256 == 0, WQ_ERR_UNSUPPORTED, "sparse24: K %d not a multiple of 256", K);
-        WQ_REQUIRE(N % 16 == 0, WQ_ERR_UNSUPPORTED, "sparse24: N %d not a multiple of 16", N);
-        WQ_REQUIRE((M + 15) / 16 <= 65535, WQ_ERR_UNSUPPORTED, "sparse24: M too large");
-        if (M == 0) return ok();
-        WQ_TRY(check_ptr(d_x, "x"));
-        WQ_TRY(check_ptr(d_vals, "vals"));
-        WQ_TRY(check_ptr(d_meta, "meta"));
-        WQ_TRY(check_ptr(d_scales, "scales"));
-        WQ_TRY(check_ptr(d_y, "y"));
-        WQ_TRY(check_dev(d_x, "x"));
-        WQ_TRY(check_dev(d_vals, "vals"));
-        WQ_TRY(check_dev(d_meta, "meta"));
-        WQ_TRY(check_dev(d_scales, "scales"));
-        WQ_TRY(check_dev(d_y, "y"));
-        wq::launch_sparse24(static_cast<const uint16_t*>(d_x), M, K, N, static_cast<const uint8_t*>(d_vals),
-                            static_cast<const uint8_t*>(d_meta), static_cast<const uint16_t*>(d_scales), group_size,
-                            static_cast<uint16_t*>(d_y), (hipStream_t)stream);
-        return after_launch("sparse24_w4a16_gemm");
+        return sparse24_gemm(4, d_x, M, K, N, d_vals, d_meta, d_scales, group_size, d_y, act_dtype, stream,
+                             "sparse24_w4a16_gemm");
     } catch (...) {
-        return fail(WQ_ERR_HIP, "sparse24: unexpected exception");
+        return fail(WQ_ERR_HIP, "sparse24_w4a16_gemm: unexpected exception");
+    }
+}
+
+wq_status sparse24_w8a16_gemm(const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
+                              const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream) {
+    try {
+        return sparse24_gemm(8, d_x, M, K, N, d_vals, d_meta, d_scales, group_size, d_y, act_dtype, stream,
+                             "sparse24_w8a16_gemm");
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "sparse24_w8a16_gemm: unexpected exception");
     }
 }
 
@@ -714,9 +731,9 @@ wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t
     }
 }
 
-size_t wq_pack_sparse24_vals_bytes(int N, int K) {
-    if (N <= 0 || K <= 0 || N % 16 || K % 256) return 0;
-    return (size_t)N * K / 4;
+size_t wq_pack_sparse24_vals_bytes(int N, int K, int bits) {
+    if (N <= 0 || K <= 0 || N % 16 || K % 256 || (bits != 4 && bits != 8)) return 0;
+    return (size_t)N * K / 2 * bits / 8;
 }
 
 size_t wq_pack_sparse24_meta_bytes(int N, int K) {
@@ -724,10 +741,11 @@ size_t wq_pack_sparse24_meta_bytes(int N, int K) {
     return (size_t)N * K / 8;
 }
 
-wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, const uint8_t* idx,
+wq_status wq_pack_sparse24(int N, int K, int bits, int group_size, const int8_t* vals, const uint8_t* idx,
                            const uint16_t* scales, void* vals_packed, void* meta_packed, uint16_t* scales_packed) {
     try {
         WQ_REQUIRE(N > 0 && K > 0, WQ_ERR_INVALID, "pack_sparse24: bad sizes");
+        WQ_REQUIRE(bits == 4 || bits == 8, WQ_ERR_UNSUPPORTED, "pack_sparse24: bits %d (4 or 8)", bits);
         WQ_REQUIRE(group_size == 128 || group_size == -1, WQ_ERR_UNSUPPORTED, "pack_sparse24: group_size %d",
                    group_size);
         WQ_REQUIRE(N % 16 == 0 && K % 256 == 0, WQ_ERR_UNSUPPORTED, "pack_sparse24: need N %% 16 == 0, K %% 256 == 0");
@@ -735,8 +753,8 @@ wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, con
                    "pack_sparse24: NULL buffer");
         const size_t half = (size_t)N * K / 2;
         for (size_t i = 0; i < half; i += 2) {
-            WQ_REQUIRE(vals[i] >= -8 && vals[i] <= 7 && vals[i + 1] >= -8 && vals[i + 1] <= 7, WQ_ERR_INVALID,
-                       "pack_sparse24: code out of [-8, 7]");
+            WQ_REQUIRE(bits == 8 || (vals[i] >= -8 && vals[i] <= 7 && vals[i + 1] >= -8 && vals[i + 1] <= 7),
+                       WQ_ERR_INVALID, "pack_sparse24: code out of [-8, 7]");
             WQ_REQUIRE(idx[i] < idx[i + 1] && idx[i + 1] <= 3, WQ_ERR_INVALID,
                        "pack_sparse24: keep positions must be ascending in 0..3");
         }
@@ -749,7 +767,8 @@ wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, con
                 const int8_t* vr = vals + (size_t)n * (K / 2);
                 const uint8_t* ir = idx + (size_t)n * (K / 2);
                 for (int c = 0; c < C; ++c) {
-                    uint32_t* vd = reinterpret_cast<uint32_t*>(vo + (((size_t)t * C + c) * 64 + l) * 16);
+                    // lane l's values: 16 bytes (4-bit) or 32 bytes (8-bit) per chunk
+                    uint8_t* vd = vo + (((size_t)t * C + c) * 64 + l) * (size_t)(4 * bits);
                     uint16_t* md = reinterpret_cast<uint16_t*>(mo + (((size_t)t * C + c) * 64 + l) * 8);
                     for (int st = 0; st < 4; ++st) {
                         const int g4 = (256 * c + 64 * st + 16 * (l >> 4)) / 4;  // first group of 4 of this lane
@@ -759,11 +778,12 @@ wq_status wq_pack_sparse24(int N, int K, int group_size, const int8_t* vals, con
                             for (int h = 0; h < 2; ++h) {
                                 const int j = 2 * b + h;
                                 const size_t v = (size_t)2 * (g4 + b) + h;
-                                d |= (uint32_t)(vr[v] + 8) << (4 * (j >> 1) + 16 * (j & 1));
+                                if (bits == 4) d |= (uint32_t)(vr[v] + 8) << (4 * (j >> 1) + 16 * (j & 1));
+                                else vd[8 * st + j] = (uint8_t)vr[v];  // two's complement, natural order
                                 m |= (uint32_t)ir[v] << (4 * b + 2 * h);
                             }
                         }
-                        vd[st] = d;
+                        if (bits == 4) std::memcpy(vd + 4 * st, &d, 4);
                         md[st] = (uint16_t)m;
                     }
                 }

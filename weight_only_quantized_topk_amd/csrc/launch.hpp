@@ -73,8 +73,9 @@ void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* s
 // (ascending, fp32), rounded to act; slab z starts at y + z * M*topk*n
 void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf16, uint16_t* out, hipStream_t s);
 
-// group_size 128 (scales [K/128, N]) or -1 (one scale per output column, [1, N])
-void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+// 2:4-sparse linear with 4- or 8-bit kept codes; group_size 128 (scales
+// [K/128, N]) or -1 (one scale per output column, [1, N])
+void launch_sparse24(int bits, const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                      const uint16_t* scales, int group_size, uint16_t* y, hipStream_t s);
 
 // ExpertsInt8 load-time quantizer: rows of k 16-bit weights -> int8 codes and

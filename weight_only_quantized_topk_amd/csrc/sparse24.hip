@@ -34,6 +34,40 @@ constexpr int SP_THREADS = 64 * SP_WAVES;
 constexpr int SP_KCHUNK = 256;  // dense input channels per packed piece
 constexpr int SPT_ROWB_S = SP_KCHUNK * 2;  // LDS bytes of one token row of a chunk
 
+// The kept values of one lane for one 256-channel chunk: 8 per 64-channel
+// step s, as 4-bit offset codes (one dword per step, 16 bytes) or 8-bit two's
+// complement codes in natural order (two dwords per step, 32 bytes).  A chunk
+// of a 16-row tile holds 64 lanes' values, 1 or 2 KiB.
+template <int VBITS>
+struct SpVals {
+    u32x4 v[VBITS / 4];
+};
+template <int VBITS>
+constexpr int sp_lane_bytes() { return 4 * VBITS; }
+template <int VBITS>
+constexpr int sp_chunk_bytes() { return 64 * sp_lane_bytes<VBITS>(); }
+
+template <int VBITS>
+__device__ __forceinline__ SpVals<VBITS> sp_load(const uint8_t* p) {
+    SpVals<VBITS> r;
+#pragma unroll
+    for (int h = 0; h < VBITS / 4; ++h) r.v[h] = ldg128_stream(p + 16 * h);
+    return r;
+}
+
+// the 8 fp16 A-operand values of step s, each q * scale rounded once to fp16
+template <int VBITS, int S>
+__device__ __forceinline__ u32x4 sp_dequant(const SpVals<VBITS>& w, uint32_t sv) {
+    const f16x2 s2 = __builtin_bit_cast(f16x2, sv | (sv << 16));
+    if constexpr (VBITS == 4) {
+        return dequant_w4_f16_scaled(w.v[0][S], s2);
+    } else {
+        const u32x4 d = dequant_w8x8<false>(w.v[S >> 1][2 * (S & 1)], w.v[S >> 1][2 * (S & 1) + 1]);
+        const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3];
+        return u32x4{f16x2_mul(d0, s2), f16x2_mul(d1, s2), f16x2_mul(d2, s2), f16x2_mul(d3, s2)};
+    }
+}
+
 // ------------------------------------------------- streaming (small batches)
 // One workgroup: NWV waves, wave w multiplies 16-row tile NWV*blockIdx.x + w by
 // the 16*R tokens of blockIdx.y; all waves walk the same 256-channel chunks.
@@ -41,7 +75,7 @@ constexpr int SPT_ROWB_S = SP_KCHUNK * 2;  // LDS bytes of one token row of a ch
 // issued XP chunks ahead; each wave keeps the weights of PF chunks of its tile
 // in flight in registers.  Chunk slots are static: the chunk loop is unrolled
 // by PF.
-template <int R, int PF, int NWV>
+template <int VBITS, int R, int PF, int NWV>
 __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                      int N, const uint8_t* __restrict__ vals,
                                                                      const uint8_t* __restrict__ meta,
@@ -64,15 +98,15 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
     const int C = K / SP_KCHUNK;
     const int nrow = lane & 15;
 
-    const uint8_t* vt = vals + (size_t)t * C * 1024 + lane * 16;
+    const uint8_t* vt = vals + (size_t)t * C * sp_chunk_bytes<VBITS>() + lane * sp_lane_bytes<VBITS>();
     const uint8_t* mt = meta + (size_t)t * C * 512 + lane * 8;
     const uint16_t* sn = scales + 16 * t + nrow;
     // the two scale halves stay apart until used, so no wait follows their loads
-    u32x4 wv[SPS_PF];
+    SpVals<VBITS> wv[SPS_PF];
     u32x2 wm[SPS_PF];
     uint32_t ws0[SPS_PF], ws1[SPS_PF];
     auto wload = [&](int c, int slot) {
-        wv[slot] = ldg128_stream(vt + (size_t)c * 1024);
+        wv[slot] = sp_load<VBITS>(vt + (size_t)c * sp_chunk_bytes<VBITS>());
         wm[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
         ws0[slot] = sn[(size_t)(2 * c) * sstride];
         ws1[slot] = sn[(size_t)(2 * c + 1) * sstride];
@@ -98,10 +132,10 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
     for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int slot, int buf) {
         const uint8_t* xb = xs[buf];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        static_for<0, 4>([&](auto S_) {
+            constexpr int s = decltype(S_)::value;
             const uint32_t sv = (s < 2) ? ws0[slot] : ws1[slot];
-            const u32x4 a = dequant_w4_f16_scaled(wv[slot][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+            const u32x4 a = sp_dequant<VBITS, s>(wv[slot], sv);
             const int idx = (int)wm[slot][s >> 1];
             const int plo = 8 * s + (lane >> 4), phi = plo + 4;
 #pragma unroll
@@ -110,10 +144,9 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
                 const u32x4 lo = *reinterpret_cast<const u32x4*>(xb + row * SPT_ROWB_S + ((plo ^ nrow) << 4));
                 const u32x4 hi = *reinterpret_cast<const u32x4*>(xb + row * SPT_ROWB_S + ((phi ^ nrow) << 4));
                 const u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                if (s & 1) acc[r] = smfmac16x16x64<1>(a, b, idx, acc[r]);
-                else acc[r] = smfmac16x16x64<0>(a, b, idx, acc[r]);
+                acc[r] = smfmac16x16x64<s & 1>(a, b, idx, acc[r]);
             }
-        }
+        });
     };
 
     // every load is unconditional (chunk indices clamped to the last chunk, which
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(NWV * 64) void sparse24_stream_kernel(const uint16_
 // shortening the prefetch.  The NW partial sums are added in LDS in wave
 // order.  Loads sit outside branches except in the guarded tail of fewer than
 // DEPTH chunks.
-template <int NW, int DEPTH, int TPW>
+template <int VBITS, int NW, int DEPTH, int TPW>
 __global__ __launch_bounds__(NW * TPW * 64) void sparse24_decode_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                     int N, const uint8_t* __restrict__ vals,
                                                                     const uint8_t* __restrict__ meta,
@@ -186,15 +219,15 @@ __global__ __launch_bounds__(NW * TPW * 64) void sparse24_decode_kernel(const ui
     // weights first, so their loads are in flight during the token staging
     const int nw = wave < C ? (C - 1 - wave) / NW + 1 : 0;
     const int clast = wave < C ? wave + (nw - 1) * NW : C - 1;  // chunk C - 1 for a wave without chunks
-    const uint8_t* vt = vals + (size_t)t * C * 1024 + lane * 16;
+    const uint8_t* vt = vals + (size_t)t * C * sp_chunk_bytes<VBITS>() + lane * sp_lane_bytes<VBITS>();
     const uint8_t* mt = meta + (size_t)t * C * 512 + lane * 8;
     const uint16_t* sn = scales + 16 * t + nrow;
-    u32x4 wv[DEPTH];
+    SpVals<VBITS> wv[DEPTH];
     u32x2 wm[DEPTH];
     uint32_t ws0[DEPTH], ws1[DEPTH];
     auto wload = [&](int i, int slot) {
         const int c = min(wave + NW * i, clast);
-        wv[slot] = ldg128_stream(vt + (size_t)c * 1024);
+        wv[slot] = sp_load<VBITS>(vt + (size_t)c * sp_chunk_bytes<VBITS>());
         wm[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + (size_t)c * 512));
         ws0[slot] = sn[(size_t)(2 * c) * sstride];
         ws1[slot] = sn[(size_t)(2 * c + 1) * sstride];
@@ -214,17 +247,16 @@ __global__ __launch_bounds__(NW * TPW * 64) void sparse24_decode_kernel(const ui
     auto body = [&](int i, auto U) {
         constexpr int u = decltype(U)::value;
         const uint8_t* xc = xl + (size_t)min(wave + NW * i, clast) * (2 * SP_KCHUNK);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        static_for<0, 4>([&](auto S_) {
+            constexpr int s = decltype(S_)::value;
             const uint32_t sv = (s < 2) ? ws0[u] : ws1[u];
-            const u32x4 a = dequant_w4_f16_scaled(wv[u][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+            const u32x4 a = sp_dequant<VBITS, s>(wv[u], sv);
             const int idx = (int)wm[u][s >> 1];
             const u32x4 lo = *reinterpret_cast<const u32x4*>(xc + 128 * s);
             const u32x4 hi = *reinterpret_cast<const u32x4*>(xc + 128 * s + 64);
             const u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            if (s & 1) acc = smfmac16x16x64<1>(a, b, idx, acc);
-            else acc = smfmac16x16x64<0>(a, b, idx, acc);
-        }
+            acc = smfmac16x16x64<s & 1>(a, b, idx, acc);
+        });
         wload(i + DEPTH, u);
     };
     int i0 = 0;
@@ -259,7 +291,7 @@ constexpr int SPT_XPIECES = SPT_BM * (SPT_ROWB / 16) / SP_THREADS;  // 16-byte t
 
 __device__ __forceinline__ int spt_off(int row, int piece) { return row * SPT_ROWB + ((piece ^ (row & 15)) << 4); }
 
-template <int OCC>
+template <int VBITS, int OCC>
 __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                       int N, const uint8_t* __restrict__ vals,
                                                                       const uint8_t* __restrict__ meta,
@@ -279,7 +311,7 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
     const uint16_t* xcol = x + (tid & 31) * 8;
     const int xrow0 = m0 + (tid >> 5);
     u32x4 xv[SPT_XPIECES];
-    u32x4 v[4], vn[4];
+    SpVals<VBITS> v[4], vn[4];
     u32x2 md[4], mdn[4];
     uint32_t sc0[4], sc1[4], scn0[4], scn1[4];  // scales of groups 2c and 2c+1 of this lane's row
     auto gload = [&](int c) {
@@ -289,7 +321,7 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const size_t pc = ((size_t)(t0 + i) * C + c) * 64 + lane;
-            vn[i] = ldg128_stream(vals + pc * 16);
+            vn[i] = sp_load<VBITS>(vals + pc * sp_lane_bytes<VBITS>());
             mdn[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(meta + pc * 8));
             const int n = 16 * (t0 + i) + nrow;
             scn0[i] = scales[(size_t)(2 * c) * sstride + n];
@@ -314,7 +346,7 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t sv = (s < 2) ? sc0[i] : sc1[i];
-            a[i] = dequant_w4_f16_scaled(v[i][s], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+            a[i] = sp_dequant<VBITS, s>(v[i], sv);
             idx[i] = (int)md[i][s >> 1];
         }
         const int plo = 8 * s + (lane >> 4), phi = plo + 4;
@@ -367,19 +399,19 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
     }
 }
 
-template <int R>
+template <int VBITS, int R>
 static void launch_stream(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                           const uint16_t* scales, int sstride, uint16_t* y, hipStream_t s) {
     const dim3 grid((N / 16 + 3) / 4, (M + 16 * R - 1) / (16 * R));
-    hipLaunchKernelGGL((sparse24_stream_kernel<R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales,
+    hipLaunchKernelGGL((sparse24_stream_kernel<VBITS, R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales,
                        sstride, y);
 }
 
-template <int NW, int TPW>
+template <int VBITS, int NW, int TPW>
 static void launch_decode(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                           const uint16_t* scales, int sstride, uint16_t* y, hipStream_t s) {
     const size_t lds = sparse24_decode_lds(M, K);
-    auto kern = sparse24_decode_kernel<NW, 4, TPW>;
+    auto kern = sparse24_decode_kernel<VBITS, NW, 4, TPW>;
     if (lds + sizeof(f32x4) * 64 * NW * TPW > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
@@ -389,23 +421,30 @@ static void launch_decode(const uint16_t* x, int M, int K, int N, const uint8_t*
 
 // batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480:
 // M = 1, 2: 18 -> 13 us; M = 4: 18.6 -> 17.0 us with the decode kernel
-void launch_sparse24(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
-                     const uint16_t* scales, int group_size, uint16_t* y, hipStream_t s) {
-    const int ss = group_size == -1 ? 0 : N;  // scale row stride: per-column scales reread row 0
+template <int VBITS>
+static void launch_sparse24_b(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+                              const uint16_t* scales, int ss, uint16_t* y, hipStream_t s) {
     if (M <= 4 && sparse24_decode_lds(M, K) <= SP_DECODE_LDS_MAX) {
-        if (M <= 2) launch_decode<2, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
-        else launch_decode<4, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
+        if (M <= 2) launch_decode<VBITS, 2, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
+        else launch_decode<VBITS, 4, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else if (M > 128 && N % SPT_BN == 0) {
         const dim3 grid(N / SPT_BN, (M + SPT_BM - 1) / SPT_BM);
-        hipLaunchKernelGGL(sparse24_tile_kernel<2>, grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta, scales, ss,
-                           y);
+        hipLaunchKernelGGL((sparse24_tile_kernel<VBITS, 2>), grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta,
+                           scales, ss, y);
     } else if (M <= 16) {
-        launch_stream<1>(x, M, K, N, vals, meta, scales, ss, y, s);
+        launch_stream<VBITS, 1>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else if (M <= 64) {
-        launch_stream<2>(x, M, K, N, vals, meta, scales, ss, y, s);
+        launch_stream<VBITS, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else {
-        launch_stream<4>(x, M, K, N, vals, meta, scales, ss, y, s);
+        launch_stream<VBITS, 4>(x, M, K, N, vals, meta, scales, ss, y, s);
     }
+}
+
+void launch_sparse24(int bits, const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+                     const uint16_t* scales, int group_size, uint16_t* y, hipStream_t s) {
+    const int ss = group_size == -1 ? 0 : N;  // scale row stride: per-column scales reread row 0
+    if (bits == 8) launch_sparse24_b<8>(x, M, K, N, vals, meta, scales, ss, y, s);
+    else launch_sparse24_b<4>(x, M, K, N, vals, meta, scales, ss, y, s);
 }
 
 }  // namespace wq

@@ -18,7 +18,7 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
 
 __all__ = [
     "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
-    "sparse24_w4a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
+    "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "pack_w4", "pack_w8", "pack_sparse24", "act_code",
 ]
 
@@ -148,15 +148,24 @@ def moe_w8a16_gemm(stage, a, M, topk, E, n_out, k_in, w_packed, scales, sorted_t
                  workspace, stream, act_dtype)
 
 
-def sparse24_w4a16_gemm(x, vals, meta, scales, N: int, out=None, group_size: int = 128, stream=None):
-    """x [M, K] fp16 (device) -> y [M, N] fp16."""
+def _sparse24(fn, x, vals, meta, scales, N, out, group_size, stream):
     torch = _torch()
     M, K = x.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    check(load().sparse24_w4a16_gemm(_ptr(x), M, K, N, _ptr(vals), _ptr(meta), _ptr(scales), group_size, _ptr(out),
-                                     act_code(x.dtype), _stream(stream)), "sparse24_w4a16_gemm")
+    check(fn(_ptr(x), M, K, N, _ptr(vals), _ptr(meta), _ptr(scales), group_size, _ptr(out), act_code(x.dtype),
+             _stream(stream)), fn.__name__)
     return out
+
+
+def sparse24_w4a16_gemm(x, vals, meta, scales, N: int, out=None, group_size: int = 128, stream=None):
+    """x [M, K] fp16 (device) -> y [M, N] fp16, 4-bit kept codes."""
+    return _sparse24(load().sparse24_w4a16_gemm, x, vals, meta, scales, N, out, group_size, stream)
+
+
+def sparse24_w8a16_gemm(x, vals, meta, scales, N: int, out=None, group_size: int = 128, stream=None):
+    """x [M, K] fp16 (device) -> y [M, N] fp16, 8-bit kept codes (packed with bits=8)."""
+    return _sparse24(load().sparse24_w8a16_gemm, x, vals, meta, scales, N, out, group_size, stream)
 
 
 def dense_gemm_workspace_bytes(M: int, K: int, N: int, act_order: bool = False) -> int:
@@ -253,16 +262,17 @@ def pack_w8(q: np.ndarray, scales_bits: np.ndarray, row_perm: Optional[np.ndarra
     return packed, sp
 
 
-def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray, group_size: int = 128):
+def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray, group_size: int = 128, bits: int = 4):
     """vals int8 [N, K/2], idx uint8 [N, K/2], scales uint16 [K/128, N] (group
-    128) or [1, N] (group -1) -> (vals, meta, scales) packed."""
+    128) or [1, N] (group -1) -> (vals, meta, scales) packed for 4- or 8-bit
+    kept codes."""
     vals = np.ascontiguousarray(vals, dtype=np.int8)
     idx = np.ascontiguousarray(idx, dtype=np.uint8)
     s = np.ascontiguousarray(scales_bits, dtype=np.uint16)
     N, Kh = vals.shape
     K = 2 * Kh
     L = load()
-    vb = int(L.wq_pack_sparse24_vals_bytes(N, K))
+    vb = int(L.wq_pack_sparse24_vals_bytes(N, K, bits))
     mb = int(L.wq_pack_sparse24_meta_bytes(N, K))
     if vb == 0 or mb == 0:
         raise ValueError("unsupported 2:4 shape N=%d K=%d" % (N, K))
@@ -272,8 +282,8 @@ def pack_sparse24(vals: np.ndarray, idx: np.ndarray, scales_bits: np.ndarray, gr
     G = 1 if group_size == -1 else K // 128
     if s.shape != (G, N):
         raise ValueError("scales must be [%d, %d] for group_size %d, got %s" % (G, N, group_size, s.shape))
-    check(L.wq_pack_sparse24(N, K, group_size, _np_ptr(vals), _np_ptr(idx), _np_ptr(s), _np_ptr(vp), _np_ptr(mp),
-                             _np_ptr(sp)), "wq_pack_sparse24")
+    check(L.wq_pack_sparse24(N, K, bits, group_size, _np_ptr(vals), _np_ptr(idx), _np_ptr(s), _np_ptr(vp),
+                             _np_ptr(mp), _np_ptr(sp)), "wq_pack_sparse24")
     return vp, mp, sp
 
 
