@@ -11,7 +11,8 @@ prompt length of the end-to-end latency workload in "[Kernel] W8A16 Int8
 inside FusedMoE" (vLLM PR 7415, latency table).  The other batch sizes of that
 layer's sweep are timed too and reported under "sweep"; the other workloads
 (int4 act-order Mixtral, the 2:4-sparse int4 linear layer, the DeepSeek-V2
-shaped int8 layer, and the dense int4 linear layer of the 2:4 layer's shape)
+shaped int8 layer, the 2:4 layer with 8-bit codes, and the dense int4 linear
+layer of the 2:4 layer's shape)
 under "rows", with the ExpertsInt8 load-time quantizer on Mixtral's w1 (HBM
 GB/s).
 
@@ -210,9 +211,10 @@ def measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup):
     vd, md, sd = dev
     x = torch.from_numpy(gen.make_sparse_x(spec, m).view(np.int16)).cuda().view(torch.float16)
     y = torch.empty((m, spec.N), dtype=torch.float16, device="cuda")
+    fn = wq.sparse24_w4a16_gemm if spec.bits == 4 else wq.sparse24_w8a16_gemm
 
     def step(marks):
-        wq.sparse24_w4a16_gemm(x, vd, md, sd, spec.N, out=y)
+        fn(x, vd, md, sd, spec.N, out=y)
         if marks:
             marks[0].record()
 
@@ -252,6 +254,16 @@ def bench_rows(torch, wq, gen, timer, steps, warmup):
         r = measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup)
         log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
         rows.append(dict(workload=spec.name, **rounded(r)))
+    del dev
+    spec8 = spec.with_(bits=8)                 # the 2:4 support's 8-bit variant, same shape
+    log("bench: rows: generating and packing %s (8-bit)" % spec.name)
+    sw = gen.make_sparse_weights(spec8)
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, bits=8)
+    dev = (torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(), torch.from_numpy(sp.view(np.int16)).cuda())
+    for m in spec.m_sweep:
+        r = measure_sparse(torch, wq, gen, timer, spec8, dev, m, steps, warmup)
+        log("bench: rows: %s 8-bit M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
+        rows.append(dict(workload="yi34b-mlp-sparse24-w8a16", **rounded(r)))
     del dev
     log("bench: rows: generating and packing the dense int4 layer")
     ddev = dense_weights(torch, wq, spec)
