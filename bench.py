@@ -52,7 +52,7 @@ FLUSH_BYTES = 1 << 30
 # rocprofv3 counter summary of the large-batch gate/up kernel at the default
 # workload; its traffic figure is used only while the kernel sources hash the same
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill_gate_up_mixtral_w8a16_m1024.md")
-KERNEL_SOURCES = ["gemm_prefill.hip", "common.hpp", "launch.hpp"]
+KERNEL_SOURCES = ("gemm_prefill.hip", "common.hpp")  # plus the kernel-argument part of launch.hpp
 
 
 def log(*a):
@@ -60,10 +60,18 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """sha256 over the large-batch kernel's sources: gemm_prefill.hip,
+    common.hpp, and from launch.hpp the kernel-argument struct and the stage
+    constants (the rest of that header declares other kernels)."""
+    csrc = os.path.join(ROOT, "weight_only_quantized_topk_amd", "csrc")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "weight_only_quantized_topk_amd", "csrc", f), "rb") as fh:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(csrc, "launch.hpp")) as fh:
+        text = fh.read()
+    for part in re.findall(r"constexpr int STAGE_\w+ = \d+;", text) + re.findall(r"struct GemmArgs \{.*?\n\};", text, re.S):
+        h.update(part.encode())
     return h.hexdigest()
 
 
