@@ -26,12 +26,15 @@ W4AO = W4.with_(name="w4ao-small", act_order=True)
 W4PC = W4.with_(name="w4-percol-small", group_size=-1)
 W8 = gen.CFG2.with_(name="w8-small", E=8, topk=2, K=512, N=384)
 W8E = gen.CFG5.with_(name="w8-many-small", E=40, topk=6, K=256, N=256, zipf_s=1.1)
+# 64 or more experts with skewed routing: the small-batch fused stage takes two
+# token blocks per pass
+W8E80 = gen.CFG5.with_(name="w8-many-80", E=80, topk=6, K=256, N=256, zipf_s=1.1)
 # long k_in, narrow output: the large-batch DOWN splits K into 4 slices; their
 # GATE_UP (8192 outputs) takes the 512-row shape
 W4K = W4.with_(name="w4-longk", K=256, N=4096)
 W8K = W8.with_(name="w8-longk", K=256, N=4096)
-SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E, "w4k": W4K, "w8k": W8K}
-SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505, "w4k": 506, "w8k": 507}
+SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E, "w4k": W4K, "w8k": W8K, "w8e80": W8E80}
+SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505, "w4k": 506, "w8k": 507, "w8e80": 508}
 
 
 def _pack(spec, wts):
@@ -176,6 +179,33 @@ def test_down_split_k(key, bs, M):
     spec = SPECS[key]
     ws = _check_down(key, bs, M)
     assert ws >= 4 * M * spec.topk * spec.K * 4
+
+
+@pytest.mark.parametrize("key", ["w4k", "w8k"])
+@pytest.mark.parametrize("M", [1, 5])
+def test_down_decode_long_k(key, M):
+    """k_in = 4096 with 256 outputs over few experts through the small-batch
+    kernel (long reductions: 8 waves per workgroup)."""
+    _check_down(key, 16, M)
+
+
+@pytest.mark.parametrize("M", [5, 37, 90])
+def test_gate_up_many_experts_two_blocks(M):
+    """80 experts, top-6, Zipf-skewed routing, blocks of 16: the small-batch
+    fused stage with two token blocks per pass (and its one-block tail)."""
+    need_gpu()
+    spec, wts, p = setup("w8e80")
+    toks, w, ids = routed(spec, M, seed=780 + M)
+    say("gate_up many experts", M)
+    h, st, ex, nt, cap = run_gate_up(spec, p, dev_u16(toks.x, spec.act), ids, 16)
+    _, h_ref = oracle.moe_up(toks.x_f32(), ids, wts.w1q, wts.s1_f32(), wts.g1)
+    got = host_f32(h)
+    stn, exn, ntn = st.cpu().numpy(), ex.cpu().numpy(), int(nt.cpu()[0])
+    T = M * spec.topk
+    rows = [pos for pos in range(ntn) if stn[pos] < T]
+    assert_close_fp(got[rows], h_ref[stn[rows]], "H many experts M=%d" % M)
+    pads = [pos for pos in range(ntn) if stn[pos] >= T]
+    assert not np.any(got[pads])
 
 
 def test_down_split_wide_grid_w4():

@@ -257,8 +257,9 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH>), grid, dim3(64 * NW), 0, s, g);
 }
 
-// Shapes by batch, measured on MI355X (Mixtral-shaped int8 and int4 layers,
-// and the 160-expert int8 layer with skewed routing).  One token block per
+// Shapes by batch, measured on MI355X with the last-level cache flushed before
+// every launch (Mixtral-shaped int8 and int4 layers, and the 160-expert int8
+// layer with skewed routing).  One token block per
 // pass when experts are thin, two up to ~24 rows per expert, four beyond
 // (larger batches normally take the large-batch kernel).  The waves of a
 // workgroup split the input channels, so their count follows the number of
@@ -266,6 +267,10 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
 // waves with 2 or 4 row tiles, a long one 8 waves; int4 (half the bytes per
 // weight, so half the work per wave) takes two gate/up tile pairs per
 // workgroup, and four row tiles in DOWN once that grid still fills the GPU.
+// The fused stage of a many-expert layer (E >= 64, skewed routing) takes two
+// token blocks per pass whatever the mean rows per expert: its head experts
+// hold several blocks (DeepSeek-V2 shape M = 64: gate/up 157 -> 132 us in the
+// layer).
 template <int WBITS, bool BF16, int STAGE>
 static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
     constexpr bool GU = STAGE == STAGE_GATE_UP;
@@ -278,7 +283,11 @@ static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
     const bool short_k = g.k_in / WFmt<WBITS>::KCHUNK <= 32;
     // workgroups of a 4-tile DOWN grid over the touched experts
     const long wg4 = (long)touched * (g.n_out / (TILE_ROWS * 4));
-    if (T <= 16 || rows <= 8) {
+    if (GU && g.E >= 64 && T > 16 && np2_ok) {
+        // many experts with skewed routing: the head experts hold several token
+        // blocks, which one block per pass would stream their weights for each
+        launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);
+    } else if (T <= 16 || rows <= 8) {
         if (GU && WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 2>(g, s);
         else if (GU) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
         else if (!np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 8, 4>(g, s);
