@@ -1,10 +1,10 @@
 """GPU parity of the dense single-expert W4A16 / W8A16 linear layer
 (dense_w4a16_gemm, dense_w8a16_gemm) against the oracle's projection with one
-expert and top-1: every batch regime of the dispatch (the small-batch kernel up
-to 24 rows, 64-row tiles up to 96, 128-row tiles above, with a K split for a
-long K and few outputs), int8 per-column, int4 group-128, per-column and
-act-order weights.  Relative Frobenius error <= 5e-3 and max abs error <=
-3e-2 * max |ref|."""
+expert and top-1: every batch regime of the dispatch (the single-kernel path
+for 1..4 rows, the grouped small-batch kernel up to 24 rows, 64-row tiles up to
+96, 128-row tiles above, with a K split for a long K and few outputs), int8
+per-column, int4 group-128, per-column and act-order weights.  Relative
+Frobenius error <= 5e-3 and max abs error <= 3e-2 * max |ref|."""
 import numpy as np
 import pytest
 
@@ -42,7 +42,7 @@ def setup(key):
 
 
 @pytest.mark.parametrize("key", ["w8", "w4", "w4ao", "w4pc"])
-@pytest.mark.parametrize("M", [1, 13, 40, 300])
+@pytest.mark.parametrize("M", [1, 2, 4, 13, 40, 300])
 def test_dense_matches_oracle(key, M):
     need_gpu()
     spec, wts, (wd, sd, kd) = setup(key)
@@ -74,6 +74,30 @@ def test_dense_long_k_split():
     torch.cuda.synchronize()
     ref, _ = oracle.moe_up(toks.x_f32(), np.zeros((M, 1), np.int32), wts.w1q, wts.s1_f32(), None, want_gu=True)
     assert_close_fp(host_f32(y), ref, "dense long-k M=%d" % M)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dense_rows_too_long_for_lds(bits):
+    """4 rows of K = 16384: the rows do not fit the single kernel's LDS, so the
+    grouped path runs (with its workspace)."""
+    need_gpu()
+    base = W4 if bits == 4 else W8
+    spec = base.with_(name="dense-longrow-%d" % bits, K=16384, N=64)
+    wts = gen.make_moe_weights(spec, seed_config=680 + bits)
+    if bits == 4:
+        packed, sp, _ = wq.pack_w4(wts.w1q, wts.s1, spec.group_size)
+    else:
+        packed, sp = wq.pack_w8(wts.w1q, wts.s1)
+    wd, sd = torch.from_numpy(packed).cuda(), torch.from_numpy(sp.view(np.int16)).cuda()
+    n_out = wts.w1q.shape[1]
+    M = 4
+    assert wq.dense_gemm_workspace_bytes(M, spec.K, n_out) > 0
+    toks = gen.make_tokens(spec, M, seed_config=681)
+    x = dev_u16(toks.x, spec.act)
+    y = wq.dense_w4a16_gemm(x, n_out, wd, sd, spec.group_size) if bits == 4 else wq.dense_w8a16_gemm(x, n_out, wd, sd)
+    torch.cuda.synchronize()
+    ref, _ = oracle.moe_up(toks.x_f32(), np.zeros((M, 1), np.int32), wts.w1q, wts.s1_f32(), None, want_gu=True)
+    assert_close_fp(host_f32(y), ref, "dense long rows %d-bit" % bits)
 
 
 def test_dense_equals_moe_raw_bits():

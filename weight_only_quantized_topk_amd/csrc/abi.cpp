@@ -410,10 +410,12 @@ wq_status sparse24_w8a16_gemm(const void* d_x, int M, int K, int N, const void* 
 }
 
 // ---------------------------------------------------------------------------
-// Dense single-expert linear: the grouped kernels with E = 1 and top-1 on
-// identity routing written into the workspace, the DOWN stage with unit routed
-// weights (rows gathered by token, not by sorted position: x has M rows), the
-// combine rounding the fp32 result to the activation type.
+// Dense single-expert linear.  1..4 rows (without act-order): one small-batch
+// kernel with the rows staged in LDS, no workspace.  Otherwise the grouped
+// kernels with E = 1 and top-1 on identity routing written into the workspace,
+// the DOWN stage with unit routed weights (rows gathered by token, not by
+// sorted position: x has M rows), the combine rounding the fp32 result to the
+// activation type.
 // ---------------------------------------------------------------------------
 namespace {
 struct DenseLayout {
@@ -470,18 +472,25 @@ wq_status dense_gemm(int wbits, const void* d_x, int M, int K, int N, const void
     WQ_TRY(check_ptr(d_w, "w_packed"));
     WQ_TRY(check_ptr(d_scales, "scales"));
     WQ_TRY(check_ptr(d_y, "y"));
-    WQ_TRY(check_ptr(d_ws, "workspace"));
     WQ_TRY(check_dev(d_x, "x"));
     WQ_TRY(check_dev(d_w, "w_packed"));
     WQ_TRY(check_dev(d_scales, "scales"));
     WQ_TRY(check_dev(d_y, "y"));
-    WQ_TRY(check_dev(d_ws, "workspace"));
     if (act_order) WQ_TRY(check_dev(d_k_perm, "k_perm"));
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = act_dtype == WQ_BF16;
+    const int groups = (wbits == 4 && group_size == 128) ? K / 128 : 1;
+    if (need == 0) {  // 1..4 rows: one kernel, no workspace
+        wq::launch_dense_decode(wbits, bf16, static_cast<const uint16_t*>(d_x), M, K, N,
+                                static_cast<const uint8_t*>(d_w), static_cast<const uint16_t*>(d_scales), groups,
+                                static_cast<uint16_t*>(d_y), s);
+        return after_launch(who);
+    }
+    WQ_TRY(check_ptr(d_ws, "workspace"));
+    WQ_TRY(check_dev(d_ws, "workspace"));
     WQ_REQUIRE(reinterpret_cast<uintptr_t>(d_ws) % 256 == 0, WQ_ERR_INVALID, "%s: workspace not 256-byte aligned",
                who);
 
-    hipStream_t s = (hipStream_t)stream;
-    const bool bf16 = act_dtype == WQ_BF16;
     const DenseLayout L = dense_layout(M, K, N, act_order);
     uint8_t* ws = static_cast<uint8_t*>(d_ws);
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
@@ -507,7 +516,7 @@ wq_status dense_gemm(int wbits, const void* d_x, int M, int K, int N, const void
     g.n_out = N;
     g.k_in = K;
     g.block_size = L.bs;
-    g.groups = (wbits == 4 && group_size == 128) ? K / 128 : 1;
+    g.groups = groups;
     g.a_direct = 0;  // x row = token of the pair (x has M rows, no pad rows)
     g.cap = (int)L.cap;
     if (act_order) {
@@ -529,6 +538,7 @@ wq_status dense_gemm(int wbits, const void* d_x, int M, int K, int N, const void
 size_t dense_gemm_workspace_bytes(int M, int K, int N, int act_order) {
     if (M < 0 || K <= 0 || N <= 0 || M > MAX_PAIRS) return 0;
     if (M == 0) return 0;
+    if (!act_order && wq::dense_decode_supported(M, K)) return 0;  // the single-kernel small-batch path
     return dense_layout(M, K, N, act_order != 0).total;
 }
 

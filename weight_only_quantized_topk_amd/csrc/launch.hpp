@@ -78,6 +78,11 @@ void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf1
 void launch_sparse24(int bits, const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                      const uint16_t* scales, int group_size, uint16_t* y, hipStream_t s);
 
+// dense single-expert linear at 1..4 token rows (rows staged in LDS, at most 96 KiB)
+bool dense_decode_supported(int M, int K);
+void launch_dense_decode(int wbits, bool bf16, const uint16_t* x, int M, int K, int N, const uint8_t* w,
+                         const uint16_t* s, int groups, uint16_t* y, hipStream_t st);
+
 // ExpertsInt8 load-time quantizer: rows of k 16-bit weights -> int8 codes and
 // one 16-bit scale per row
 void launch_quant_w8(const uint16_t* w, int64_t rows, int k, bool bf16, int8_t* q, uint16_t* s, hipStream_t st);
