@@ -234,13 +234,17 @@ wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int ren
 }
 
 // ---------------------------------------------------------------------------
+// fp32 slabs of M*topk x n_out the DOWN stage may write (one per K slice)
+static int down_slabs(int M, int topk, int E, int n_out, int k_in) {
+    return std::max(wq::prefill_down_split_max(M * topk, E, n_out, k_in), wq::tiny_down_slabs(M, k_in));
+}
+
 size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, int k_in, size_t capacity,
                                 int act_order) {
     if (M < 0 || topk <= 0 || E <= 0 || n_out <= 0 || k_in <= 0) return 0;
     size_t b = 0;
     if ((stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_RAW) && act_order) b += round256(capacity * k_in * 2);
-    if (stage == WQ_STAGE_DOWN)
-        b += round256((size_t)wq::prefill_down_split_max(M * topk, E, n_out, k_in) * M * topk * n_out * sizeof(float));
+    if (stage == WQ_STAGE_DOWN) b += round256((size_t)down_slabs(M, topk, E, n_out, k_in) * M * topk * n_out * sizeof(float));
     return b;
 }
 
@@ -322,7 +326,9 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     g.a_direct = (stage == WQ_STAGE_DOWN) ? 1 : 0;
     g.cap = (int)d->capacity;
 
-    if (act_order) {
+    const int slabs = stage == WQ_STAGE_DOWN ? down_slabs(d->M, d->topk, d->E, d->n_out, d->k_in) : 1;
+    const bool tiny = wq::tiny_supported(wbits, stage, d->M, d->k_in, g.groups, slabs);
+    if (act_order && !tiny) {
         uint16_t* a1 = static_cast<uint16_t*>(d->d_workspace);
         wq::launch_gather_perm(g.a, d->d_k_perm, g.sorted, g.expert_ids, g.ntpp, d->M, d->topk, d->k_in,
                                d->block_size, g.cap, a1, s);
@@ -336,7 +342,8 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
         g.out = y;
     }
     int ksplit = 1;
-    if (wq::prefill_supported(d->n_out, d->k_in, d->block_size)) ksplit = wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
+    if (tiny) ksplit = wq::launch_gemm_tiny(wbits, bf16, stage, g, act_order ? d->d_k_perm : nullptr, slabs, s);
+    else if (wq::prefill_supported(d->n_out, d->k_in, d->block_size)) ksplit = wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
     else wq::launch_gemm_decode(wbits, bf16, stage, g, s);
     WQ_TRY(after_launch(who));
     if (stage == WQ_STAGE_DOWN) {

@@ -49,6 +49,17 @@ struct GemmArgs {
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
 void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
+// batches of at most 4 tokens: one workgroup per (used block, 16 or 32 weight
+// rows), the block's token rows staged in LDS (through the act-order
+// permutation perm [E, k_in] when not NULL, GATE_UP / RAW only); DOWN in up
+// to max_ks K slices (fp32 slab z of the output at out + z * M*topk*n_out).
+// tiny_supported: whether it is the faster kernel for this call;
+// tiny_down_slabs: the most K slices its DOWN stage can take (for the
+// workspace); launch returns the number of K slices it wrote
+bool tiny_supported(int wbits, int stage, int M, int k_in, int groups, int max_ks);
+int tiny_down_slabs(int M, int k_in);
+int launch_gemm_tiny(int wbits, bool bf16, int stage, const GemmArgs& g, const int32_t* perm, int max_ks,
+                     hipStream_t s);
 // large-batch path: 512, 256 or 128 weight rows (dequantized in registers) x
 // 128 (or 64) token rows (staged in LDS)
 bool prefill_supported(int n_out, int k_in, int block_size);
