@@ -110,6 +110,38 @@ def test_raw_exact_integer(bits, bs, act_order):
     assert np.array_equal(got, gu_ref), "max diff %g" % np.abs(got - gu_ref).max()
 
 
+def test_raw_over_65535_sub_blocks():
+    """2^20 pairs in blocks of 16 rows: more 16-row sub-blocks than one grid
+    dimension holds, so the small-batch kernel's grid continues in its third
+    dimension.  Exact-integer inputs; sampled tokens bit for bit."""
+    need_gpu()
+    spec = W8.with_(name="w8-many-rows", N=64)
+    wts = gen.make_moe_weights(spec, seed_config=515)
+    E, n_out, K = wts.w1q.shape
+    rng = np.random.default_rng(516)
+    pow2 = np.array([0.25, 0.5, 1.0, 2.0], np.float32)[rng.integers(0, 4, size=(E, 1, n_out))]
+    packed, sp = wq.pack_w8(wts.w1q, gen.round_to(spec.act, pow2))
+    M, topk, bs = 1 << 19, 2, 16
+    ids = np.argsort(rng.random((M, E)), axis=1)[:, :topk].astype(np.int32)
+    cap = wq.moe_align_capacity(M, topk, E, bs)
+    assert cap // 16 > 65535
+    st, ex, nt = wq.moe_align(torch.from_numpy(ids).cuda(), E, bs, cap)
+    g = torch.Generator(device="cuda").manual_seed(517)
+    xd = torch.randint(-1, 2, (M, K), device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty((M * topk, n_out), dtype=torch.float32, device="cuda")
+    say("raw over 65535 sub-blocks")
+    wq.moe_w8a16_gemm(wq.WQ_STAGE_RAW, xd, M, topk, E, n_out, K, torch.from_numpy(packed).cuda(),
+                      torch.from_numpy(sp.view(np.int16)).cuda(), st, ex, nt, cap, bs, None, out,
+                      act_dtype=wq.WQ_BF16)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 77, 65535 * 8 // topk, M // 2, M - 2, M - 1])
+    x_rows = xd[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    ref, _ = oracle.moe_up(x_rows, ids[rows], wts.w1q, pow2, None, want_gu=True)
+    pairs = (rows[:, None] * topk + np.arange(topk)).ravel()
+    got = out[torch.from_numpy(pairs).cuda()].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, ref), "max diff %g" % np.abs(got - ref).max()
+
+
 # ----------------------------------------------------------------------------
 def run_gate_up(spec, p, xd, ids_np, bs):
     M = xd.shape[0]
@@ -206,6 +238,14 @@ def test_gate_up_many_experts_two_blocks(M):
     assert_close_fp(got[rows], h_ref[stn[rows]], "H many experts M=%d" % M)
     pads = [pos for pos in range(ntn) if stn[pos] >= T]
     assert not np.any(got[pads])
+
+
+@pytest.mark.parametrize("M", [5, 37, 90])
+def test_down_many_experts_two_blocks(M):
+    """80 experts, top-6, Zipf-skewed routing, blocks of 16: the small-batch
+    DOWN with two token blocks per pass over 4 weight tiles (head experts
+    spread over several workgroups)."""
+    _check_down("w8e80", 16, M)
 
 
 def test_down_split_wide_grid_w4():

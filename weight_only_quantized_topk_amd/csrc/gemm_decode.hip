@@ -1,7 +1,11 @@
 // gemm_decode.hip -- small-batch grouped GEMM of the quantized MoE layer.
 //
-// Work unit: one workgroup per (expert e, 16 weight rows) -- 32 rows for the
-// fused gate/up stage, a gate tile and the matching up tile.  The weights are
+// Work unit: one workgroup per (up to RMAX 16-row token sub-blocks of one
+// expert, 16 weight rows) -- 32 rows for the fused gate/up stage, a gate tile
+// and the matching up tile.  The grid runs over the sub-blocks of
+// sorted_token_ids, so an expert holding many token blocks (skewed routing)
+// is spread over several workgroups that run side by side, and experts no
+// token chose launch nothing.  The weights are
 // the MFMA A operand (16 rows x 32 input channels per v_mfma_f32_16x16x32),
 // streamed once from HBM with 128-bit loads: a packed 1 KiB chunk gives every
 // lane 16 bytes, i.e. 4 MFMA k-steps of int4 or 2 of int8.  The token rows of
@@ -22,6 +26,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace wq {
@@ -40,19 +45,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int unit = blockIdx.x;
-    const int e = blockIdx.y;
     const int T = g.M * g.topk;
     const int BS = g.block_size;
-
-    // this expert's blocks: expert_ids is non-decreasing over the used blocks
-    const int nbu = *g.ntpp / BS;
-    const int b0 = lower_bound_i32(g.expert_ids, 0, nbu, e);
-    const int b1 = lower_bound_i32(g.expert_ids, b0, nbu, e + 1);
-    if (b0 >= b1) return;
     const int spb = BS / 16;
+    __shared__ f32x4 red[NW][NT][RMAX][64];
+
+    // 16-row sub-block sbi of sorted_token_ids (grid y, then z past 65535), in block b.  The lanes read the
+    // expert ids of blocks b - 31 .. b + 32 at once; the used blocks of one
+    // expert are contiguous, so the lanes holding b's expert form one run
+    // around lane 31 (searched for beyond the window only when it reaches an end)
+    const int sbi = blockIdx.y + 65535 * blockIdx.z;
+    const int b = sbi / spb;
+    const int bi = b - 31 + lane;
+    const int ecand = (bi >= 0 && bi < g.cap / BS) ? g.expert_ids[bi] : -1;
+    const int ntpp = *g.ntpp;
+    if (sbi * 16 >= ntpp) return;
+    const int nbu = ntpp / BS;
+    const int e = __shfl(ecand, 31);
+    const uint64_t run = __ballot(bi >= 0 && bi < nbu && ecand == e);
+    const int b0 = (run & 1ull) ? lower_bound_i32(g.expert_ids, 0, b - 31, e) : b - 31 + __builtin_ctzll(run);
+    const int b1 = (run >> 63) ? lower_bound_i32(g.expert_ids, b + 33, nbu, e + 1) : b - 31 + 64 - __builtin_clzll(run);
     const int sb_first = b0 * spb;
-    int q = 0;  // live 16-row sub-blocks of the last block (its first row is a real pair)
-    while (q < spb && g.sorted[(b1 - 1) * BS + q * 16] < T) ++q;
+    const int j = sbi - sb_first;  // sub-block index within the expert
+    if (j % RMAX != 0) return;     // one workgroup per RMAX sub-blocks
+    // live 16-row sub-blocks of the expert's last block (those whose first row
+    // is a real pair: a prefix of the block)
+    const int q = __popcll(__ballot(lane < spb && g.sorted[(b1 - 1) * BS + 16 * min(lane, spb - 1)] < T));
     const int S = (b1 - 1 - b0) * spb + q;
 
     const int C = g.k_in / KCHUNK;
@@ -64,8 +82,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
     const uint16_t* se = g.s + (size_t)e * g.groups * g.n_out;
     const int rowq = 4 * (lane >> 4);  // first of this lane's 4 output rows in a tile
     const bool grouped = (WBITS == 4) && g.groups > 1;
-
-    __shared__ f32x4 red[NW][NT][RMAX][64];
 
     // one pass multiplies R token blocks (a compile-time count: full passes take
     // RMAX, the remainder one pass of 2 and/or 1), so no load depends on R
@@ -225,27 +241,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
         }
         __syncthreads();
     };
-    int s0 = 0;
-    for (; s0 + RMAX <= S; s0 += RMAX) pass(s0, std::integral_constant<int, RMAX>{});
-    if constexpr (RMAX >= 4) {
-        if (s0 + 2 <= S) {
-            pass(s0, std::integral_constant<int, 2>{});
-            s0 += 2;
+    if constexpr (STAGE == STAGE_GATE_UP) {
+        // H rows of all-pad sub-blocks (only with blocks larger than 16) are
+        // zero; the expert's first workgroup writes them
+        if (j == 0) {
+            const int N = g.n_out / 2;
+            const int p_lo = (sb_first + S) * 16;
+            const int p_hi = b1 * BS;
+            constexpr int COLS = NP * TILE_ROWS;
+            for (int k = threadIdx.x; k < (p_hi - p_lo) * COLS; k += 64 * NW) {
+                const int p = p_lo + k / COLS;
+                static_cast<uint16_t*>(g.out)[(size_t)p * N + NP * unit * TILE_ROWS + (k % COLS)] = 0;
+            }
         }
     }
-    if constexpr (RMAX >= 2) {
-        if (s0 < S) pass(s0, std::integral_constant<int, 1>{});
-    }
-
-    if constexpr (STAGE == STAGE_GATE_UP) {
-        // H rows of all-pad sub-blocks (only with blocks larger than 16) are zero
-        const int N = g.n_out / 2;
-        const int p_lo = (sb_first + S) * 16;
-        const int p_hi = b1 * BS;
-        constexpr int COLS = NP * TILE_ROWS;
-        for (int k = threadIdx.x; k < (p_hi - p_lo) * COLS; k += 64 * NW) {
-            const int p = p_lo + k / COLS;
-            static_cast<uint16_t*>(g.out)[(size_t)p * N + NP * unit * TILE_ROWS + (k % COLS)] = 0;
+    if (j >= S) return;
+    // sub-blocks j .. j + RMAX - 1 of the expert: one pass of RMAX, or of 2
+    // and/or 1 for the expert's last R < RMAX
+    const int R = min(RMAX, S - j);
+    if (R == RMAX) {
+        pass(j, std::integral_constant<int, RMAX>{});
+    } else {
+        int s0 = j;
+        if constexpr (RMAX >= 4) {
+            if (R >= 2) {
+                pass(s0, std::integral_constant<int, 2>{});
+                s0 += 2;
+            }
+        }
+        if constexpr (RMAX >= 2) {
+            if (s0 < j + R) pass(s0, std::integral_constant<int, 1>{});
         }
     }
 }
@@ -253,7 +278,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
 template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH>
 static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;
-    const dim3 grid(g.n_out / (TILE_ROWS * NT), g.E);
+    const int nsb = g.cap / 16;  // 16-row sub-blocks, over grid y (at most 65535) and z
+    const dim3 grid(g.n_out / (TILE_ROWS * NT), std::min(nsb, 65535), (nsb + 65534) / 65535);
     hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH>), grid, dim3(64 * NW), 0, s, g);
 }
 
@@ -267,9 +293,9 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
 // waves with 2 or 4 row tiles, a long one 8 waves; int4 (half the bytes per
 // weight, so half the work per wave) takes two gate/up tile pairs per
 // workgroup, and four row tiles in DOWN once that grid still fills the GPU.
-// The fused stage of a many-expert layer (E >= 64, skewed routing) takes two
-// token blocks per pass whatever the mean rows per expert: its head experts
-// hold several blocks (DeepSeek-V2 shape M = 64: gate/up 157 -> 132 us in the
+// Both stages of a many-expert layer (E >= 64, skewed routing) take two token
+// blocks per pass whatever the mean rows per expert: its head experts hold
+// several blocks (DeepSeek-V2 shape M = 64: gate/up 157 -> 132 us in the
 // layer).
 template <int WBITS, bool BF16, int STAGE>
 static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
@@ -287,6 +313,10 @@ static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
         // many experts with skewed routing: the head experts hold several token
         // blocks, which one block per pass would stream their weights for each
         launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);
+    } else if (!GU && g.E >= 64 && T > 16 && short_k && np4_ok) {
+        // the same for DOWN, whose short rows (few chunks) take 4 row tiles
+        // on 2 waves (DeepSeek-V2 shape M = 64: 93.7 -> 85.1 us)
+        launch_decode_cfg<WBITS, BF16, STAGE, 2, 4, 2, 2>(g, s);
     } else if (T <= 16 || rows <= 8) {
         if (GU && WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 2>(g, s);
         else if (GU) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
