@@ -17,8 +17,11 @@ under "rows", with the ExpertsInt8 load-time quantizer on Mixtral's w1 (HBM
 GB/s).
 
 Timing: before every step (warm-up and timed) 1 GiB of scratch memory is
-written, outside the timed span, so the weights come from HBM and not from
-the 256 MB last-level cache; each step is bracketed by stream events, and the
+read (or, with --flush write, written), outside the timed span, so the
+weights come from HBM and not from the 256 MB last-level cache -- a read
+leaves the cache full of clean lines, as the other layers' weight reads of a
+decode step do, where a write leaves dirty lines whose write-back then
+competes with the first kernels' reads; each step is bracketed by stream events, and the
 time per step is the mean over the K timed steps of its event span (route ->
 combine).  Each batch is timed twice: launched call by call (which also gives
 the per-stage split), and as one captured HIP graph replayed K times (the
@@ -125,16 +128,21 @@ def rounded(d):
 
 
 class Timer:
-    """Per-step stream events with a cache flush (1 GiB write) before every step."""
+    """Per-step stream events with a cache flush (1 GiB read, or write) before every step."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, mode="read"):
         self.torch = torch
-        self.scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.mode = mode
+        self.scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.words = self.scratch.view(torch.int32)
         self.n = 0
 
     def flush(self):
         self.n += 1
-        self.scratch.fill_(self.n & 0xFF)
+        if self.mode == "write":
+            self.scratch.fill_(self.n & 0xFF)
+        else:
+            self.sink = self.words.sum()
 
     def run(self, step, steps, warmup, nmarks):
         """step(marks) runs one step, recording marks (a list of nmarks events) or
@@ -357,6 +365,8 @@ def main(argv=None):
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="how the last-level cache is emptied before every step (1 GiB read or written)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a device-to-device copy of MIB MiB twice: the known-size reference that "
                          "scales hardware byte counters (FETCH_SIZE / WRITE_SIZE) read under a profiler")
@@ -383,7 +393,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         log("bench: copied %d bytes twice (counter calibration)" % n)
         del src, dst
-    timer = Timer(torch)
+    timer = Timer(torch, args.flush)
     spec = gen.CONFIGS[args.config]
     M = args.m or max(spec.m_sweep)
     act = torch.float16 if spec.act == "f16" else torch.bfloat16
@@ -460,7 +470,8 @@ def main(argv=None):
                    "M": M, "E": spec.E, "topk": spec.topk, "K": spec.K, "N": spec.N, "bits": spec.bits,
                    "block_size": head["block_size"], "touched_experts": head["touched_experts"],
                    "launch": head["launch"],
-                   "cache": "1 GiB scratch written before every step, outside the timed span"},
+                   "cache": "1 GiB scratch %s before every step, outside the timed span"
+                            % ("written" if args.flush == "write" else "read")},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"GBps": round(head["layer_GBps"], 1), "TFLOPs": round(head["layer_TFLOPs"], 2),
