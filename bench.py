@@ -134,7 +134,9 @@ class Timer:
         self.torch = torch
         self.mode = mode
         self.scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-        self.words = self.scratch.view(torch.int32)
+        # a float32 sum reads the buffer once (an integer sum would first copy
+        # it to int64, a 2 GiB write)
+        self.words = self.scratch.view(torch.float32)
         self.n = 0
 
     def flush(self):
