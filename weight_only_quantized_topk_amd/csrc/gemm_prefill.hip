@@ -41,9 +41,14 @@ namespace wq {
 
 constexpr int PF_BK = 64;  // input channels per K step
 constexpr int PF_ROWB = PF_BK * 2;
-constexpr int PF_PD = 2;  // K steps of weights in flight per wave
 
-__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte piece ch of token row `row` sits at piece ch ^ ((row >> 1) & 7) of
+// the row: the 16 lanes of one 128-bit LDS access (16 consecutive rows, one
+// piece, for the B operand reads; 2 rows, 8 pieces, for the stores) then hit
+// 16 distinct 16-byte bank groups, and the swizzle of row 16 j + r does not
+// depend on j, so a wave's reads of its 16-row token tiles differ by
+// immediate offsets only.
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lds_off(int row, int ch) { return row * PF_ROWB + ((ch ^ lds_swz(row)) << 4); }
 
 template <int WBITS, bool BF16, int STAGE, int NW, int RT, int BM, int OCC>
@@ -86,23 +91,25 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
     const uint8_t* wsrc = g.w + (size_t)e * expert_bytes + (size_t)rt0 * C * CHUNK_BYTES + lane * 16;
     const size_t tile_stride = (size_t)C * CHUNK_BYTES;
     const uint16_t* ssrc = se + rt0 * TILE_ROWS + (lane & 15);  // int4: scale of this lane's row
-    u32x4 w8[PF_PD][RT];
-    u32x2 w4[PF_PD][RT];
-    uint32_t sc[PF_PD][RT];
-    auto wload = [&](int step, auto SLOT) {
-        constexpr int sl = decltype(SLOT)::value;
+    // raw weights of one K step (loaded one step before they are dequantized)
+    u32x4 w8[RT];
+    u32x2 w4[RT];
+    uint32_t sc[RT];
+    // raw weights (and int4 group scale) of weight tile t for one K step
+    auto wload_t = [&](int step, int t) {
         if constexpr (WBITS == 8) {
-#pragma unroll
-            for (int t = 0; t < RT; ++t) w8[sl][t] = ldg128_stream(wsrc + t * tile_stride + (size_t)step * CHUNK_BYTES);
+            w8[t] = ldg128(wsrc + t * tile_stride + (size_t)step * CHUNK_BYTES);
         } else {
             const int c = step >> 1, half = step & 1;  // a 128-channel chunk spans two K steps
-#pragma unroll
-            for (int t = 0; t < RT; ++t)  // cached: the many token tiles of an expert re-read them
-                w4[sl][t] = *reinterpret_cast<const u32x2*>(wsrc + t * tile_stride + (size_t)c * CHUNK_BYTES + 8 * half);
+            // cached: the token tiles of an expert re-read its weight tiles
+            w4[t] = *reinterpret_cast<const u32x2*>(wsrc + t * tile_stride + (size_t)c * CHUNK_BYTES + 8 * half);
             const int grp = g.groups > 1 ? c : 0;
-#pragma unroll
-            for (int t = 0; t < RT; ++t) sc[sl][t] = ssrc[(size_t)grp * g.n_out + t * TILE_ROWS];
+            sc[t] = ssrc[(size_t)grp * g.n_out + t * TILE_ROWS];
         }
+    };
+    auto wload = [&](int step) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) wload_t(step, t);
     };
     // token pieces: pad rows read a valid row (their outputs are discarded, H pad rows written as 0)
     const uint16_t* tsrc[TPIECES];
@@ -138,55 +145,95 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) jact += __builtin_amdgcn_readfirstlane(g.sorted[row0 + 16 * j]) < T ? 1 : 0;
     const bool full = jact > TJ / 2;  // else the second half of the token tiles is padding only
-    // one K step: dequantize this step's weights, stage the next step's tokens,
-    // issue the loads of later steps, multiply, one barrier.  The token loads
-    // go out before the weight loads, so waiting for them one step later does
-    // not wait for the weights of step + PF_PD.
-    auto body = [&](int step, const uint8_t* cur, uint8_t* nxt, auto SLOT) {
-        constexpr int sl = decltype(SLOT)::value;
-        u32x4 a[RT][2];
+    // One K step multiplies this step's weights (dequantized during the
+    // previous step, in registers) by the token tile in `cur`, and spreads the
+    // dequantization of the next step's weights over the MFMAs of the first
+    // half of the token tiles, so the VALU work of one step overlaps the matrix
+    // work of the other instead of running ahead of it (the barrier that ends
+    // each step keeps the waves of a SIMD in phase, which made the two phases
+    // serial).  Each tile's raw weight registers are refilled with step + 2 as
+    // soon as they are converted, one step ahead of their dequantization.  The token loads go out before the
+    // weight loads, so waiting for them one step later does not wait for the
+    // weights.
+    constexpr int PIECES = RT * 2;  // dequantized A operands per step
+    constexpr int HALF = TJ / 2;
+    auto deq = [&](u32x4 (&an)[RT][2], auto P) {
+        constexpr int t = decltype(P)::value / 2, kk = decltype(P)::value % 2;
+        if constexpr (WBITS == 8) {
+            an[t][kk] = dequant_w8x8<BF16>(w8[t][2 * kk], w8[t][2 * kk + 1]);
+        } else {
+            const uint32_t sv = sc[t];
+            an[t][kk] = dequant_w4_f16_scaled(w4[t][kk], __builtin_bit_cast(f16x2, sv | (sv << 16)));
+        }
+        // pin the result here: without it the compiler sinks the conversion to
+        // the first use, one step later, ahead of that step's MFMAs
+        asm volatile("" : "+v"(an[t][kk]));
+    };
+    // B operands of one 16-row token tile (the two 32-channel halves of the step)
+    auto bread = [&](int j, const uint8_t* cur, u32x4 (&b)[2]) {
+        const int r = 16 * j + brow;
+        b[0] = *reinterpret_cast<const u32x4*>(cur + lds_off(r, g4));
+        b[1] = *reinterpret_cast<const u32x4*>(cur + lds_off(r, 4 + g4));
+    };
+    auto mma = [&](auto J, const u32x4 (&b)[2], const u32x4 (&ac)[RT][2]) {
+        constexpr int j = decltype(J)::value;
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t) acc[t][j] = mfma16x16x32<BF16>(ac[t][0], b[0], acc[t][j]);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if constexpr (WBITS == 8) {
-                    a[t][kk] = dequant_w8x8<BF16>(w8[sl][t][2 * kk], w8[sl][t][2 * kk + 1]);
-                } else {
-                    const uint32_t sv = sc[sl][t];
-                    a[t][kk] = dequant_w4_f16_scaled(w4[sl][t][kk], __builtin_bit_cast(f16x2, sv | (sv << 16)));
-                }
-            }
+        for (int t = 0; t < RT; ++t) acc[t][j] = mfma16x16x32<BF16>(ac[t][1], b[1], acc[t][j]);
+    };
+    // the B operands of token tile j + 1 are read from LDS before the MFMAs
+    // of tile j are issued (two register sets), so the LDS latency is hidden
+    // behind those MFMAs rather than waited for before each tile
+    auto body = [&](int step, const uint8_t* cur, uint8_t* nxt, const u32x4 (&ac)[RT][2], u32x4 (&an)[RT][2]) {
         tstore(nxt);
         tload(min(step + 2, step_end - 1));  // the last steps reload step_end - 1: no branch
-        wload(min(step + PF_PD, step_end - 1), SLOT);
-        auto tiles = [&](auto J0, auto J1) {  // token tiles [J0, J1)
-#pragma unroll
-            for (int j = decltype(J0)::value; j < decltype(J1)::value; ++j) {
-                const int r = 16 * j + brow;
-                const u32x4 b0 = *reinterpret_cast<const u32x4*>(cur + lds_off(r, g4));
-                const u32x4 b1 = *reinterpret_cast<const u32x4*>(cur + lds_off(r, 4 + g4));
-#pragma unroll
-                for (int t = 0; t < RT; ++t) {
-                    acc[t][j] = mfma16x16x32<BF16>(a[t][0], b0, acc[t][j]);
-                    acc[t][j] = mfma16x16x32<BF16>(a[t][1], b1, acc[t][j]);
-                }
+        u32x4 bx[2], by[2];
+        bread(0, cur, bx);
+        static_for<0, HALF>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if constexpr (j % 2 == 0) {
+                bread(j + 1, cur, by);
+                mma(J, bx, ac);
+            } else {
+                bread(j + 1, cur, bx);
+                mma(J, by, ac);
             }
-        };
-        tiles(std::integral_constant<int, 0>{}, std::integral_constant<int, TJ / 2>{});
-        if (full) tiles(std::integral_constant<int, TJ / 2>{}, std::integral_constant<int, TJ>{});
+            static_for<j * PIECES / HALF, (j + 1) * PIECES / HALF>([&](auto P) {
+                deq(an, P);
+                // tile t's raw registers are free once both its halves are
+                // converted: refill them with step + 2 right away (one full
+                // step of latency for every tile)
+                if constexpr (decltype(P)::value % 2 == 1) wload_t(min(step + 2, step_end - 1), decltype(P)::value / 2);
+            });
+        });
+        if (full) {
+            static_for<HALF, TJ>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                if constexpr ((j - HALF) % 2 == 0) {
+                    if constexpr (j + 1 < TJ) bread(j + 1, cur, by);
+                    mma(J, HALF % 2 == 0 ? bx : by, ac);
+                } else {
+                    if constexpr (j + 1 < TJ) bread(j + 1, cur, bx);
+                    mma(J, HALF % 2 == 0 ? by : bx, ac);
+                }
+            });
+        }
         __syncthreads();
     };
     uint8_t* b0 = lds;
     uint8_t* b1 = lds + BUF;
+    u32x4 aA[RT][2], aB[RT][2];
     tload(step0);
-    wload(step0, std::integral_constant<int, 0>{});
+    wload(step0);
     tstore(b0);
+    static_for<0, PIECES>([&](auto P) { deq(aA, P); });
     tload(min(step0 + 1, step_end - 1));
-    wload(min(step0 + 1, step_end - 1), std::integral_constant<int, 1>{});
+    wload(min(step0 + 1, step_end - 1));
     __syncthreads();
     for (int step = step0; step < step_end; step += 2) {
-        body(step, b0, b1, std::integral_constant<int, 0>{});
-        if (step + 1 < step_end) body(step + 1, b1, b0, std::integral_constant<int, 1>{});
+        body(step, b0, b1, aA, aB);
+        if (step + 1 < step_end) body(step + 1, b1, b0, aB, aA);
     }
 
     // epilogue
