@@ -51,9 +51,9 @@ def test_sparse_float(M):
 
 @pytest.mark.parametrize("M", [1, 16, 40, 100, 200])
 def test_sparse_float_long_k(M):
-    """K = 2304 (9 chunks of 256: a full block of 8 in flight plus a tail) and
-    N = 512, through each batch-size kernel (16/32/64-token streaming, 256 x
-    64 tiles)."""
+    """K = 2304 (9 chunks of 256: two full blocks of 4 in flight plus a tail)
+    and N = 512, through each batch-size kernel (16/32/64-token streaming on 8
+    or 16 waves, 256 x 64 tiles)."""
     need_gpu()
     spec = gen.CFG4.with_(K=2304, N=512)
     sw = gen.make_sparse_weights(spec, seed_config=313)

@@ -13,10 +13,11 @@
 // through ABID 0/1.
 //
 // Two kernels:
-//  - small and medium batches (M <= 128): one workgroup per 64 output rows
-//    (one 16-row tile per wave) and 16, 32 or 64 tokens; all waves walk the
-//    same 256-channel chunks, whose token tile is staged once in LDS and
-//    shared; each wave keeps the weights of 8 chunks in flight in registers;
+//  - small and medium batches (M <= 128): one workgroup per 128 (16 tokens)
+//    or 256 output rows (32 or 64 tokens), one 16-row tile per wave; all
+//    waves walk the same 256-channel chunks, whose token tile is staged once
+//    in LDS and shared; each wave keeps the weights of 4 chunks in flight in
+//    registers;
 //  - large batches: one workgroup per 256 output rows and 64 tokens; the token
 //    tile of each chunk is staged once in LDS and shared by the 4 waves, each
 //    of which multiplies its own 64 weight rows, read straight from the packed
@@ -399,12 +400,19 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
     }
 }
 
+// Workgroup shape: every workgroup stages its token rows once per chunk, so
+// the token traffic from L2 falls as a workgroup covers more weight rows;
+// measured at K = 7168, N = 20480 (4-bit / 8-bit codes): 16 tokens on 8
+// waves (128 weight rows, 4 chunks in flight) 25.0 -> 20.8 / 35.5 -> 33.4 us,
+// 32 and 64 tokens on 16 waves (256 rows) M = 64 45.7 -> 36.1 / 61.4 -> 52.6 us,
+// M = 128 76.7 -> 51.2 / 106.8 -> 73.4 us, against 4 waves, 8 in flight
 template <int VBITS, int R>
 static void launch_stream(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
                           const uint16_t* scales, int sstride, uint16_t* y, hipStream_t s) {
-    const dim3 grid((N / 16 + 3) / 4, (M + 16 * R - 1) / (16 * R));
-    hipLaunchKernelGGL((sparse24_stream_kernel<VBITS, R, 8, 4>), grid, dim3(256), 0, s, x, M, K, N, vals, meta, scales,
-                       sstride, y);
+    constexpr int NWV = R == 1 ? 8 : 16;
+    const dim3 grid((N / 16 + NWV - 1) / NWV, (M + 16 * R - 1) / (16 * R));
+    hipLaunchKernelGGL((sparse24_stream_kernel<VBITS, R, 4, NWV>), grid, dim3(64 * NWV), 0, s, x, M, K, N, vals, meta,
+                       scales, sstride, y);
 }
 
 template <int VBITS, int NW, int TPW>
