@@ -61,3 +61,80 @@ def test_graph_replay_matches_eager(key, M):
     torch.cuda.synchronize()
     assert torch.equal(out2, ref2)
     assert not torch.equal(ref2, ref)
+
+
+def _graph_of(call):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    return g
+
+
+def _check_replays(call, out, x, x2):
+    """call() writes out from x; every replay of its graph equals the eager
+    result bit for bit (eager work and synchronisations between the replays),
+    and a replay after x is overwritten in place follows the new values."""
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = _graph_of(call)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        call()  # eager work on the same buffers between replays
+        torch.cuda.synchronize()
+    x0 = x.clone()
+    x.copy_(x2)
+    call()
+    torch.cuda.synchronize()
+    ref2 = out.clone()
+    x.copy_(x0)
+    call()
+    x.copy_(x2)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref2)
+    assert not torch.equal(ref2, ref)
+
+
+@pytest.mark.parametrize("M", [1, 16, 200])
+def test_graph_replay_dense(M):
+    """The dense int4 linear layer (one kernel at one row; identity routing,
+    small- or large-batch GEMM and combine above) as a graph."""
+    need_gpu()
+    import numpy as np
+    spec = gen.CFG3.with_(name="w4-dense-graph", E=1, topk=1, K=512, N=192, act_order=False)
+    wts = gen.make_moe_weights(spec, seed_config=530)
+    packed_w, sp, _ = wq.pack_w4(wts.w1q, wts.s1, spec.group_size)
+    wd, sd = torch.from_numpy(packed_w).cuda(), torch.from_numpy(sp.view(np.int16)).cuda()
+    n_out, K = wts.w1q.shape[1], wts.w1q.shape[2]
+    say("graph dense", M)
+    x = dev_u16(gen.make_tokens(spec, M, seed_config=531).x, "f16")
+    x2 = dev_u16(gen.make_tokens(spec, M, seed_config=532).x, "f16")
+    y = torch.empty((M, n_out), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(1, wq.dense_gemm_workspace_bytes(M, K, n_out)), dtype=torch.uint8, device="cuda")
+    _check_replays(lambda: wq.dense_w4a16_gemm(x, n_out, wd, sd, 128, out=y, workspace=ws), y, x, x2)
+
+
+@pytest.mark.parametrize("M", [1, 16, 200])
+def test_graph_replay_sparse24(M):
+    """The 2:4-sparse int4 linear layer (decode, streaming and tile kernels) as a graph."""
+    need_gpu()
+    import numpy as np
+    spec = gen.CFG4.with_(K=1024, N=256)
+    sw = gen.make_sparse_weights(spec, seed_config=533)
+    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s)
+    vd, md, sd = torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(), torch.from_numpy(sp.view(np.int16)).cuda()
+    say("graph sparse", M)
+    x = dev_u16(gen.make_sparse_x(spec, M, seed_config=534), "f16")
+    x2 = dev_u16(gen.make_sparse_x(spec, M, seed_config=535), "f16")
+    y = torch.empty((M, spec.N), dtype=torch.float16, device="cuda")
+    _check_replays(lambda: wq.sparse24_w4a16_gemm(x, vd, md, sd, spec.N, out=y), y, x, x2)
