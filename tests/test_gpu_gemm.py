@@ -33,8 +33,13 @@ W8E80 = gen.CFG5.with_(name="w8-many-80", E=80, topk=6, K=256, N=256, zipf_s=1.1
 # GATE_UP (8192 outputs) takes the 512-row shape
 W4K = W4.with_(name="w4-longk", K=256, N=4096)
 W8K = W8.with_(name="w8-longk", K=256, N=4096)
-SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E, "w4k": W4K, "w8k": W8K, "w8e80": W8E80}
-SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505, "w4k": 506, "w8k": 507, "w8e80": 508}
+# an odd number of 64-channel K steps in DOWN (k_in = N = 320: 5 steps): the
+# large-batch kernel's two-step loop ends on a single step
+W8ODD = W8.with_(name="w8-odd-steps", K=512, N=320)
+SPECS = {"w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8": W8, "w8e": W8E, "w4k": W4K, "w8k": W8K, "w8e80": W8E80,
+         "w8odd": W8ODD}
+SEED = {"w4": 501, "w4ao": 502, "w4pc": 503, "w8": 504, "w8e": 505, "w4k": 506, "w8k": 507, "w8e80": 508,
+        "w8odd": 509}
 
 
 def _pack(spec, wts):
@@ -193,7 +198,7 @@ def test_gate_up(key, bs, M):
     assert_close_fp(got, h_ref, "H %s bs=%d M=%d" % (key, bs, M))
 
 
-@pytest.mark.parametrize("key", ["w4", "w4ao", "w8", "w8e"])
+@pytest.mark.parametrize("key", ["w4", "w4ao", "w8", "w8e", "w8odd"])
 @pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_down(key, bs, M):
@@ -316,7 +321,7 @@ def _check_down(key, bs, M):
 
 
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e"])
+@pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e", "w8odd"])
 @pytest.mark.parametrize("bs", [16, 64, 128])
 @pytest.mark.parametrize("M", [1, 16, 53, 512])
 def test_layer(key, bs, M):
