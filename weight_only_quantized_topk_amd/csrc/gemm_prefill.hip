@@ -10,17 +10,19 @@
 //    [8 (l/16), +8) and [32 + 8 (l/16), +8) of row l % 16 for every 64-channel
 //    K step, which is exactly the A operand layout of two
 //    v_mfma_f32_16x16x32 instructions; each wave loads its own tiles with
-//    coalesced 128-bit (int8) or 64-bit (int4) loads two K steps ahead and
-//    dequantizes them in registers (int8 exact; int4: q * group scale rounded
-//    once to fp16).  int8 weights are streamed past the caches; int4 weights
-//    are cached, which measured 9-13 % faster (an expert's weight tile is
-//    re-read by every token tile of the expert, about 8 at M = 4096).
+//    coalesced 128-bit (int8) or 64-bit (int4) loads and dequantizes them in
+//    registers (int8 exact; int4: q * group scale rounded once to fp16).  The
+//    weights go through the caches: an expert's weight tile is re-read by
+//    every token tile of the expert (about 2 at M = 1024, 8 at M = 4096).
+//  - Software pipeline of a K step: the MFMAs of step s run with step s + 1's
+//    weights converted between them, each tile's raw registers are refilled
+//    with step s + 2 as soon as they are converted, and the B operands of
+//    token tile j + 1 are read from LDS before tile j is multiplied.
 //  - The BM token rows of a K step (gathered through sorted_token_ids, or read
 //    directly for H and the act-order-permuted activations) are staged in one
 //    of two LDS buffers: step s + 1 is stored while step s is multiplied, so a
-//    K step costs one barrier.  Rows are 128 bytes split in 16-byte chunks
-//    stored at chunk ^ ((row ^ (row >> 3)) & 7), free of bank conflicts for
-//    both the B operand reads and the stores.
+//    K step costs one barrier.  Rows are 128 bytes split in 16-byte pieces;
+//    see lds_swz for the bank-conflict-free placement.
 //  - Accumulators are fp32 (v_mfma_f32_16x16x32_{bf16,f16}).  Lane l holds
 //    output rows 4 (l/16) + r of a weight tile for token row l % 16.  With the
 //    gate/up interleave of the packer, weight tile 2q holds 16 gate rows and
