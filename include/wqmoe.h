@@ -147,7 +147,9 @@ wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int ren
  * Expert rows are those of d_sorted_token_ids (from moe_align with the same
  * block_size); block_size 64 or a multiple of 128 (with n_out a multiple of 128
  * and k_in a multiple of 64) selects the large-batch kernel, other blocks the
- * small-batch (decode) kernel.
+ * small-batch (decode) kernel.  The large-batch kernel addresses the
+ * activation rows with 32-bit byte offsets: capacity * k_in * 2 bytes above
+ * 4 GiB is rejected with WQ_ERR_UNSUPPORTED (nothing is launched).
  *
  * Stages (A is d_a, W the expert's packed weight of n_out rows, k_in columns):
  *  GATE_UP  d_a = x [M, k_in]; W = w1 packed with WQ_PACK_INTERLEAVE_GATE_UP,
@@ -238,7 +240,8 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
  *     0 bytes (NULL allowed) for 1..4 rows without act-order when the rows fit
  *     96 KiB of LDS: one small-batch kernel with the rows staged in LDS
  * Limits: int4 K % 128 == 0 and fp16 activations; int8 K % 64 == 0; N % 16 ==
- * 0.  Asynchronous on `stream`; calls sharing a workspace must be
+ * 0; above 24 rows (large-batch kernel) at most 4 GiB of activation rows
+ * including the block padding (else WQ_ERR_UNSUPPORTED).  Asynchronous on `stream`; calls sharing a workspace must be
  * stream-ordered.
  */
 size_t dense_gemm_workspace_bytes(int M, int K, int N, int act_order);

@@ -365,3 +365,22 @@ def test_layer_empty_batch():
                        torch.empty((0, spec.E), dtype=torch.float32, device="cuda"), p, spec.topk)
     torch.cuda.synchronize()
     assert out.shape == (0, spec.K)
+
+
+def test_large_batch_rejects_activations_over_4gib():
+    """The large-batch kernel addresses activation rows with 32-bit byte
+    offsets: a capacity whose rows x k_in x 2 bytes exceed 4 GiB is refused
+    with WQ_ERR_UNSUPPORTED before anything is launched (the buffers are never
+    touched, so small ones suffice)."""
+    need_gpu()
+    spec, wts, p = setup("w8")
+    M, bs = 300, 128
+    toks, w, ids = routed(spec, M, seed=990)
+    st, ex, nt, cap = align_dev(ids, spec.E, bs)
+    big = (1 << 28)  # rows; x 512 channels x 2 bytes = 2^38 bytes
+    h = torch.empty((cap, spec.N), dtype=p.act, device="cuda")
+    with pytest.raises(wq.WqError) as ei:
+        wq.moe_w8a16_gemm(wq.WQ_STAGE_GATE_UP, dev_u16(toks.x, spec.act), M, spec.topk, spec.E, 2 * spec.N, spec.K,
+                          p.w1, p.s1, st, ex, nt, big, bs, None, h, None, act_dtype=p.act_code)
+    assert ei.value.status == 2
+    torch.cuda.synchronize()

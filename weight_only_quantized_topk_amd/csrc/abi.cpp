@@ -328,6 +328,10 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
 
     const int slabs = stage == WQ_STAGE_DOWN ? down_slabs(d->M, d->topk, d->E, d->n_out, d->k_in) : 1;
     const bool tiny = wq::tiny_supported(wbits, stage, d->M, d->k_in, g.groups, slabs);
+    const bool large = !tiny && wq::prefill_supported(d->n_out, d->k_in, d->block_size);
+    WQ_REQUIRE(!large || wq::prefill_fits(d->capacity, d->k_in), WQ_ERR_UNSUPPORTED,
+               "%s: activations of %zu rows x %d channels exceed 4 GiB (large-batch kernel)", who, d->capacity,
+               d->k_in);
     if (act_order && !tiny) {
         uint16_t* a1 = static_cast<uint16_t*>(d->d_workspace);
         wq::launch_gather_perm(g.a, d->d_k_perm, g.sorted, g.expert_ids, g.ntpp, d->M, d->topk, d->k_in,
@@ -343,7 +347,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     }
     int ksplit = 1;
     if (tiny) ksplit = wq::launch_gemm_tiny(wbits, bf16, stage, g, act_order ? d->d_k_perm : nullptr, slabs, s);
-    else if (wq::prefill_supported(d->n_out, d->k_in, d->block_size)) ksplit = wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
+    else if (large) ksplit = wq::launch_gemm_prefill(wbits, bf16, stage, g, s);
     else wq::launch_gemm_decode(wbits, bf16, stage, g, s);
     WQ_TRY(after_launch(who));
     if (stage == WQ_STAGE_DOWN) {
@@ -499,6 +503,8 @@ wq_status dense_gemm(int wbits, const void* d_x, int M, int K, int N, const void
                who);
 
     const DenseLayout L = dense_layout(M, K, N, act_order);
+    WQ_REQUIRE(L.bs == 16 || wq::prefill_fits(L.cap, K), WQ_ERR_UNSUPPORTED,
+               "%s: activations of %d rows x %d channels exceed 4 GiB (large-batch kernel)", who, M, K);
     uint8_t* ws = static_cast<uint8_t*>(d_ws);
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
     int32_t* eids = reinterpret_cast<int32_t*>(ws + L.off_eids);

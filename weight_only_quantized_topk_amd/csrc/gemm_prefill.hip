@@ -44,6 +44,11 @@ namespace wq {
 constexpr int PF_BK = 64;  // input channels per K step
 constexpr int PF_ROWB = PF_BK * 2;
 
+// buffer resource over 4 GiB from base (raw addressing: offsets are bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
 // 16-byte piece ch of token row `row` sits at piece ch ^ ((row >> 1) & 7) of
 // the row: the 16 lanes of one 128-bit LDS access (16 consecutive rows, one
 // piece, for the B operand reads; 2 rows, 8 pieces, for the stores) then hit
@@ -89,9 +94,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
     const uint16_t* se = g.s + (size_t)e * g.groups * g.n_out;
 
     // ----------------------------------------------------------- loaders
-    const int rt0 = ntile * (BN / TILE_ROWS) + wave * RT;  // first 16-row weight tile of this wave
-    const uint8_t* wsrc = g.w + (size_t)e * expert_bytes + (size_t)rt0 * C * CHUNK_BYTES + lane * 16;
-    const size_t tile_stride = (size_t)C * CHUNK_BYTES;
+    // Buffer loads: the wave-uniform part of a weight address (expert, weight
+    // tile, K step) is the resource base or the scalar offset, and a token
+    // piece's address a 32-bit offset from the activations' base, which frees
+    // the vector registers 64-bit addresses would hold (int4 large-batch
+    // Mixtral gate/up 1.83 -> 1.77 ms at M = 4096).
+    const int rt0 = ntile * (BN / TILE_ROWS) + __builtin_amdgcn_readfirstlane(wave) * RT;  // first tile of the wave
+    const int tile_stride = C * CHUNK_BYTES;
+    const __amdgpu_buffer_rsrc_t wres = make_rsrc(g.w + (size_t)e * expert_bytes + (size_t)rt0 * tile_stride);
+    const int wlane = lane * 16;
     const uint16_t* ssrc = se + rt0 * TILE_ROWS + (lane & 15);  // int4: scale of this lane's row
     // raw weights of one K step (loaded one step before they are dequantized)
     u32x4 w8[RT];
@@ -100,11 +111,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
     // raw weights (and int4 group scale) of weight tile t for one K step
     auto wload_t = [&](int step, int t) {
         if constexpr (WBITS == 8) {
-            w8[t] = ldg128(wsrc + t * tile_stride + (size_t)step * CHUNK_BYTES);
+            w8[t] = __builtin_amdgcn_raw_buffer_load_b128(wres, wlane, t * tile_stride + step * CHUNK_BYTES, 0);
         } else {
             const int c = step >> 1, half = step & 1;  // a 128-channel chunk spans two K steps
             // cached: the token tiles of an expert re-read its weight tiles
-            w4[t] = *reinterpret_cast<const u32x2*>(wsrc + t * tile_stride + (size_t)c * CHUNK_BYTES + 8 * half);
+            w4[t] = __builtin_amdgcn_raw_buffer_load_b64(wres, wlane, t * tile_stride + c * CHUNK_BYTES + 8 * half, 0);
             const int grp = g.groups > 1 ? c : 0;
             sc[t] = ssrc[(size_t)grp * g.n_out + t * TILE_ROWS];
         }
@@ -114,19 +125,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
         for (int t = 0; t < RT; ++t) wload_t(step, t);
     };
     // token pieces: pad rows read a valid row (their outputs are discarded, H pad rows written as 0)
-    const uint16_t* tsrc[TPIECES];
+    // (byte offsets fit 32 bits: the host checks rows x k_in x 2 < 2^32)
+    const __amdgpu_buffer_rsrc_t ares = make_rsrc(g.a);
+    uint32_t toff[TPIECES];
 #pragma unroll
     for (int i = 0; i < TPIECES; ++i) {
         const int id = tid + NT * i;
         const int p = row0 + (id >> 3);
         const int pair = g.sorted[p];
         const int src = g.a_direct ? p : (pair < T ? pair / g.topk : 0);
-        tsrc[i] = g.a + (size_t)src * g.k_in + (id & 7) * 8;
+        toff[i] = (uint32_t)src * (uint32_t)(g.k_in * 2) + (id & 7) * 16;
     }
     u32x4 tv[TPIECES];
     auto tload = [&](int step) {
 #pragma unroll
-        for (int i = 0; i < TPIECES; ++i) tv[i] = ldg128(tsrc[i] + step * PF_BK);
+        for (int i = 0; i < TPIECES; ++i) tv[i] = __builtin_amdgcn_raw_buffer_load_b128(ares, toff[i], step * PF_BK * 2, 0);
     };
     auto tstore = [&](uint8_t* buf) {
 #pragma unroll
@@ -377,6 +390,8 @@ static void launch_prefill_s(int stage, const GemmArgs& g, int ksplit, hipStream
 bool prefill_supported(int n_out, int k_in, int block_size) {
     return (block_size == 64 || block_size % 128 == 0) && n_out % 128 == 0 && k_in % PF_BK == 0;
 }
+
+bool prefill_fits(size_t rows, int k_in) { return rows * (size_t)k_in * 2 <= (size_t)0xffffffffu; }
 
 int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s) {
     const int ksplit =

@@ -63,6 +63,9 @@ int launch_gemm_tiny(int wbits, bool bf16, int stage, const GemmArgs& g, const i
 // large-batch path: 512, 256 or 128 weight rows (dequantized in registers) x
 // 128 (or 64) token rows (staged in LDS)
 bool prefill_supported(int n_out, int k_in, int block_size);
+// the large-batch kernel addresses its activations (rows x k_in 16-bit values)
+// with 32-bit byte offsets
+bool prefill_fits(size_t rows, int k_in);
 // K slices of the large-batch DOWN stage for T = M*topk rows over E experts in
 // blocks of block_size rows (1, 2 or 4); the DOWN workspace holds that many
 // fp32 slabs of T x n_out.  _max: the largest over the supported block sizes
