@@ -237,8 +237,10 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
  *   d_k_perm: int4 act-order permutation from wq_pack_w4 ([1, K]) or NULL
  *   d_workspace: dense_gemm_workspace_bytes(M, K, N, act_order) bytes, 256-byte
  *     aligned (the routing arrays, the act-order gather, fp32 partial sums);
- *     0 bytes (NULL allowed) for 1..4 rows without act-order when the rows fit
- *     96 KiB of LDS: one small-batch kernel with the rows staged in LDS
+ *     0 bytes (NULL allowed) for 1..16 rows without act-order: one
+ *     small-batch kernel (1..4 rows staged in LDS whole when they fit 96 KiB,
+ *     else the tokens of each K chunk staged in LDS and shared by the 8
+ *     weight tiles of a workgroup)
  * Limits: int4 K % 128 == 0 and fp16 activations; int8 K % 64 == 0; N % 16 ==
  * 0; above 24 rows (large-batch kernel) at most 4 GiB of activation rows
  * including the block padding (else WQ_ERR_UNSUPPORTED).  Asynchronous on `stream`; calls sharing a workspace must be

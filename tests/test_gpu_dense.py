@@ -1,9 +1,11 @@
 """GPU parity of the dense single-expert W4A16 / W8A16 linear layer
 (dense_w4a16_gemm, dense_w8a16_gemm) against the oracle's projection with one
-expert and top-1: every batch regime of the dispatch (the single-kernel path
-for 1..4 rows, the grouped small-batch kernel up to 24 rows, 64-row tiles up to
-96, 128-row tiles above, with a K split for a long K and few outputs), int8
-per-column, int4 group-128, per-column and act-order weights.  Relative
+expert and top-1: every batch regime of the dispatch (the single-kernel paths
+for 1..4 rows staged whole and for 5..16 rows staged per K chunk, the grouped
+small-batch kernel up to 24 rows and with act-order, 64-row tiles up to 96,
+128-row tiles above, with a K split for a long K and few outputs), int8
+per-column, int4 group-128, per-column and act-order weights, and output
+counts that leave the last 8-tile workgroup partial.  Relative
 Frobenius error <= 5e-3 and max abs error <= 3e-2 * max |ref|."""
 import numpy as np
 import pytest
@@ -22,7 +24,11 @@ W4 = gen.CFG3.with_(name="w4-dense", E=1, topk=1, K=512, N=192, act_order=False)
 W4AO = W4.with_(name="w4ao-dense", act_order=True)
 W4PC = W4.with_(name="w4pc-dense", group_size=-1)
 W8LK = W8.with_(name="w8-dense-longk", K=4096, N=128)
-SPECS = {"w8": W8, "w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8lk": W8LK}
+# 400 outputs = 25 row tiles: the 8-tile workgroups of 5..16 rows end on a
+# partial group
+W8RAG = W8.with_(name="w8-dense-ragged", N=200)
+W4RAG = W4.with_(name="w4-dense-ragged", N=200)
+SPECS = {"w8": W8, "w4": W4, "w4ao": W4AO, "w4pc": W4PC, "w8lk": W8LK, "w8rag": W8RAG, "w4rag": W4RAG}
 _cache = {}
 
 
@@ -41,8 +47,8 @@ def setup(key):
     return _cache[key]
 
 
-@pytest.mark.parametrize("key", ["w8", "w4", "w4ao", "w4pc"])
-@pytest.mark.parametrize("M", [1, 2, 4, 13, 40, 300])
+@pytest.mark.parametrize("key", ["w8", "w4", "w4ao", "w4pc", "w8rag", "w4rag"])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 13, 16, 40, 300])
 def test_dense_matches_oracle(key, M):
     need_gpu()
     spec, wts, (wd, sd, kd) = setup(key)
@@ -78,8 +84,8 @@ def test_dense_long_k_split():
 
 @pytest.mark.parametrize("bits", [4, 8])
 def test_dense_rows_too_long_for_lds(bits):
-    """4 rows of K = 16384: the rows do not fit the single kernel's LDS, so the
-    grouped path runs (with its workspace)."""
+    """4 rows of K = 16384 do not fit the LDS whole, so the kernel that stages
+    the tokens of one K chunk at a time runs (still one kernel, no workspace)."""
     need_gpu()
     base = W4 if bits == 4 else W8
     spec = base.with_(name="dense-longrow-%d" % bits, K=16384, N=64)
@@ -91,7 +97,7 @@ def test_dense_rows_too_long_for_lds(bits):
     wd, sd = torch.from_numpy(packed).cuda(), torch.from_numpy(sp.view(np.int16)).cuda()
     n_out = wts.w1q.shape[1]
     M = 4
-    assert wq.dense_gemm_workspace_bytes(M, spec.K, n_out) > 0
+    assert wq.dense_gemm_workspace_bytes(M, spec.K, n_out) == 0
     toks = gen.make_tokens(spec, M, seed_config=681)
     x = dev_u16(toks.x, spec.act)
     y = wq.dense_w4a16_gemm(x, n_out, wd, sd, spec.group_size) if bits == 4 else wq.dense_w8a16_gemm(x, n_out, wd, sd)
@@ -107,7 +113,7 @@ def test_dense_equals_moe_raw_bits():
     need_gpu()
     spec, wts, (wd, sd, _) = setup("w8")
     n_out, K = wts.w1q.shape[1], wts.w1q.shape[2]
-    M = 13  # small-batch kernel, blocks of 16
+    M = 20  # grouped small-batch kernel, blocks of 16 (up to 16 rows a kernel of its own runs)
     toks = gen.make_tokens(spec, M, seed_config=670)
     x = dev_u16(toks.x, spec.act)
     y = wq.dense_w8a16_gemm(x, n_out, wd, sd)

@@ -116,9 +116,122 @@ __global__ __launch_bounds__(NW * 64) void dense_decode_kernel(const uint16_t* _
     }
 }
 
+// ----------------------------------------------------------------------------
+// 5..16 token rows (one 16-row token tile): one workgroup per NWV 16-row weight
+// tiles, one tile per wave, every wave walking all of K.  The tokens of one
+// K chunk (16 rows x KCHUNK channels) are staged once in LDS and shared by the
+// NWV waves (double-buffered, one barrier per chunk): a workgroup covering
+// many weight rows stages the token rows few times, where a workgroup per
+// tile would read them from L2 once per tile.  Each wave keeps PF chunks of
+// its weights in flight; token rows at or beyond M read row M - 1 and their
+// outputs are dropped.  Same numerics as the kernel above; no reduction
+// across waves, the output is rounded once to the activation type.
+constexpr int DS_ROWB = 2 * 128 + 16;  // LDS bytes per token row of one chunk (int4 chunk + pad)
+
+template <int WBITS, bool BF16, int NWV, int PF>
+__global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* __restrict__ x, int M, int K, int N,
+                                                                const uint8_t* __restrict__ w,
+                                                                const uint16_t* __restrict__ s, int groups,
+                                                                uint16_t* __restrict__ y) {
+    constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
+    constexpr int KSTEPS = KCHUNK / 32;
+    constexpr int NT = NWV * 64;
+    constexpr int PIECES = 16 * KCHUNK / 8;  // 16-byte token pieces per chunk
+    static_assert(PIECES <= NT, "one token piece per thread");
+    static_assert(PF % 2 == 0, "chunk parity = slot parity: the token buffers alternate with it");
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * DS_ROWB];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ntiles = N / TILE_ROWS;
+    const int t_raw = NWV * blockIdx.x + wave;
+    const bool tvalid = t_raw < ntiles;
+    const int t = tvalid ? t_raw : ntiles - 1;  // surplus waves stream the last tile and store nothing
+    const int C = K / KCHUNK;
+    const int rowq = 4 * (lane >> 4);
+
+    const uint8_t* wt = w + (size_t)t * C * CHUNK_BYTES + lane * 16;
+    const uint16_t* st = s + (size_t)t * TILE_ROWS + rowq;
+    u32x4 wv[PF];
+    u32x2 sv[PF];
+    auto wload = [&](int c, int slot) {
+        wv[slot] = ldg128_stream(wt + (size_t)c * CHUNK_BYTES);
+        if constexpr (WBITS == 4)
+            sv[slot] = *reinterpret_cast<const u32x2*>(st + (size_t)(groups > 1 ? c : 0) * N);
+    };
+    // token piece of this thread (threads past PIECES reload the last piece)
+    const int q = min(tid, PIECES - 1);
+    const int xr = q / (KCHUNK / 8), xp = q % (KCHUNK / 8);
+    const uint16_t* xsrc = x + (size_t)min(xr, M - 1) * K + 8 * xp;
+    const int xoff = xr * DS_ROWB + 16 * xp;
+    u32x4 xv[2];
+    auto xload = [&](int c, int slot) { xv[slot] = ldg128(xsrc + (size_t)c * KCHUNK); };
+    auto xstore = [&](int slot, int buf) { *reinterpret_cast<u32x4*>(&xs[buf][xoff]) = xv[slot]; };
+
+    const int brow = min(lane & 15, M - 1);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int slot, int buf) {
+        const uint8_t* xb = &xs[buf][brow * DS_ROWB + 16 * (lane >> 4)];
+        if constexpr (WBITS == 4) {
+            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                part = mfma16x16x32<false>(dequant_w4_f16(wv[slot][ks]),
+                                           *reinterpret_cast<const u32x4*>(xb + 64 * ks), part);
+            const uint32_t lo = sv[slot][0], hi = sv[slot][1];
+            acc[0] += part[0] * f16_to_f32((uint16_t)(lo & 0xffffu));
+            acc[1] += part[1] * f16_to_f32((uint16_t)(lo >> 16));
+            acc[2] += part[2] * f16_to_f32((uint16_t)(hi & 0xffffu));
+            acc[3] += part[3] * f16_to_f32((uint16_t)(hi >> 16));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                acc = mfma16x16x32<BF16>(dequant_w8x8<BF16>(wv[slot][2 * ks], wv[slot][2 * ks + 1]),
+                                         *reinterpret_cast<const u32x4*>(xb + 64 * ks), acc);
+        }
+    };
+    // chunk c: store its tokens (loaded one chunk earlier), load chunk c + 2's
+    // tokens, barrier, multiply, refill the weight slot with chunk c + PF.
+    // Every load is unconditional (indices clamp to the last chunk).
+    auto body = [&](int c, auto U) {
+        constexpr int u = decltype(U)::value;
+        xstore(u & 1, u & 1);
+        xload(min(c + 2, C - 1), u & 1);
+        __syncthreads();
+        compute(u, u & 1);
+        wload(min(c + PF, C - 1), u);
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) wload(min(p, C - 1), p);
+    xload(0, 0);
+    xload(min(1, C - 1), 1);
+    int c0 = 0;
+    for (; c0 + PF <= C; c0 += PF) static_for<0, PF>([&](auto U) { body(c0 + decltype(U)::value, U); });
+    static_for<0, PF - 1>([&](auto U) {  // tail of fewer than PF chunks (uniform guard)
+        if (c0 + decltype(U)::value < C) body(c0 + decltype(U)::value, U);
+    });
+
+    const int m = lane & 15;
+    if (tvalid && m < M) {
+        const int n0 = t * TILE_ROWS + rowq;
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            o[r] = acc[r];
+            if constexpr (WBITS == 8) o[r] *= act_to_f32<BF16>(s[n0 + r]);
+        }
+        u32x2 stv;
+        stv[0] = (uint32_t)f32_to_act<BF16>(o[0]) | ((uint32_t)f32_to_act<BF16>(o[1]) << 16);
+        stv[1] = (uint32_t)f32_to_act<BF16>(o[2]) | ((uint32_t)f32_to_act<BF16>(o[3]) << 16);
+        *reinterpret_cast<u32x2*>(y + (size_t)m * N + n0) = stv;
+    }
+}
+
 size_t dense_decode_lds(int M, int K) { return (size_t)M * (2 * (size_t)K + 16); }
 
-bool dense_decode_supported(int M, int K) { return M >= 1 && M <= 4 && dense_decode_lds(M, K) <= 96 * 1024; }
+static bool dense_rows_in_lds(int M, int K) { return M >= 1 && M <= 4 && dense_decode_lds(M, K) <= 96 * 1024; }
+
+bool dense_decode_supported(int M, int K) { return dense_rows_in_lds(M, K) || (M >= 1 && M <= 16); }
 
 template <int WBITS, bool BF16>
 static void launch_dd(const uint16_t* x, int M, int K, int N, const uint8_t* w, const uint16_t* s, int groups,
@@ -132,11 +245,25 @@ static void launch_dd(const uint16_t* x, int M, int K, int N, const uint8_t* w, 
     hipLaunchKernelGGL(kern, dim3(N / TILE_ROWS), dim3(NW * 64), lds, st, x, M, K, N, w, s, groups, y);
 }
 
+template <int WBITS, bool BF16>
+static void launch_ds(const uint16_t* x, int M, int K, int N, const uint8_t* w, const uint16_t* s, int groups,
+                      uint16_t* y, hipStream_t st) {
+    constexpr int NWV = 8, PF = 6;
+    hipLaunchKernelGGL((dense_stream_kernel<WBITS, BF16, NWV, PF>), dim3((N / TILE_ROWS + NWV - 1) / NWV),
+                       dim3(NWV * 64), 0, st, x, M, K, N, w, s, groups, y);
+}
+
 void launch_dense_decode(int wbits, bool bf16, const uint16_t* x, int M, int K, int N, const uint8_t* w,
                          const uint16_t* s, int groups, uint16_t* y, hipStream_t st) {
-    if (wbits == 4) launch_dd<4, false>(x, M, K, N, w, s, groups, y, st);
-    else if (bf16) launch_dd<8, true>(x, M, K, N, w, s, groups, y, st);
-    else launch_dd<8, false>(x, M, K, N, w, s, groups, y, st);
+    if (dense_rows_in_lds(M, K)) {
+        if (wbits == 4) launch_dd<4, false>(x, M, K, N, w, s, groups, y, st);
+        else if (bf16) launch_dd<8, true>(x, M, K, N, w, s, groups, y, st);
+        else launch_dd<8, false>(x, M, K, N, w, s, groups, y, st);
+    } else {
+        if (wbits == 4) launch_ds<4, false>(x, M, K, N, w, s, groups, y, st);
+        else if (bf16) launch_ds<8, true>(x, M, K, N, w, s, groups, y, st);
+        else launch_ds<8, false>(x, M, K, N, w, s, groups, y, st);
+    }
 }
 
 }  // namespace wq
