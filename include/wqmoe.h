@@ -238,7 +238,7 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
  *   d_workspace: dense_gemm_workspace_bytes(M, K, N, act_order) bytes, 256-byte
  *     aligned (the routing arrays, the act-order gather, fp32 partial sums);
  *     0 bytes (NULL allowed) for 1..16 rows without act-order: one
- *     small-batch kernel (1..4 rows staged in LDS whole when they fit 96 KiB,
+ *     small-batch kernel (1..2 rows staged in LDS whole when they fit 96 KiB,
  *     else the tokens of each K chunk staged in LDS and shared by the 8
  *     weight tiles of a workgroup)
  * Limits: int4 K % 128 == 0 and fp16 activations; int8 K % 64 == 0; N % 16 ==

@@ -116,7 +116,7 @@ def test_dense_validation_and_workspace():
     L = wq.load()
     p = C.c_void_p(FAKE)
     assert L.dense_gemm_workspace_bytes(1, 4096, 4096, 0) == 0   # 1..16 rows: one kernel, no workspace
-    assert L.dense_gemm_workspace_bytes(4, 16384, 4096, 0) == 0  # rows too long for LDS: staged per chunk
+    assert L.dense_gemm_workspace_bytes(2, 32768, 4096, 0) == 0  # rows too long for LDS: staged per chunk
     assert L.dense_gemm_workspace_bytes(16, 4096, 4096, 0) == 0
     assert L.dense_gemm_workspace_bytes(1, 4096, 4096, 1) > 0     # act-order gathers through the workspace
     assert L.dense_gemm_workspace_bytes(17, 4096, 4096, 0) >= 17 * 4096 * 4

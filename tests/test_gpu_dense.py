@@ -1,7 +1,7 @@
 """GPU parity of the dense single-expert W4A16 / W8A16 linear layer
 (dense_w4a16_gemm, dense_w8a16_gemm) against the oracle's projection with one
 expert and top-1: every batch regime of the dispatch (the single-kernel paths
-for 1..4 rows staged whole and for 5..16 rows staged per K chunk, the grouped
+for 1..2 rows staged whole and for 3..16 rows staged per K chunk, the grouped
 small-batch kernel up to 24 rows and with act-order, 64-row tiles up to 96,
 128-row tiles above, with a K split for a long K and few outputs), int8
 per-column, int4 group-128, per-column and act-order weights, and output
@@ -84,11 +84,11 @@ def test_dense_long_k_split():
 
 @pytest.mark.parametrize("bits", [4, 8])
 def test_dense_rows_too_long_for_lds(bits):
-    """4 rows of K = 16384 do not fit the LDS whole, so the kernel that stages
+    """2 rows of K = 32768 do not fit the LDS whole, so the kernel that stages
     the tokens of one K chunk at a time runs (still one kernel, no workspace)."""
     need_gpu()
     base = W4 if bits == 4 else W8
-    spec = base.with_(name="dense-longrow-%d" % bits, K=16384, N=64)
+    spec = base.with_(name="dense-longrow-%d" % bits, K=32768, N=64)
     wts = gen.make_moe_weights(spec, seed_config=680 + bits)
     if bits == 4:
         packed, sp, _ = wq.pack_w4(wts.w1q, wts.s1, spec.group_size)
@@ -96,7 +96,7 @@ def test_dense_rows_too_long_for_lds(bits):
         packed, sp = wq.pack_w8(wts.w1q, wts.s1)
     wd, sd = torch.from_numpy(packed).cuda(), torch.from_numpy(sp.view(np.int16)).cuda()
     n_out = wts.w1q.shape[1]
-    M = 4
+    M = 2
     assert wq.dense_gemm_workspace_bytes(M, spec.K, n_out) == 0
     toks = gen.make_tokens(spec, M, seed_config=681)
     x = dev_u16(toks.x, spec.act)

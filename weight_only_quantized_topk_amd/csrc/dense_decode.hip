@@ -1,6 +1,6 @@
 // dense_decode.hip -- the dense single-expert linear layer at small batches.
 //
-// y[m, n] = sum_k x[m, k] W[n, k] for at most 4 token rows (the GEMV end of the
+// y[m, n] = sum_k x[m, k] W[n, k] for 1 or 2 token rows (the GEMV end of the
 // batch-size dispatch of "[WIP] AWQ Faster Kernels", vLLM issue 3289).  The
 // weights are the packed layout of the grouped GEMM with one expert: a 1 KiB
 // chunk of a 16-row tile gives every lane the A operand of 2 (int8) or 4
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void dense_decode_kernel(const uint16_t* _
 }
 
 // ----------------------------------------------------------------------------
-// 5..16 token rows (one 16-row token tile): one workgroup per NWV 16-row weight
+// 3..16 token rows (one 16-row token tile): one workgroup per NWV 16-row weight
 // tiles, one tile per wave, every wave walking all of K.  The tokens of one
 // K chunk (16 rows x KCHUNK channels) are staged once in LDS and shared by the
 // NWV waves (double-buffered, one barrier per chunk): a workgroup covering
@@ -229,7 +229,10 @@ __global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* 
 
 size_t dense_decode_lds(int M, int K) { return (size_t)M * (2 * (size_t)K + 16); }
 
-static bool dense_rows_in_lds(int M, int K) { return M >= 1 && M <= 4 && dense_decode_lds(M, K) <= 96 * 1024; }
+// rows staged whole for 1 or 2 rows; from 3 rows the chunk-streaming kernel
+// is the faster one (Yi-34B shape int4: M = 1 19.6 / 28.3 us, M = 2 23.6 /
+// 28.7 us, M = 4 34.0 / 29.1 us whole-row / chunk-streaming)
+static bool dense_rows_in_lds(int M, int K) { return M >= 1 && M <= 2 && dense_decode_lds(M, K) <= 96 * 1024; }
 
 bool dense_decode_supported(int M, int K) { return dense_rows_in_lds(M, K) || (M >= 1 && M <= 16); }
 
