@@ -1,10 +1,11 @@
 """GPU parity of the grouped GEMM for batches of at most 4 tokens (the kernel
 that stages a block's token rows in LDS): the DOWN stage with a long reduction
 (64 or more 1 KiB chunks per weight tile) in 4, 2 or 1 K slices, int4 group-128,
-int4 per-column and int8 weights; the int4 GATE_UP / RAW stage of one token,
-with and without act-order (the permutation applied while staging); and a
-token's top-k naming one expert more than once (more rows than the LDS holds,
-and more than one block per expert), against the oracle.  Float comparisons:
+int4 per-column and int8 weights; the int4 RAW stage of one token, with and
+without act-order (the permutation applied while staging); the int4 GATE_UP
+stage of one token (which runs the small-batch kernel after the gather); and
+a token's top-k naming one expert more than once (more rows than the LDS
+holds, and more than one block per expert), against the oracle.  Float comparisons:
 relative Frobenius error <= 5e-3 and max abs error <= 3e-2 * max |ref|; the
 RAW stage on exact-integer inputs bit for bit."""
 import numpy as np
@@ -155,8 +156,7 @@ def test_gate_up_one_token(key, bs):
 
 @pytest.mark.parametrize("key", ["w4g", "w4gao"])
 def test_gate_up_one_token_repeated_expert(key):
-    """One token whose top-2 names expert 3 twice: two rows for a one-row LDS,
-    multiplied in two passes."""
+    """One token whose top-2 names expert 3 twice: two rows of one expert."""
     need_gpu()
     spec, wts, p = setup(key)
     toks = gen.make_tokens(spec, 1, seed_config=1180)
@@ -165,10 +165,13 @@ def test_gate_up_one_token_repeated_expert(key):
     check_gate_up(spec, wts, p, toks.x_f32(), ids, 16, "%s repeated expert" % key)
 
 
+@pytest.mark.parametrize("pair", [(6, 1), (3, 3)])
 @pytest.mark.parametrize("act_order", [False, True])
-def test_raw_exact_integer_one_token(act_order):
+def test_raw_exact_integer_one_token(act_order, pair):
     """Power-of-two group scales and x in {-1, 0, 1}: the RAW projection of
-    one token is bit-exact (every partial sum is a dyadic number below 2^24)."""
+    one token is bit-exact (every partial sum is a dyadic number below 2^24);
+    with expert 3 named twice, two rows for a one-row LDS, multiplied in two
+    passes."""
     need_gpu()
     spec = W4GAO if act_order else W4G
     wts = gen.make_moe_weights(spec, seed_config=1190)
@@ -178,7 +181,7 @@ def test_raw_exact_integer_one_token(act_order):
     pow2 = np.array([0.25, 0.5, 1.0, 2.0], np.float32)[rng.integers(0, 4, size=(E, G, n_out))]
     s_bits = gen.round_to(spec.act, pow2)
     x = rng.integers(-1, 2, size=(1, K)).astype(np.float32)
-    ids = np.array([[6, 1]], np.int32)
+    ids = np.array([pair], np.int32)
     ref, _ = oracle.moe_up(x, ids, wts.w1q, pow2, wts.g1, want_gu=True)
     packed, sp, kp = wq.pack_w4(wts.w1q, s_bits, spec.group_size, g_idx=wts.g1)
     st, ex, nt, cap = align_dev(ids, E, 16)
@@ -186,7 +189,7 @@ def test_raw_exact_integer_one_token(act_order):
     kpd = torch.from_numpy(kp).cuda() if kp is not None else None
     ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_RAW, 1, 2, E, n_out, K, cap, kp is not None)
     work = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
-    say("tiny raw exact", act_order)
+    say("tiny raw exact", act_order, pair)
     wq.moe_w4a16_gemm(wq.WQ_STAGE_RAW, dev_u16(gen.round_to(spec.act, x), spec.act), 1, 2, E, n_out, K,
                       torch.from_numpy(packed).cuda(), torch.from_numpy(sp.view(np.int16)).cuda(), spec.group_size,
                       kpd, st, ex, nt, cap, 16, None, out, work)

@@ -293,11 +293,12 @@ static int launch_tiny_s(const GemmArgs& g, const int32_t* perm, int max_ks, hip
 }
 
 // Where it is used: DOWN with a long reduction (>= 64 chunks per tile) up to
-// 4 tokens, where it beats the small-batch kernel; GATE_UP / RAW of int4
-// weights for one token, where staging through the act-order permutation
-// replaces the gather kernel (39.3 -> 36.7 us for the pair measured alone,
-// equal time inside the layer).  Many-expert layers with short rows (K = 1536)
-// and int8 GATE_UP gain nothing.
+// 4 tokens, where it beats the small-batch kernel; the RAW stage of int4
+// weights for one token (staging through the act-order permutation in place
+// of the gather kernel).  GATE_UP of one token now runs faster on the
+// small-batch kernel after the gather (Mixtral act-order int4 layer 68.2 ->
+// 67.0 us, equal without act-order).  Many-expert layers with short rows
+// (K = 1536) and int8 GATE_UP gain nothing.
 bool tiny_supported(int wbits, int stage, int M, int k_in, int groups, int max_ks) {
     if (M < 1 || M > TINY_MAX_ROWS) return false;
     const int c = k_in / (wbits == 4 ? WFmt<4>::KCHUNK : WFmt<8>::KCHUNK);
@@ -305,7 +306,7 @@ bool tiny_supported(int wbits, int stage, int M, int k_in, int groups, int max_k
     if (stage == STAGE_DOWN) {
         if (c < 64) return false;
         ks = tiny_down_split(wbits, k_in, max_ks);
-    } else if (wbits != 4 || M != 1) {
+    } else if (stage != STAGE_RAW || wbits != 4 || M != 1) {
         return false;
     }
     return tiny_lds(wbits, M, k_in, groups, 2, 4, ks) <= 96 * 1024;
