@@ -293,6 +293,9 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
 // waves with 2 or 4 row tiles, a long one 8 waves; int4 (half the bytes per
 // weight, so half the work per wave) takes two gate/up tile pairs per
 // workgroup, and four row tiles in DOWN once that grid still fills the GPU.
+// The int4 gate/up of one or two tokens (at most 4 pairs) splits K over 2
+// waves instead of 4 (Mixtral act-order layer M = 1: 66.6 -> 65.3 us; 4 and
+// 16 tokens measured slower that way).
 // A single expert (the dense linear layer: the grid is one expert's tiles)
 // takes 4 row tiles on 4 waves for int4 and 2 on 2 waves for int8 (7168 ->
 // 20480, 16 tokens: int4 47.9 -> 32.5 us, int8 42.7 -> 39.3 us).
@@ -321,7 +324,8 @@ static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
         // on 2 waves (DeepSeek-V2 shape M = 64: 93.7 -> 85.1 us)
         launch_decode_cfg<WBITS, BF16, STAGE, 2, 4, 2, 2>(g, s);
     } else if (T <= 16 || rows <= 8) {
-        if (GU && WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 2>(g, s);
+        if (GU && WBITS == 4 && np2_ok && T <= 4) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 2, 2>(g, s);
+        else if (GU && WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 4, 2>(g, s);
         else if (GU) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 4, 2>(g, s);
         else if (!np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 1, 8, 4>(g, s);
         else if (g.E == 1 && WBITS == 4 && np4_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, 4, 4, 2>(g, s);
