@@ -1,7 +1,9 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the
 benchmark times (block size chosen by the batch-size heuristic).  Routing and
 the padded sort are compared bit for bit over the whole batch; the layer
-output on sampled rows, which the oracle computes one by one."""
+output on sampled rows, which the oracle computes one by one.  The benchmark's
+other rows at the 2:4 layer's shape -- 8-bit kept codes and the dense int4
+linear layer -- likewise."""
 import numpy as np
 import pytest
 
@@ -85,3 +87,58 @@ def test_config_sparse24(M):
     rows = sample_rows(M, n=4, seed=400 + M)
     ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128, rows=rows)
     assert_close_fp(host_f32(y)[rows], ref, "cfg4 M=%d" % M)
+
+
+@pytest.mark.parametrize("M", gen.CFG4.m_sweep)
+def test_config_sparse24_8bit(M):
+    """The 2:4 layer of the Yi-34B MLP shape with 8-bit kept codes (the 2:4
+    support's 8-bit variant), at the benchmark's batch sizes, sampled rows."""
+    need_gpu()
+    spec = gen.CFG4.with_(bits=8)
+    if "w8" not in _sparse:
+        _sparse.clear()
+        _cache.clear()
+        torch.cuda.empty_cache()
+        say("generating and packing config 4, 8-bit codes")
+        sw = gen.make_sparse_weights(spec)
+        vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, bits=8)
+        _sparse["w8"] = (sw, torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(),
+                         torch.from_numpy(sp.view(np.int16)).cuda())
+    sw, vd, md, sd = _sparse["w8"]
+    x = gen.make_sparse_x(spec, M)
+    say("config 4 8-bit M", M)
+    y = wq.sparse24_w8a16_gemm(dev_u16(x, "f16"), vd, md, sd, spec.N)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, n=4, seed=450 + M)
+    ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128, rows=rows)
+    assert_close_fp(host_f32(y)[rows], ref, "cfg4 8-bit M=%d" % M)
+
+
+_dense = {}
+
+
+@pytest.mark.parametrize("M", gen.CFG4.m_sweep)
+def test_config_dense_w4(M):
+    """The dense int4 linear layer of the same shape (K = 7168 -> 20480, group
+    128), the 2:4 layer's dense counterpart, at the benchmark's batch sizes:
+    every regime of its dispatch, sampled rows against the oracle."""
+    need_gpu()
+    spec = gen.CFG3.with_(name="yi34b-dense-w4", E=1, topk=1, K=gen.CFG4.K, N=gen.CFG4.N // 2, act_order=False)
+    if "w" not in _dense:
+        _sparse.clear()
+        _cache.clear()
+        torch.cuda.empty_cache()
+        say("generating and packing the dense int4 layer")
+        wts = gen.make_moe_weights(spec, seed_config=460)
+        packed, sp, _ = wq.pack_w4(wts.w1q, wts.s1, spec.group_size)
+        _dense["w"] = (wts, torch.from_numpy(packed).cuda(), torch.from_numpy(sp.view(np.int16)).cuda())
+    wts, wd, sd = _dense["w"]
+    n_out = wts.w1q.shape[1]
+    toks = gen.make_tokens(spec, M, seed_config=461)
+    say("dense int4 M", M)
+    y = wq.dense_w4a16_gemm(dev_u16(toks.x, spec.act), n_out, wd, sd, spec.group_size)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, n=4, seed=470 + M)
+    ref, _ = oracle.moe_up(toks.x_f32()[rows], np.zeros((rows.size, 1), np.int32), wts.w1q, wts.s1_f32(), None,
+                           want_gu=True)
+    assert_close_fp(host_f32(y)[rows], ref, "dense int4 Yi-34B shape M=%d" % M)
