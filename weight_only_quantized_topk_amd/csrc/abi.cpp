@@ -434,8 +434,10 @@ struct DenseLayout {
     size_t cap, off_sorted, off_eids, off_ntpp, off_w, off_a1, off_y, total;
 };
 
-// batch-size dispatch: the small-batch kernel (blocks of 16 rows) up to 24
-// rows, the large-batch kernel with 64-row tiles up to 96, 128-row tiles above
+// batch-size dispatch of the grouped path (above 16 rows, or with act-order;
+// up to 16 rows without act-order one dense kernel runs, no workspace): the
+// small-batch kernel (blocks of 16 rows) up to 24 rows, the large-batch kernel
+// with 64-row tiles up to 96, 128-row tiles above
 int dense_block_size(int M, int N, int K) {
     const int bs = M <= 24 ? 16 : (M <= 96 ? 64 : 128);
     return (bs == 16 || wq::prefill_supported(N, K, bs)) ? bs : 16;
