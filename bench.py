@@ -482,7 +482,9 @@ def main(argv=None):
         cpu = cpu_baseline(spec, wts_cpu, toks, args.cpu_seconds)
 
     res = {
-        "metric": "fused-MoE W%dA16 tokens/s" % spec.bits,
+        # the headline metric: layer tokens/s; the HBM GB/s (M <= 64) and
+        # TFLOP/s (M >= 1024) figures are in "roofline", "sweep" and "rows"
+        "metric": "fused-MoE W4/W8A16 tokens/s; HBM GB/s at M\u226464, TFLOP/s at M\u22651024",
         "value": round(head["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
