@@ -227,10 +227,11 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
  * integration", nm-vllm PR 266, review thread: the MoE file compared against
  * csrc/quantization/gptq_marlin/gptq_marlin.cu -- and the GEMV/GEMM mix picked
  * by batch-size heuristics of "[WIP] AWQ Faster Kernels", vLLM issue 3289).
- * 1..4 rows run one small-batch (GEMV-like) kernel; beyond that the grouped
- * GEMM of this library with one expert and top-1: up to 24 rows the
- * small-batch kernel, up to 96 the large-batch kernel with 64-row tiles, above
- * that 128-row tiles; fp32 accumulation, rounded once to the activation type.
+ * 1..16 rows without act-order run one small-batch (GEMV-like) kernel; beyond
+ * that (or with act-order) the grouped GEMM of this library with one expert and
+ * top-1: up to 24 rows the small-batch kernel, up to 192 the large-batch kernel
+ * with 64-row tiles, above that 128-row tiles; fp32 accumulation, rounded once
+ * to the activation type.
  *   d_x [M, K] act dtype; d_y [M, N] act dtype
  *   d_w_packed, d_scales: wq_pack_w4 / wq_pack_w8 output for E = 1, n_out = N,
  *     k_in = K (no gate/up interleave); int4 group_size 128 or -1, int8 -1

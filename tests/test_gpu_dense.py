@@ -2,7 +2,7 @@
 (dense_w4a16_gemm, dense_w8a16_gemm) against the oracle's projection with one
 expert and top-1: every batch regime of the dispatch (the single-kernel paths
 for 1..2 rows staged whole and for 3..16 rows staged per K chunk, the grouped
-small-batch kernel up to 24 rows and with act-order, 64-row tiles up to 96,
+small-batch kernel up to 24 rows and with act-order, 64-row tiles up to 192,
 128-row tiles above, with a K split for a long K and few outputs), int8
 per-column, int4 group-128, per-column and act-order weights, and output
 counts that leave the last 8-tile workgroup partial.  Relative
@@ -48,7 +48,7 @@ def setup(key):
 
 
 @pytest.mark.parametrize("key", ["w8", "w4", "w4ao", "w4pc", "w8rag", "w4rag"])
-@pytest.mark.parametrize("M", [1, 2, 4, 5, 13, 16, 40, 300])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 13, 16, 40, 150, 300])
 def test_dense_matches_oracle(key, M):
     need_gpu()
     spec, wts, (wd, sd, kd) = setup(key)
