@@ -404,8 +404,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU (one MI355X per box); --gpus %d is not supported. "
-              "Expert- or tensor-parallel sharding is described in the design notes but not run." % args.gpus,
+        print("bench.py: the benchmark runs on one GPU; --gpus %d is not supported (the layer is not sharded "
+              "across GPUs: expert- or tensor-parallel sharding is a design, not code)." % args.gpus,
               file=sys.stderr)
         return 2
 

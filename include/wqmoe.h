@@ -52,7 +52,7 @@ extern "C" {
 typedef int wq_status;
 #define WQ_OK 0
 #define WQ_ERR_INVALID 1      /* null pointer, bad size, capacity/workspace too small, misaligned */
-#define WQ_ERR_UNSUPPORTED 2  /* a valid request this build does not implement (dtype, group size, shape) */
+#define WQ_ERR_UNSUPPORTED 2  /* a valid request the library does not implement (dtype, group size, shape) */
 #define WQ_ERR_DEVICE 3       /* a device pointer that is not on the current device */
 #define WQ_ERR_HIP 4          /* the HIP runtime reported an error at launch */
 
