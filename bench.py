@@ -65,8 +65,9 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     """sha256 over the large-batch kernel's sources: gemm_prefill.hip,
-    common.hpp, and from launch.hpp the kernel-argument struct and the stage
-    constants (the rest of that header declares other kernels)."""
+    common.hpp, from launch.hpp the kernel-argument struct and the stage
+    constants (the rest of that header declares other kernels), and the
+    compiler flags of gemm_prefill.hip (the include path left out)."""
     csrc = os.path.join(ROOT, "weight_only_quantized_topk_amd", "csrc")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -76,6 +77,8 @@ def kernel_source_hash() -> str:
         text = fh.read()
     for part in re.findall(r"constexpr int STAGE_\w+ = \d+;", text) + re.findall(r"struct GemmArgs \{.*?\n\};", text, re.S):
         h.update(part.encode())
+    from weight_only_quantized_topk_amd import build as _build
+    h.update(" ".join(_build.FLAGS[:-2] + _build.SOURCE_FLAGS.get("gemm_prefill.hip", [])).encode())
     return h.hexdigest()
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwqmoe.so")
-SOURCES = ["abi.cpp", "route_align.hip", "gemm_decode.hip", "gemm_prefill.hip", "sparse24.hip", "quant.hip", "dense_decode.hip", "gemm_tiny.hip"]
+SOURCES = ["abi.cpp", "route_align.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_n256.hip", "sparse24.hip", "quant.hip", "dense_decode.hip", "gemm_tiny.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,11 +27,17 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# per-source flags.  The large-batch GEMM is scheduled by LLVM's iterative
+# ILP strategy: measured on MI355X, its gate/up launches run 1-2 % faster
+# than under the default scheduler (Mixtral int8 M=1024 0.485 -> 0.478 ms,
+# int4 act-order M=4096 1.77 -> 1.75 ms), with no register spills except in
+# the 256 x 128 shape, which gemm_prefill_n256.hip builds under the default one
+SOURCE_FLAGS = {"gemm_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(line for line in (r.stdout + r.stderr).splitlines() if noise not in line)

@@ -300,6 +300,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
     }
 }
 
+template <int WBITS, bool BF16, int STAGE, int NW, int RT, int BM, int OCC>
+static void launch_prefill_cfg(const GemmArgs& g, int ksplit, hipStream_t s) {
+    const dim3 grid(g.n_out / (NW * RT * 16), g.cap / BM, ksplit);
+    hipLaunchKernelGGL((gemm_prefill_kernel<WBITS, BF16, STAGE, NW, RT, BM, OCC>), grid, dim3(NW * 64), 0, s, g);
+}
+
+// The 256 x 128 shape for int8 weights, built in a translation unit of its own
+// (gemm_prefill_n256.hip, which includes this file with
+// WQ_PREFILL_KERNEL_ONLY defined) under the default instruction scheduler;
+// this file's kernels are built under LLVM's iterative ILP scheduler, which
+// spills that shape's registers.
+template <int WBITS, bool BF16, int STAGE>
+void launch_prefill_n256(const GemmArgs& g, int ksplit, hipStream_t s);
+
+#ifndef WQ_PREFILL_KERNEL_ONLY
 // ------------------------------------------------------------------ plans
 // Workgroup shapes (weight rows x token rows, waves, workgroups per CU):
 //   N512  512 x 128, 8 waves, 1 per CU
@@ -362,17 +377,14 @@ int prefill_down_split_max(int T, int E, int n_out, int k_in) {
     return std::max(prefill_down_split(T, E, n_out, k_in, 64), prefill_down_split(T, E, n_out, k_in, 128));
 }
 
-template <int WBITS, bool BF16, int STAGE, int NW, int RT, int BM, int OCC>
-static void launch_prefill_cfg(const GemmArgs& g, int ksplit, hipStream_t s) {
-    const dim3 grid(g.n_out / (NW * RT * 16), g.cap / BM, ksplit);
-    hipLaunchKernelGGL((gemm_prefill_kernel<WBITS, BF16, STAGE, NW, RT, BM, OCC>), grid, dim3(NW * 64), 0, s, g);
-}
-
 template <int WBITS, bool BF16, int STAGE>
 static void launch_prefill_shape(PrefillShape sh, const GemmArgs& g, int ksplit, hipStream_t s) {
     switch (sh) {
         case PF_N512: launch_prefill_cfg<WBITS, BF16, STAGE, 8, 4, 128, 1>(g, ksplit, s); break;
-        case PF_N256: launch_prefill_cfg<WBITS, BF16, STAGE, 4, 4, 128, 2>(g, ksplit, s); break;
+        case PF_N256:  // int8 only
+            if constexpr (WBITS == 8) launch_prefill_n256<WBITS, BF16, STAGE>(g, ksplit, s);
+            else launch_prefill_cfg<WBITS, BF16, STAGE, 4, 2, 128, 3>(g, ksplit, s);
+            break;
         case PF_N128: launch_prefill_cfg<WBITS, BF16, STAGE, 4, 2, 128, 3>(g, ksplit, s); break;
         case PF_T256: launch_prefill_cfg<WBITS, BF16, STAGE, 4, 4, 64, 2>(g, ksplit, s); break;
         default: launch_prefill_cfg<WBITS, BF16, STAGE, 4, 2, 64, 3>(g, ksplit, s); break;
@@ -401,5 +413,6 @@ int launch_gemm_prefill(int wbits, bool bf16, int stage, const GemmArgs& g, hipS
     else launch_prefill_s<8, false>(stage, g, ksplit, s);
     return ksplit;
 }
+#endif  // WQ_PREFILL_KERNEL_ONLY
 
 }  // namespace wq
