@@ -171,11 +171,46 @@ class Timer:
         return spans, wall
 
 
+def host_cpu():
+    """(CPU model name, physical cores, logical CPUs) of this host, from
+    /proc/cpuinfo (physical cores = distinct (physical id, core id) pairs)."""
+    model, cores, logical = "unknown", set(), 0
+    try:
+        phys = core = None
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "processor":
+                    logical += 1
+                elif k == "model name" and model == "unknown":
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return model, (len(cores) or None), (logical or os.cpu_count())
+
+
 def cpu_baseline(spec, wts, toks, seconds):
     """The oracle, as it stands, on the first n tokens of the same batch (route +
-    layer for those tokens), n chosen so the run takes about `seconds`."""
+    layer for those tokens), n chosen so the run takes about `seconds`.  It is
+    compiled here with -O3 -march=native (same arithmetic as the test build) and
+    runs OpenMP on OMP_NUM_THREADS threads (else one per logical CPU)."""
+    import tempfile
+
     import oracle
+    build_dir = tempfile.mkdtemp(prefix="wq_oracle_")
+    oracle.use_native_build(build_dir)
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    model, phys_cores, logical = host_cpu()
     x = toks.x_f32()
     s1, s2 = wts.s1_f32(), wts.s2_f32()
 
@@ -191,7 +226,9 @@ def cpu_baseline(spec, wts, toks, seconds):
     dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "route + layer for the first %d of the %d tokens of the timed batch, %.1f s, fp64 "
-                      "accumulation, OpenMP over (token, slot, output row)" % (n, toks.M, dt)}
+                      "accumulation, OpenMP over (token, slot, output row)" % (n, toks.M, dt),
+            "cpu_model": model, "physical_cores": phys_cores, "logical_cpus": logical,
+            "build": "gcc " + " ".join(oracle.NATIVE_FLAGS[:2] + ["-ffp-contract=off", "-fopenmp"])}
 
 
 def measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup):

@@ -22,25 +22,45 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
+_lib_path = _LIB
+
+# No fast-math and no FMA contraction: every sum is the plain sequence of
+# double additions in ascending order, whatever the optimisation level, so
+# results do not depend on the host CPU or on these flags.
+_COMMON_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-std=c11", "-Wall", "-Wextra", "-shared",
+                 "-fPIC"]
+# the build the tests load: portable code (it may run on another machine than the one that built it)
+PORTABLE_FLAGS = ["-O2"] + _COMMON_FLAGS
+# the build the CPU baseline times, compiled on the machine it runs on
+NATIVE_FLAGS = ["-O3", "-march=native"] + _COMMON_FLAGS
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FMA
-    contraction, so results do not depend on the host CPU)."""
+    """Compile oracle.c into liboracle.so (gcc, PORTABLE_FLAGS)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-std=c11",
-                               "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc"] + PORTABLE_FLAGS + [_SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def use_native_build(out_dir: str) -> str:
+    """Compile oracle.c with NATIVE_FLAGS (-O3 -march=native) into out_dir and
+    make this process's oracle calls use that build.  For timing the oracle
+    as a CPU baseline on the host it runs on; the arithmetic is the same."""
+    global _lib, _lib_path
+    path = os.path.join(out_dir, "liboracle_native.so")
+    subprocess.check_call(["gcc"] + NATIVE_FLAGS + [_SRC, "-o", path, "-lm"])
+    _lib, _lib_path = None, path
+    return path
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _lib_path == _LIB and not os.path.exists(_LIB):
             build()
-        L = C.CDLL(_LIB)
+        L = C.CDLL(_lib_path)
         i64, i32, p = C.c_int64, C.c_int, C.c_void_p
         L.orc_route.argtypes = [p, i64, i32, i32, i32, p, p]
         L.orc_align_capacity.argtypes = [i64, i32, i32]

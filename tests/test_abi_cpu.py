@@ -133,6 +133,10 @@ def test_dense_validation_and_workspace():
     assert _status("dense_w4a16_gemm", *a4(M=-1))[0] == wq.WQ_ERR_INVALID
     assert _status("dense_w4a16_gemm", *a4(x=None))[0] == wq.WQ_ERR_INVALID
     assert _status("dense_w4a16_gemm", *a4(M=0, ws=0))[0] == wq.WQ_OK
+    # the act-order permutation is checked like every other pointer (the gather reads it 16 bytes at a time)
+    a4p = lambda kp: [p, 40, 512, 256, p, p, 128, kp, p, wq.WQ_F16, p, 1 << 30, None]
+    st, msg = _status("dense_w4a16_gemm", *a4p(C.c_void_p(FAKE + 4)))
+    assert st == wq.WQ_ERR_INVALID and "k_perm" in msg
     a8 = lambda **k: [p, 4, k.get("K", 512), 256, p, p, p, wq.WQ_BF16, p, 1 << 30, None]
     assert _status("dense_w8a16_gemm", *a8(K=96))[0] == wq.WQ_ERR_UNSUPPORTED       # K % 64
 

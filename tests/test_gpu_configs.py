@@ -1,9 +1,17 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the
 benchmark times (block size chosen by the batch-size heuristic).  Routing and
-the padded sort are compared bit for bit over the whole batch; the layer
-output on sampled rows, which the oracle computes one by one.  The benchmark's
-other rows at the 2:4 layer's shape -- 8-bit kept codes and the dense int4
-linear layer -- likewise."""
+the padded sort are compared bit for bit over the whole batch (routing weights
+exactly, with at most one weight in 10^4 allowed one ulp: the device and host
+double exp may differ in their last bit).  The layer output is compared over
+the whole tensor wherever the oracle takes about a minute or less (the tiny
+layer, every Mixtral int8 batch up to 1024 tokens, the act-order int4 layer
+up to 256 tokens, the DeepSeek-V2-shaped layer at 64 tokens); at 4096 tokens
+over a contiguous run of 128 tokens plus every token that has a pair in some
+expert's last, partly filled token tile (the ragged edge of each expert's
+rows), plus the first and last token.  The benchmark's other rows at the 2:4
+layer's shape -- 8-bit kept codes and the dense int4 linear layer -- likewise:
+whole tensor up to 128 tokens, at 1024 tokens the first, last and one seeded
+run of 128 rows."""
 import numpy as np
 import pytest
 
@@ -14,6 +22,10 @@ from tests.gpu_common import dev_u16, host_f32, need_gpu, say, torch, ulp_diff_f
 from tests.helpers import assert_close_fp
 
 pytestmark = pytest.mark.gpu
+
+# largest batch compared over the whole output tensor, per workload
+FULL_MAX = {1: 16, 2: 1024, 3: 256, 5: 64}
+RUN = 128  # contiguous run of tokens compared in the sampled cases
 
 _cache = {}
 
@@ -31,17 +43,39 @@ def packed_config(cid):
     return _cache[cid]
 
 
-def sample_rows(M, n=6, seed=0):
-    if M <= n:
+def run_rows(M, seed, run=RUN):
+    """First and last row plus one contiguous run of `run` rows at a seeded offset."""
+    if M <= run:
         return np.arange(M)
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, n - 2, replace=False)]))
+    r0 = int(np.random.default_rng(seed).integers(1, M - run))
+    return np.unique(np.concatenate([[0, M - 1], np.arange(r0, r0 + run)]))
+
+
+def ragged_tile_tokens(st, ex, nt, T, topk, bs):
+    """Tokens with a pair in the last token tile of an expert when that tile is
+    only partly filled.  Tiles are the kernels' row tiles: 16 rows for the
+    small-batch kernel (block 16 / 32), else min(block, 128)."""
+    tile = 16 if bs < 64 else min(bs, 128)
+    toks = set()
+    for b0 in range(0, nt, bs):
+        e = ex[b0 // bs]
+        if b0 + bs < nt and ex[(b0 + bs) // bs] == e:
+            continue  # not the expert's last block
+        valid = np.nonzero(st[b0:b0 + bs] < T)[0]
+        if valid.size == 0:
+            continue
+        last = b0 + int(valid[-1])
+        t0 = last - (last - b0) % tile
+        if last - t0 + 1 < tile:
+            toks.update((st[t0:last + 1] // topk).tolist())
+    return toks
 
 
 CASES = [(cid, M) for cid in (1, 2, 3, 5) for M in gen.CONFIGS[cid].m_sweep]
 
 
 @pytest.mark.parametrize("cid,M", CASES)
+@pytest.mark.timeout(900)
 def test_config_layer(cid, M):
     need_gpu()
     spec, wts, p = packed_config(cid)
@@ -52,16 +86,24 @@ def test_config_layer(cid, M):
     torch.cuda.synchronize()
     w_ref, ids_ref = oracle.route(toks.logits, spec.topk, spec.renormalize)
     assert np.array_equal(aux["topk_ids"].cpu().numpy(), ids_ref)
-    assert ulp_diff_f32(aux["topk_weights"].cpu().numpy(), w_ref).max() <= 1
+    w_got = aux["topk_weights"].cpu().numpy()
+    ud = ulp_diff_f32(w_got, w_ref)
+    assert ud.max() <= 1
+    assert int((ud > 0).sum()) <= max(1, w_ref.size // 10000), "%d routing weights differ" % int((ud > 0).sum())
     bs = aux["block_size"]
     st_ref, ex_ref, nt_ref = oracle.align(ids_ref, spec.E, bs)
     assert int(aux["num_tokens_post_padded"].cpu()[0]) == nt_ref
     assert np.array_equal(aux["sorted_token_ids"].cpu().numpy()[:st_ref.size], st_ref)
     assert np.array_equal(aux["expert_ids"].cpu().numpy()[:ex_ref.size], ex_ref)
-    rows = sample_rows(M, seed=cid * 100 + M)
-    ref = oracle.moe_layer_from_weights(wts, toks.x_f32(), aux["topk_weights"].cpu().numpy(), ids_ref,
-                                        rows=rows)["out"]
-    assert_close_fp(host_f32(out)[rows], ref, "cfg%d M=%d (rows %s)" % (cid, M, rows.tolist()))
+    if M <= FULL_MAX[cid]:
+        rows = np.arange(M)
+    else:
+        ragged = ragged_tile_tokens(st_ref, ex_ref, nt_ref, M * spec.topk, spec.topk, bs)
+        rows = np.unique(np.concatenate([run_rows(M, seed=cid * 100 + M), np.array(sorted(ragged), np.int64)]))
+    say("  oracle over %d of %d tokens" % (rows.size, M))
+    ref = oracle.moe_layer_from_weights(wts, toks.x_f32(), w_got, ids_ref, rows=rows)["out"]
+    what = "cfg%d M=%d (%s)" % (cid, M, "all tokens" if rows.size == M else "%d tokens" % rows.size)
+    assert_close_fp(host_f32(out)[rows], ref, what)
 
 
 _sparse = {}
@@ -84,7 +126,7 @@ def test_config_sparse24(M):
     say("config 4 M", M)
     y = wq.sparse24_w4a16_gemm(dev_u16(x, "f16"), vd, md, sd, spec.N)
     torch.cuda.synchronize()
-    rows = sample_rows(M, n=4, seed=400 + M)
+    rows = run_rows(M, seed=400 + M)
     ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128, rows=rows)
     assert_close_fp(host_f32(y)[rows], ref, "cfg4 M=%d" % M)
 
@@ -92,7 +134,7 @@ def test_config_sparse24(M):
 @pytest.mark.parametrize("M", gen.CFG4.m_sweep)
 def test_config_sparse24_8bit(M):
     """The 2:4 layer of the Yi-34B MLP shape with 8-bit kept codes (the 2:4
-    support's 8-bit variant), at the benchmark's batch sizes, sampled rows."""
+    support's 8-bit variant), at the benchmark's batch sizes."""
     need_gpu()
     spec = gen.CFG4.with_(bits=8)
     if "w8" not in _sparse:
@@ -109,7 +151,7 @@ def test_config_sparse24_8bit(M):
     say("config 4 8-bit M", M)
     y = wq.sparse24_w8a16_gemm(dev_u16(x, "f16"), vd, md, sd, spec.N)
     torch.cuda.synchronize()
-    rows = sample_rows(M, n=4, seed=450 + M)
+    rows = run_rows(M, seed=450 + M)
     ref = oracle.sparse24(gen.bits_to_f32("f16", x), sw.vals, sw.idx, sw.s_f32(), 128, rows=rows)
     assert_close_fp(host_f32(y)[rows], ref, "cfg4 8-bit M=%d" % M)
 
@@ -121,7 +163,7 @@ _dense = {}
 def test_config_dense_w4(M):
     """The dense int4 linear layer of the same shape (K = 7168 -> 20480, group
     128), the 2:4 layer's dense counterpart, at the benchmark's batch sizes:
-    every regime of its dispatch, sampled rows against the oracle."""
+    every regime of its dispatch, against the oracle."""
     need_gpu()
     spec = gen.CFG3.with_(name="yi34b-dense-w4", E=1, topk=1, K=gen.CFG4.K, N=gen.CFG4.N // 2, act_order=False)
     if "w" not in _dense:
@@ -138,7 +180,7 @@ def test_config_dense_w4(M):
     say("dense int4 M", M)
     y = wq.dense_w4a16_gemm(dev_u16(toks.x, spec.act), n_out, wd, sd, spec.group_size)
     torch.cuda.synchronize()
-    rows = sample_rows(M, n=4, seed=470 + M)
+    rows = run_rows(M, seed=470 + M)
     ref, _ = oracle.moe_up(toks.x_f32()[rows], np.zeros((rows.size, 1), np.int32), wts.w1q, wts.s1_f32(), None,
                            want_gu=True)
     assert_close_fp(host_f32(y)[rows], ref, "dense int4 Yi-34B shape M=%d" % M)

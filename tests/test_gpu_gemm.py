@@ -1,6 +1,8 @@
 """GPU parity of the grouped GEMMs, stage by stage and as a whole layer, on
 shapes that span several tiles with ragged token counts, on both kernels
-(small-batch block 16, large-batch block 128):
+(small-batch blocks of 16 and 32, large-batch blocks of 64, 128 and 256 --
+the last with batches small enough that the second 128-row half of a block is
+padding only):
   - RAW stage, exact-integer case: the fp32 projection equals the oracle's bit
     for bit (all partial sums are dyadic numbers below 2^24);
   - GATE_UP: H against the oracle's silu(gate) * up;
@@ -172,7 +174,7 @@ def h_perm(spec, wts, e):
 
 
 @pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e", "w4k", "w8k"])
-@pytest.mark.parametrize("bs", [16, 64, 128])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_gate_up(key, bs, M):
     need_gpu()
@@ -199,7 +201,7 @@ def test_gate_up(key, bs, M):
 
 
 @pytest.mark.parametrize("key", ["w4", "w4ao", "w8", "w8e", "w8odd"])
-@pytest.mark.parametrize("bs", [16, 64, 128])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("M", [1, 37, 300])
 def test_down(key, bs, M):
     """DOWN from the oracle's H rounded to the activation type."""
@@ -322,7 +324,7 @@ def _check_down(key, bs, M):
 
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("key", ["w4", "w4ao", "w4pc", "w8", "w8e", "w8odd"])
-@pytest.mark.parametrize("bs", [16, 64, 128])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("M", [1, 16, 53, 512])
 def test_layer(key, bs, M):
     need_gpu()

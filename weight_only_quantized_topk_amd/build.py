@@ -31,8 +31,13 @@ FLAGS = [
 # ILP strategy: measured on MI355X, its gate/up launches run 1-2 % faster
 # than under the default scheduler (Mixtral int8 M=1024 0.485 -> 0.478 ms,
 # int4 act-order M=4096 1.77 -> 1.75 ms), with no register spills except in
-# the 256 x 128 shape, which gemm_prefill_n256.hip builds under the default one
-SOURCE_FLAGS = {"gemm_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# the 256 x 128 shape, which gemm_prefill_n256.hip builds under the default one.
+# WQ_PREFILL_SCHED=default builds it under LLVM's default scheduler instead.
+PREFILL_SCHED = os.environ.get("WQ_PREFILL_SCHED", "iterative-ilp")
+if PREFILL_SCHED not in ("iterative-ilp", "default"):
+    raise ValueError("WQ_PREFILL_SCHED must be 'iterative-ilp' or 'default', got %r" % PREFILL_SCHED)
+SOURCE_FLAGS = ({"gemm_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+                if PREFILL_SCHED == "iterative-ilp" else {})
 
 
 def _compile(src: str) -> str:

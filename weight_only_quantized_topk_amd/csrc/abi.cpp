@@ -487,6 +487,7 @@ wq_status dense_gemm(int wbits, const void* d_x, int M, int K, int N, const void
     WQ_TRY(check_ptr(d_w, "w_packed"));
     WQ_TRY(check_ptr(d_scales, "scales"));
     WQ_TRY(check_ptr(d_y, "y"));
+    if (act_order) WQ_TRY(check_ptr(d_k_perm, "k_perm"));  // read with 128-bit loads by the gather
     WQ_TRY(check_dev(d_x, "x"));
     WQ_TRY(check_dev(d_w, "w_packed"));
     WQ_TRY(check_dev(d_scales, "scales"));

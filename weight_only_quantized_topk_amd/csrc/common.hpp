@@ -93,6 +93,11 @@ __device__ __forceinline__ uint16_t f32_to_act(float f) {
 // for channels 4..7).  OR-ing the exponent of 1024 (0x6400) gives 1024 + u, or
 // 1024 + 16u for the upper nibble of a byte, exactly; 1024 + u - 1032 = q and
 // (1024 + 16u) / 16 - 72 = q are exact in fp16.  9 VALU ops per 8 codes.
+// This is the published fast integer-to-half conversion with an interleaved
+// nibble order (Kim et al., "Who Says Elephants Can't Run: Bringing Large
+// Scale MoE Models into Cloud Scale Production", 2022), the conversion the
+// Marlin kernels also use; the mask and bias constants follow from the fp16
+// encoding of 1024 + u and are fixed by the method.
 // ---------------------------------------------------------------------------
 // (16-bit float arithmetic on a dword holding two halves; only scalars are
 // bit-cast: a bit-cast of an ext-vector element reads the vector's first dword)
