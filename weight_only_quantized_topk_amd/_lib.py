@@ -65,6 +65,12 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libwqmoe.so is not built (%s); run `python -m weight_only_quantized_topk_amd.build`"
                           % LIB_PATH)
+    # torch first: the library and torch must share one HIP runtime.  Both need
+    # libamdhip64.so.7, which torch bundles and ROCm installs; the loader maps
+    # whichever comes first for both, and torch has to run on its own (loaded
+    # the other way round, the library's hipGetDevice failed in a process where
+    # torch then initialised the GPU)
+    import torch  # noqa: F401
     L = C.CDLL(LIB_PATH)
     p, i, sz = C.c_void_p, C.c_int, C.c_size_t
     L.wq_version.restype = i
