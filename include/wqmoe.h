@@ -29,7 +29,9 @@
  *    be 16-byte aligned.  Row-major layouts throughout.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *  - Ownership: the caller allocates and frees everything, workspaces
- *    included.  The library keeps no state beyond a thread-local error text.
+ *    included (except for moe_w8a16_gemm_noalloc, whose workspace is a device
+ *    array inside the library).  The library keeps no other state than a
+ *    thread-local error text and that array's device address per GPU.
  *  - Errors: arguments are validated on the host before anything is launched.
  *    A failing call launches nothing and returns a non-zero status; the text of
  *    the last error on this thread is returned by wq_last_error().  No call
@@ -197,6 +199,28 @@ size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, in
                                 int act_order);
 wq_status moe_w4a16_gemm(const wq_moe_gemm_desc* d, void* stream);
 wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
+
+/*
+ * moe_w8a16_gemm_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moe_w8a16_gemm with the same descriptor, kernels and results,
+ * whose workspace is a device array inside the library instead of the
+ * caller's buffer.  d->d_workspace must be NULL and d->workspace_bytes 0; the
+ * caller still passes every input and output.
+ *  - The array holds WQ_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the
+ *    library is loaded on, until the process ends.  A call whose
+ *    moe_gemm_workspace_bytes() exceeds it returns WQ_ERR_UNSUPPORTED and
+ *    launches nothing (64 MiB covers the DOWN stage of the Mixtral-8x7B shape
+ *    up to 512 tokens and of the DeepSeek-V2 shape up to 512 tokens; GATE_UP
+ *    and RAW of int8 weights need none).
+ *  - No hipMalloc, hipFree or other allocation, no memset: the DOWN stage
+ *    writes every scratch element it later reads.
+ *  - All calls on one GPU share its array: calls that overlap in time on one
+ *    GPU (different streams, or host threads without stream ordering) race on
+ *    it.  Calls on one stream are ordered and safe.
+ */
+#define WQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+wq_status moe_w8a16_gemm_noalloc(const wq_moe_gemm_desc* d, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* 2:4-sparse W4A16 linear layer                                             */

@@ -176,6 +176,11 @@ def _desc(**kw):
     ("moe_w8a16_gemm", dict(group_size=-1, k_in=96), wq.WQ_ERR_UNSUPPORTED),
     ("moe_w8a16_gemm", dict(group_size=-1, d_k_perm=FAKE), wq.WQ_ERR_INVALID),
     ("moe_w8a16_gemm", dict(group_size=-1, M=1 << 24), wq.WQ_ERR_UNSUPPORTED),
+    # the no-allocation variant takes no workspace and refuses one beyond its scratch
+    ("moe_w8a16_gemm_noalloc", dict(group_size=-1, d_workspace=FAKE, workspace_bytes=1 << 20), wq.WQ_ERR_INVALID),
+    ("moe_w8a16_gemm_noalloc", dict(group_size=-1, stage=wq.WQ_STAGE_DOWN, M=1 << 15, n_out=256, k_in=4096,
+                                    capacity=wq.moe_align_capacity(1 << 15, 2, 8, 16)), wq.WQ_ERR_UNSUPPORTED),
+    ("moe_w8a16_gemm_noalloc", dict(group_size=-1, k_in=96), wq.WQ_ERR_UNSUPPORTED),
 ])
 def test_gemm_validation(fn, kw, expect):
     d = _desc(**kw)

@@ -13,11 +13,12 @@ WQ_OK, WQ_ERR_INVALID, WQ_ERR_UNSUPPORTED, WQ_ERR_DEVICE, WQ_ERR_HIP = 0, 1, 2, 
 WQ_F16, WQ_BF16 = 0, 1
 WQ_STAGE_GATE_UP, WQ_STAGE_DOWN, WQ_STAGE_RAW = 0, 1, 2
 WQ_PACK_INTERLEAVE_GATE_UP = 1
+WQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "wq_version", "wq_status_string", "wq_last_error",
     "moe_route", "moe_align_capacity", "moe_align", "moe_route_align",
-    "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
+    "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm", "moe_w8a16_gemm_noalloc",
     "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "wq_quantize_w8",
     "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "wq_pack_w4_bytes", "wq_pack_w8_bytes", "wq_pack_w4", "wq_pack_w8",
@@ -86,6 +87,7 @@ def load():
     L.moe_gemm_workspace_bytes.restype = sz
     L.moe_w4a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.moe_w8a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
+    L.moe_w8a16_gemm_noalloc.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.sparse24_w4a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
     L.sparse24_w8a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
     L.wq_quantize_w8.argtypes = [p, C.c_int64, i, i, p, p, p]
@@ -104,7 +106,8 @@ def load():
     L.wq_pack_sparse24_meta_bytes.argtypes = [i, i]
     L.wq_pack_sparse24_meta_bytes.restype = sz
     L.wq_pack_sparse24.argtypes = [i, i, i, i, p, p, p, p, p, p]
-    for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm", "sparse24_w4a16_gemm",
+    for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm",
+              "moe_w8a16_gemm_noalloc", "sparse24_w4a16_gemm",
               "sparse24_w8a16_gemm",
               "wq_quantize_w8", "dense_w4a16_gemm", "dense_w8a16_gemm", "wq_pack_w4",
               "wq_pack_w8", "wq_pack_sparse24"):

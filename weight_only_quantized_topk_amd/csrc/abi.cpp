@@ -11,9 +11,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -80,6 +82,41 @@ wq_status after_launch(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(WQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+// ---------------------------------------------------------------------------
+// The no-allocation entry point's workspace: one file-scope device array per
+// GPU, held from the library's load until the process ends.  Host code never
+// uses the array's name as an address (on the host it names a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device with that
+// device current, and is kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[WQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_addr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// device address of the current device's scratch array
+wq_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(WQ_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(WQ_ERR_UNSUPPORTED, "device %d >= %d", dev, MAX_DEVICES);
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();
+                return fail(WQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+            }
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return WQ_OK;
 }
 
 bool valid_block_size(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
@@ -248,7 +285,9 @@ size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, in
     return b;
 }
 
-static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, const char* who) {
+// noalloc: the workspace is the library's scratch array (d_workspace must be
+// NULL and workspace_bytes 0; a need above its size is refused)
+static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, const char* who, bool noalloc = false) {
     WQ_REQUIRE(d != nullptr, WQ_ERR_INVALID, "%s: desc is NULL", who);
     WQ_REQUIRE(d->struct_size >= sizeof(wq_moe_gemm_desc), WQ_ERR_INVALID, "%s: struct_size %zu < %zu", who,
                d->struct_size, sizeof(wq_moe_gemm_desc));
@@ -280,8 +319,16 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     WQ_REQUIRE(!act_order || (wbits == 4 && stage != WQ_STAGE_DOWN), WQ_ERR_INVALID,
                "%s: k_perm only applies to int4 GATE_UP/RAW", who);
     const size_t ws = moe_gemm_workspace_bytes(stage, d->M, d->topk, d->E, d->n_out, d->k_in, d->capacity, act_order);
-    WQ_REQUIRE(d->workspace_bytes >= ws, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who, d->workspace_bytes,
-               ws);
+    if (noalloc) {
+        WQ_REQUIRE(d->d_workspace == nullptr && d->workspace_bytes == 0, WQ_ERR_INVALID,
+                   "%s: takes no workspace (d_workspace must be NULL, workspace_bytes 0)", who);
+        WQ_REQUIRE(ws <= (size_t)WQ_NOALLOC_SCRATCH_BYTES, WQ_ERR_UNSUPPORTED,
+                   "%s: needs %zu bytes of workspace, more than the %zu-byte scratch", who, ws,
+                   (size_t)WQ_NOALLOC_SCRATCH_BYTES);
+    } else {
+        WQ_REQUIRE(d->workspace_bytes >= ws, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who,
+                   d->workspace_bytes, ws);
+    }
     if (d->M == 0) return ok();
     WQ_TRY(check_ptr(d->d_a, "a"));
     WQ_TRY(check_ptr(d->d_w_packed, "w_packed"));
@@ -292,7 +339,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     WQ_TRY(check_ptr(d->d_out, "out"));
     if (act_order) WQ_TRY(check_ptr(d->d_k_perm, "k_perm"));
     if (stage == WQ_STAGE_DOWN) WQ_TRY(check_ptr(d->d_topk_weights, "topk_weights"));
-    if (ws) WQ_TRY(check_ptr(d->d_workspace, "workspace"));
+    if (ws && !noalloc) WQ_TRY(check_ptr(d->d_workspace, "workspace"));
 
     WQ_TRY(check_dev(d->d_a, "a"));
     WQ_TRY(check_dev(d->d_w_packed, "w_packed"));
@@ -303,7 +350,9 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     WQ_TRY(check_dev(d->d_out, "out"));
     if (act_order) WQ_TRY(check_dev(d->d_k_perm, "k_perm"));
     if (stage == WQ_STAGE_DOWN) WQ_TRY(check_dev(d->d_topk_weights, "topk_weights"));
-    if (ws) WQ_TRY(check_dev(d->d_workspace, "workspace"));
+    if (ws && !noalloc) WQ_TRY(check_dev(d->d_workspace, "workspace"));
+    void* workspace = d->d_workspace;
+    if (ws && noalloc) WQ_TRY(scratch_for_current_device(&workspace));
 
     hipStream_t s = (hipStream_t)stream;
     const bool bf16 = d->act_dtype == WQ_BF16;
@@ -333,7 +382,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
                "%s: activations of %zu rows x %d channels exceed 4 GiB (large-batch kernel)", who, d->capacity,
                d->k_in);
     if (act_order && !tiny) {
-        uint16_t* a1 = static_cast<uint16_t*>(d->d_workspace);
+        uint16_t* a1 = static_cast<uint16_t*>(workspace);
         wq::launch_gather_perm(g.a, d->d_k_perm, g.sorted, g.expert_ids, g.ntpp, d->M, d->topk, d->k_in,
                                d->block_size, g.cap, a1, s);
         WQ_TRY(after_launch(who));
@@ -342,7 +391,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     }
     float* y = nullptr;
     if (stage == WQ_STAGE_DOWN) {
-        y = static_cast<float*>(d->d_workspace);
+        y = static_cast<float*>(workspace);
         g.out = y;
     }
     int ksplit = 1;
@@ -370,6 +419,14 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream) {
         return moe_gemm(d, 8, stream, "moe_w8a16_gemm");
     } catch (...) {
         return fail(WQ_ERR_HIP, "moe_w8a16_gemm: unexpected exception");
+    }
+}
+
+wq_status moe_w8a16_gemm_noalloc(const wq_moe_gemm_desc* d, void* stream) {
+    try {
+        return moe_gemm(d, 8, stream, "moe_w8a16_gemm_noalloc", true);
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_w8a16_gemm_noalloc: unexpected exception");
     }
 }
 

@@ -18,7 +18,7 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
 
 __all__ = [
     "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
-    "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
+    "moe_w8a16_gemm_noalloc", "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "pack_w4", "pack_w8", "pack_sparse24", "act_code",
 ]
 
@@ -146,6 +146,16 @@ def moe_w8a16_gemm(stage, a, M, topk, E, n_out, k_in, w_packed, scales, sorted_t
     return _gemm("moe_w8a16_gemm", stage, a, M, topk, E, n_out, k_in, w_packed, scales, -1, None,
                  sorted_token_ids, expert_ids, num_tokens_post_padded, capacity, block_size, topk_weights, out,
                  workspace, stream, act_dtype)
+
+
+def moe_w8a16_gemm_noalloc(stage, a, M, topk, E, n_out, k_in, w_packed, scales, sorted_token_ids, expert_ids,
+                           num_tokens_post_padded, capacity, block_size, topk_weights, out, stream=None,
+                           act_dtype=WQ_BF16):
+    """moe_w8a16_gemm with the library's own scratch as the workspace (no
+    workspace argument; nothing is allocated)."""
+    return _gemm("moe_w8a16_gemm_noalloc", stage, a, M, topk, E, n_out, k_in, w_packed, scales, -1, None,
+                 sorted_token_ids, expert_ids, num_tokens_post_padded, capacity, block_size, topk_weights, out,
+                 None, stream, act_dtype)
 
 
 def _sparse24(fn, x, vals, meta, scales, N, out, group_size, stream):
