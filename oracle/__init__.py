@@ -73,8 +73,12 @@ def lib():
                                     p, p, p, p]
         L.orc_sparse24.argtypes = [i64, i32, i32, p, p, p, p, i32, p, i64, p]
         L.orc_quant_w8.argtypes = [i64, i32, p, i32, p, p]
+        L.orc_fp8_decode.argtypes = [i64, p, p]
+        L.orc_fp8_quant.argtypes = [i64, p, C.c_float, p]
+        L.orc_fp8_moe_layer.argtypes = [i64, i32, i32, i32, i32, p, p, p, p, p, p, p, C.c_float, C.c_float, p, i64,
+                                        p, p, p, p]
         for f in ("orc_route", "orc_align", "orc_moe_up", "orc_moe_down", "orc_moe_combine", "orc_moe_layer",
-                  "orc_sparse24", "orc_quant_w8"):
+                  "orc_sparse24", "orc_quant_w8", "orc_fp8_decode", "orc_fp8_quant", "orc_fp8_moe_layer"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -229,3 +233,53 @@ def quant_w8(w, bf16: bool):
     s = np.empty(w.shape[:-1], np.float32)
     _check(lib().orc_quant_w8(rows, k, _ptr(w), int(bool(bf16)), _ptr(q), _ptr(s)), "quant_w8")
     return q, s
+
+
+# ----------------------------------------------------------------------------
+# FP8 (OCP E4M3) W8A8 MoE layer
+# ----------------------------------------------------------------------------
+def fp8_decode(codes) -> np.ndarray:
+    """E4M3 codes (uint8, any shape) -> their values (float64; NaN for 0x7F/0xFF)."""
+    c = _c(codes, np.uint8)
+    v = np.empty(c.shape, np.float64)
+    _check(lib().orc_fp8_decode(c.size, _ptr(c), _ptr(v)), "fp8_decode")
+    return v
+
+
+def fp8_quant(v, scale: float) -> np.ndarray:
+    """Codes of v / scale (float32 division), nearest E4M3 after saturating to
+    +-448, ties to even; v float32 values (any shape)."""
+    a = _c(v, np.float32)
+    q = np.empty(a.shape, np.uint8)
+    _check(lib().orc_fp8_quant(a.size, _ptr(a), float(scale), _ptr(q)), "fp8_quant")
+    return q
+
+
+def fp8_moe_layer(x, topk_weights, topk_ids, w1, sw1, w2, sw2, a1: float, a2: float, rows=None,
+                  want=("out",)):
+    """FP8 W8A8 layer: x [M, K] float32 values, w1 [E, 2N, K] / w2 [E, K, N]
+    E4M3 codes, sw1 [E, 2N] / sw2 [E, K] float32 per-column weight scales, a1 /
+    a2 static activation scales.  Returns a dict with 'out' [R, K] (float64)
+    and on request 'gu' [R*topk, 2N], 'hq' [R*topk, N] (codes), 'y' [R*topk, K]."""
+    x = _c(x, np.float32)
+    w = _c(topk_weights, np.float32)
+    ids = _c(topk_ids, np.int32)
+    M, K = x.shape
+    topk = ids.shape[1]
+    E, n_out, _ = w1.shape
+    N = n_out // 2
+    rows_a = _c(rows, np.int64)
+    R = M if rows_a is None else rows_a.size
+    res = {"out": np.empty((R, K))}
+    if "gu" in want:
+        res["gu"] = np.empty((R * topk, n_out))
+    if "hq" in want:
+        res["hq"] = np.empty((R * topk, N), np.uint8)
+    if "y" in want:
+        res["y"] = np.empty((R * topk, K))
+    rc = lib().orc_fp8_moe_layer(M, K, N, E, topk, _ptr(x), _ptr(w), _ptr(ids), _ptr(_c(w1, np.uint8)),
+                                 _ptr(_c(sw1, np.float32)), _ptr(_c(w2, np.uint8)), _ptr(_c(sw2, np.float32)),
+                                 float(a1), float(a2), _ptr(rows_a), R, _ptr(res.get("gu")), _ptr(res.get("hq")),
+                                 _ptr(res.get("y")), _ptr(res["out"]))
+    _check(rc, "fp8_moe_layer")
+    return res

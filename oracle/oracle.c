@@ -410,3 +410,139 @@ ORC_EXPORT int orc_quant_w8(int64_t rows, int k, const float* w, int bf16, int8_
     }
     return bad ? -1 : 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 W8A8 MoE layer: the comparison method of the ExpertsInt8 latency      */
+/* table ("[Kernel] W8A16 Int8 inside FusedMoE", latency table rows "FP8     */
+/* (MoE quant-only)", and the review thread naming it use_fp8_w8a8: weights  */
+/* and activations both in 8-bit floating point).  The pages give no scheme;  */
+/* the reading followed here:                                                 */
+/*  - FP8 format: OCP E4M3 -- sign, 4 exponent bits with bias 7, 3 mantissa   */
+/*    bits, no infinities, exponent 15 with mantissa 7 is NaN; largest finite */
+/*    448, smallest normal 2^-6, subnormals (m/8) 2^-6.                       */
+/*  - Weights: E4M3 codes, one float32 scale per expert and output column:    */
+/*    W[e, r, k] = dec(c[e, r, k]) * sw[e, r].                               */
+/*  - Activations: one static float32 scale per tensor (a1 for the layer      */
+/*    input, a2 for the intermediate H), quantised as                        */
+/*    q = enc(v / a)  with v / a a float32 division, enc = nearest E4M3 value */
+/*    after clamping to [-448, 448] (saturating), ties to the even mantissa,  */
+/*    the sign kept on zero; dequantised as dec(q) * a.  H is rounded to      */
+/*    float32 before its division (the kernel holds H in float32).            */
+/*  - The layer is the W8A16 one with these dequantised operands: gate/up     */
+/*    over dequantised x, SiLU(gate) * up, quantise H, down, weighted sum.    */
+/* ------------------------------------------------------------------------ */
+ORC_EXPORT double orc_e4m3_decode(uint8_t c)
+{
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* nearest E4M3 code to a finite v (saturating at +-448, ties to even) */
+ORC_EXPORT uint8_t orc_e4m3_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a > 448.0) a = 448.0;
+    /* 4 significant bits, exponents down to -6; exact in double (a is a
+     * float32 value, the step a power of two); 448 is representable, so the
+     * clamped value never rounds past it */
+    const double r = round_sig(a, 4, -6, 448.0);
+    if (r == 0.0) return sign;
+    int e = ilogb(r);
+    if (e < -6) return sign | (uint8_t)(r / ldexp(1.0, -9)); /* subnormal: r = m 2^-9 */
+    const int m = (int)((r / ldexp(1.0, e) - 1.0) * 8.0);
+    return sign | (uint8_t)((e + 7) << 3) | (uint8_t)m;
+}
+
+/* values of n codes */
+ORC_EXPORT int orc_fp8_decode(int64_t n, const uint8_t* q, double* v)
+{
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) v[i] = orc_e4m3_decode(q[i]);
+    return 0;
+}
+
+/* codes of v / scale (float32 division) for n values */
+ORC_EXPORT int orc_fp8_quant(int64_t n, const float* v, float scale, uint8_t* q)
+{
+    if (n < 0 || !(scale > 0.0f)) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(v[i])) return -1;
+        const float t = v[i] / scale;
+        q[i] = orc_e4m3_encode((double)t);
+    }
+    return 0;
+}
+
+/*
+ * The FP8 W8A8 layer for already-routed tokens (rows: evaluated tokens, NULL
+ * for all M).  x [M,K] (float32 values of the 16-bit activations),
+ * w1 [E,2N,K] and w2 [E,K,N] E4M3 codes, sw1 [E,2N], sw2 [E,K] float32.
+ * Outputs per evaluated (token, slot) r: optionally gu [r, 2N] (the gate/up
+ * projections of the quantised input), hq [r, N] (the codes of H); y [r, K]
+ * unweighted down projections; out [row, K] the weighted sum (ascending j).
+ */
+ORC_EXPORT int orc_fp8_moe_layer(int64_t M, int K, int N, int E, int topk,
+                                 const float* x, const float* topk_weights, const int32_t* topk_ids,
+                                 const uint8_t* w1, const float* sw1, const uint8_t* w2, const float* sw2,
+                                 float a1, float a2, const int64_t* rows, int64_t nrows,
+                                 double* gu, uint8_t* hq, double* y_out, double* out)
+{
+    if (!rows) nrows = M;
+    if (!(a1 > 0.0f) || !(a2 > 0.0f) || K <= 0 || N <= 0 || E <= 0 || topk <= 0) return -1;
+    const int n_out = 2 * N;
+    double* y = y_out ? y_out : (double*)malloc(sizeof(double) * (size_t)(nrows * topk) * (size_t)K);
+    if (!y) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        for (int j = 0; j < topk; ++j) {
+            const int64_t m = rows ? rows[rr] : rr;
+            if (m < 0 || m >= M) { SET_BAD(bad); continue; }
+            const int e = topk_ids[m * topk + j];
+            if (e < 0 || e >= E) { SET_BAD(bad); continue; }
+            const int64_t r = rr * topk + j;
+            double* xd = (double*)malloc(sizeof(double) * (size_t)K);
+            double* hd = (double*)malloc(sizeof(double) * (size_t)N);
+            if (!xd || !hd) { free(xd); free(hd); SET_BAD(bad); continue; }
+            /* the layer input, quantised and dequantised */
+            for (int k = 0; k < K; ++k) {
+                const float t = x[m * K + k] / a1;
+                xd[k] = orc_e4m3_decode(orc_e4m3_encode((double)t)) * (double)a1;
+            }
+            const uint8_t* c1 = w1 + (int64_t)e * n_out * K;
+            for (int n = 0; n < N; ++n) {
+                double gate = 0.0, up = 0.0;
+                for (int k = 0; k < K; ++k)
+                    gate += xd[k] * (orc_e4m3_decode(c1[(int64_t)n * K + k]) * (double)sw1[(int64_t)e * n_out + n]);
+                for (int k = 0; k < K; ++k)
+                    up += xd[k] * (orc_e4m3_decode(c1[(int64_t)(N + n) * K + k]) *
+                                   (double)sw1[(int64_t)e * n_out + N + n]);
+                if (gu) {
+                    gu[r * n_out + n] = gate;
+                    gu[r * n_out + N + n] = up;
+                }
+                const double h = silu(gate) * up;
+                const float t = (float)h / a2;
+                const uint8_t c = orc_e4m3_encode((double)t);
+                if (hq) hq[r * N + n] = c;
+                hd[n] = orc_e4m3_decode(c) * (double)a2;
+            }
+            const uint8_t* c2 = w2 + (int64_t)e * K * N;
+            for (int cc = 0; cc < K; ++cc) {
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n)
+                    acc += hd[n] * (orc_e4m3_decode(c2[(int64_t)cc * N + n]) * (double)sw2[(int64_t)e * K + cc]);
+                y[r * K + cc] = acc;
+            }
+            free(xd);
+            free(hd);
+        }
+    }
+    int rc = bad ? -1 : 0;
+    if (!rc) rc = orc_moe_combine(M, K, topk, topk_weights, rows, nrows, y, out);
+    if (!y_out) free(y);
+    return rc;
+}
