@@ -286,3 +286,71 @@ def make_sparse_x(spec: SparseSpec, M: int, seed_config: Optional[int] = None) -
     cid = spec.config_id if seed_config is None else seed_config
     rx = rng_for(cid, M, STREAM_X)
     return round_to(spec.act, rx.standard_normal((M, spec.K), dtype=np.float32))
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) W8A8 MoE tensors
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Fp8MoESpec:
+    """An FP8 W8A8 MoE layer: E4M3 weight codes with float32 per-column scales,
+    static float32 activation scales a1 (layer input) and a2 (intermediate H).
+
+    Weight codes are drawn as bit patterns: sign uniform, exponent field
+    uniform in [exp_lo, exp_hi] (values 2^(e-7) (1 + m/8)), mantissa uniform;
+    scales uniform in [scale_lo, scale_hi] as float32.  a1 and a2 are powers of
+    two chosen so the largest |x| / a1 and |h| / a2 of the workload stay below
+    448 (a calibrated static scale)."""
+    name: str
+    config_id: int
+    E: int
+    topk: int
+    K: int
+    N: int
+    act: str
+    scale_lo: float
+    scale_hi: float
+    exp_lo: int
+    exp_hi: int
+    a1: float
+    a2: float
+    renormalize: bool = True
+    zipf_s: Optional[float] = None
+    m_sweep: Tuple[int, ...] = field(default_factory=tuple)
+
+    def with_(self, **kw) -> "Fp8MoESpec":
+        return replace(self, **kw)
+
+
+# the pages' FP8 rows run Mixtral-8x7B; same shape and batch sizes as the int8 layer
+# (a1 = 2^-6: |x| <= 5.5 maps below 352; a2 = 2^-4: |h| of the 1024-token batch stays below 448 a2)
+CFG_FP8 = Fp8MoESpec("mixtral8x7b-fp8-w8a8", 6, E=8, topk=2, K=4096, N=14336, act="bf16", scale_lo=1e-3,
+                     scale_hi=4e-3, exp_lo=4, exp_hi=10, a1=2.0 ** -6, a2=2.0 ** -4, m_sweep=(1, 4, 8, 64, 1024))
+
+
+@dataclass
+class Fp8MoEWeights:
+    """w1 [E, 2N, K] / w2 [E, K, N] E4M3 codes (uint8); s1 [E, 2N] / s2 [E, K] float32."""
+    spec: Fp8MoESpec
+    w1: np.ndarray
+    s1: np.ndarray
+    w2: np.ndarray
+    s2: np.ndarray
+
+
+def _draw_e4m3(rng, shape, exp_lo, exp_hi) -> np.ndarray:
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8)
+    expo = rng.integers(exp_lo, exp_hi + 1, size=shape, dtype=np.uint8)
+    mant = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign << 7) | (expo << 3) | mant
+
+
+def make_fp8_weights(spec: Fp8MoESpec, seed_config: Optional[int] = None) -> Fp8MoEWeights:
+    cid = spec.config_id if seed_config is None else seed_config
+    rng = rng_for(cid, 0, STREAM_WEIGHTS)
+    E, K, N = spec.E, spec.K, spec.N
+    w1 = _draw_e4m3(rng, (E, 2 * N, K), spec.exp_lo, spec.exp_hi)
+    s1 = rng.uniform(spec.scale_lo, spec.scale_hi, size=(E, 2 * N)).astype(np.float32)
+    w2 = _draw_e4m3(rng, (E, K, N), spec.exp_lo, spec.exp_hi)
+    s2 = rng.uniform(spec.scale_lo, spec.scale_hi, size=(E, K)).astype(np.float32)
+    return Fp8MoEWeights(spec, w1, s1, w2, s2)

@@ -12,6 +12,7 @@
  *   moe_w8a16_gemm        grouped GEMM, int8 per-column weights, bf16/fp16 activations
  *   sparse24_w4a16_gemm   2:4-sparse int4 dense linear layer, fp16 activations
  *   sparse24_w8a16_gemm   the same with 8-bit kept codes
+ *   moe_fp8_w8a8_gemm     grouped GEMM with FP8 (E4M3) weights and activations
  * Beside them: dense_w4a16_gemm / dense_w8a16_gemm (one quantized weight
  * matrix, the same kernels with one expert) and wq_quantize_w8 (the int8
  * weights and scales from a 16-bit checkpoint on the device, at load time).
@@ -223,6 +224,42 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
 wq_status moe_w8a16_gemm_noalloc(const wq_moe_gemm_desc* d, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* FP8 W8A8 grouped GEMM                                                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * The comparison method of the ExpertsInt8 latency table ("[Kernel] W8A16
+ * Int8 inside FusedMoE", vLLM PR 7415: rows "FP8 (MoE quant-only)", and the
+ * review thread naming it use_fp8_w8a8): weights and activations both in OCP
+ * FP8 E4M3 (no infinities, 0x7F / 0xFF = NaN, largest finite 448), one float32
+ * weight scale per expert and output column, one static float32 scale per
+ * activation tensor (a1 for the layer input, a2 for H).  A value v is
+ * quantised to the E4M3 code nearest to v / a (float32 division) after
+ * clamping to +-448, ties to even.  Same descriptor as moe_w8a16_gemm, read
+ * as follows:
+ *  GATE_UP  d_a = x [M, k_in] in act_dtype, quantised with in_scale = a1 into
+ *           the workspace; W = wq_pack_fp8 output with
+ *           WQ_PACK_INTERLEAVE_GATE_UP, n_out = 2N; d_out = H codes uint8
+ *           [capacity, N]: H[p, n] = code of silu(g) * u / out_scale (out_scale
+ *           = a2) with g, u = in_scale * scale[row] * (x codes . weight codes),
+ *           pad rows code 0.
+ *  DOWN     d_a = H codes uint8 [capacity, k_in] from GATE_UP, in_scale = a2;
+ *           d_out = out [M, n_out] act_dtype, the routed-weight sum of
+ *           in_scale * scale[c] * (H codes . weight codes) in ascending slot
+ *           order, fp32, rounded once; out_scale unused.
+ *  RAW      d_a = x as for GATE_UP; d_out = fp32 [M*topk, n_out] (testing).
+ *  d_scales float32 [E, n_out] from wq_pack_fp8 (packed row order);
+ *  group_size -1; d_k_perm NULL; in_scale (and for GATE_UP out_scale) finite
+ *  and > 0; the workspace (moe_fp8_gemm_workspace_bytes) holds the x codes
+ *  (GATE_UP / RAW) or the fp32 per-pair rows of DOWN.
+ * Blocks of 64 or a multiple of 128 (n_out % 128 == 0) take the large-batch
+ * kernel (v_mfma_scale_f32_16x16x128_f8f6f4, token rows in LDS), which
+ * refuses more than 4 GiB of activation codes; other blocks the small-batch
+ * kernel.  Limits: k_in % 128 == 0, n_out % 16 (32 for GATE_UP) == 0.
+ */
+size_t moe_fp8_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, int k_in);
+wq_status moe_fp8_w8a8_gemm(const wq_moe_gemm_desc* d, float in_scale, float out_scale, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* 2:4-sparse W4A16 linear layer                                             */
 /* ------------------------------------------------------------------------ */
 /*
@@ -337,6 +374,17 @@ wq_status wq_pack_w4(int E, int n_out, int k_in, const int8_t* q, const uint16_t
                      void* packed, uint16_t* scales_packed, int32_t* k_perm);
 wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t* scales,
                      const int32_t* row_perm, int flags, void* packed, uint16_t* scales_packed);
+
+/*
+ * FP8 packer: codes uint8 [E, n_out, k_in] (E4M3, no NaN), scales float32
+ * [E, n_out] -> packed (wq_pack_fp8_bytes: E * n_out * k_in bytes, tiles of 16
+ * rows x 128 channels) and scales_packed float32 [E, n_out] in packed row
+ * order; row_perm and flags as for wq_pack_w8.  Limits: n_out % 16 == 0 (% 32
+ * with interleave), k_in % 128 == 0.
+ */
+size_t wq_pack_fp8_bytes(int E, int n_out, int k_in);
+wq_status wq_pack_fp8(int E, int n_out, int k_in, const uint8_t* codes, const float* scales,
+                      const int32_t* row_perm, int flags, void* packed, float* scales_packed);
 
 /*
  * 2:4 sparse canonical input: vals int8 [N, K/2] (kept codes, in [-8, 7] for

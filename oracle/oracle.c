@@ -495,6 +495,8 @@ ORC_EXPORT int orc_fp8_moe_layer(int64_t M, int K, int N, int E, int topk,
     const int n_out = 2 * N;
     double* y = y_out ? y_out : (double*)malloc(sizeof(double) * (size_t)(nrows * topk) * (size_t)K);
     if (!y) return -1;
+    double dec[256]; /* the value of every code, looked up in the loops below */
+    for (int c = 0; c < 256; ++c) dec[c] = orc_e4m3_decode((uint8_t)c);
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2)
     for (int64_t rr = 0; rr < nrows; ++rr) {
@@ -510,16 +512,15 @@ ORC_EXPORT int orc_fp8_moe_layer(int64_t M, int K, int N, int E, int topk,
             /* the layer input, quantised and dequantised */
             for (int k = 0; k < K; ++k) {
                 const float t = x[m * K + k] / a1;
-                xd[k] = orc_e4m3_decode(orc_e4m3_encode((double)t)) * (double)a1;
+                xd[k] = dec[orc_e4m3_encode((double)t)] * (double)a1;
             }
             const uint8_t* c1 = w1 + (int64_t)e * n_out * K;
             for (int n = 0; n < N; ++n) {
                 double gate = 0.0, up = 0.0;
                 for (int k = 0; k < K; ++k)
-                    gate += xd[k] * (orc_e4m3_decode(c1[(int64_t)n * K + k]) * (double)sw1[(int64_t)e * n_out + n]);
+                    gate += xd[k] * (dec[c1[(int64_t)n * K + k]] * (double)sw1[(int64_t)e * n_out + n]);
                 for (int k = 0; k < K; ++k)
-                    up += xd[k] * (orc_e4m3_decode(c1[(int64_t)(N + n) * K + k]) *
-                                   (double)sw1[(int64_t)e * n_out + N + n]);
+                    up += xd[k] * (dec[c1[(int64_t)(N + n) * K + k]] * (double)sw1[(int64_t)e * n_out + N + n]);
                 if (gu) {
                     gu[r * n_out + n] = gate;
                     gu[r * n_out + N + n] = up;
@@ -528,13 +529,13 @@ ORC_EXPORT int orc_fp8_moe_layer(int64_t M, int K, int N, int E, int topk,
                 const float t = (float)h / a2;
                 const uint8_t c = orc_e4m3_encode((double)t);
                 if (hq) hq[r * N + n] = c;
-                hd[n] = orc_e4m3_decode(c) * (double)a2;
+                hd[n] = dec[c] * (double)a2;
             }
             const uint8_t* c2 = w2 + (int64_t)e * K * N;
             for (int cc = 0; cc < K; ++cc) {
                 double acc = 0.0;
                 for (int n = 0; n < N; ++n)
-                    acc += hd[n] * (orc_e4m3_decode(c2[(int64_t)cc * N + n]) * (double)sw2[(int64_t)e * K + cc]);
+                    acc += hd[n] * (dec[c2[(int64_t)cc * N + n]] * (double)sw2[(int64_t)e * K + cc]);
                 y[r * K + cc] = acc;
             }
             free(xd);

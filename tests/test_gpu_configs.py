@@ -184,3 +184,41 @@ def test_config_dense_w4(M):
     ref, _ = oracle.moe_up(toks.x_f32()[rows], np.zeros((rows.size, 1), np.int32), wts.w1q, wts.s1_f32(), None,
                            want_gu=True)
     assert_close_fp(host_f32(y)[rows], ref, "dense int4 Yi-34B shape M=%d" % M)
+
+
+_fp8 = {}
+
+
+@pytest.mark.parametrize("M", gen.CFG_FP8.m_sweep)
+@pytest.mark.timeout(900)
+def test_config_fp8(M):
+    """The FP8 W8A8 layer of the Mixtral-8x7B shape (the comparison method of
+    the ExpertsInt8 latency table) at the benchmark's batch sizes: routing and
+    sort bit for bit, the whole output tensor against the oracle."""
+    need_gpu()
+    spec = gen.CFG_FP8
+    if "p" not in _fp8:
+        _cache.clear()
+        _sparse.clear()
+        _dense.clear()
+        torch.cuda.empty_cache()
+        say("generating and packing the FP8 layer")
+        wts = gen.make_fp8_weights(spec)
+        _fp8["p"] = (wts, wq.pack_moe_fp8(wts.w1, wts.s1, wts.w2, wts.s2, torch.bfloat16, spec.a1, spec.a2))
+    wts, p = _fp8["p"]
+    toks = gen.make_tokens(spec, M)
+    say("fp8 config M", M)
+    out, aux = wq.fused_moe_fp8(dev_u16(toks.x, spec.act), torch.from_numpy(toks.logits).cuda(), p, spec.topk,
+                                spec.renormalize, keep=True)
+    torch.cuda.synchronize()
+    w_ref, ids_ref = oracle.route(toks.logits, spec.topk, spec.renormalize)
+    assert np.array_equal(aux["topk_ids"].cpu().numpy(), ids_ref)
+    w_got = aux["topk_weights"].cpu().numpy()
+    ud = ulp_diff_f32(w_got, w_ref)
+    assert ud.max() <= 1 and int((ud > 0).sum()) <= max(1, w_ref.size // 10000)
+    bs = aux["block_size"]
+    st_ref, ex_ref, nt_ref = oracle.align(ids_ref, spec.E, bs)
+    assert int(aux["num_tokens_post_padded"].cpu()[0]) == nt_ref
+    assert np.array_equal(aux["sorted_token_ids"].cpu().numpy()[:st_ref.size], st_ref)
+    ref = oracle.fp8_moe_layer(toks.x_f32(), w_got, ids_ref, wts.w1, wts.s1, wts.w2, wts.s2, spec.a1, spec.a2)["out"]
+    assert_close_fp(host_f32(out), ref, "fp8 Mixtral M=%d (all tokens)" % M)

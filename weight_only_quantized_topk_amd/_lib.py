@@ -23,6 +23,7 @@ EXPORTS = (
     "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "wq_pack_w4_bytes", "wq_pack_w8_bytes", "wq_pack_w4", "wq_pack_w8",
     "wq_pack_sparse24_vals_bytes", "wq_pack_sparse24_meta_bytes", "wq_pack_sparse24",
+    "moe_fp8_gemm_workspace_bytes", "moe_fp8_w8a8_gemm", "wq_pack_fp8_bytes", "wq_pack_fp8",
 )
 
 
@@ -106,11 +107,17 @@ def load():
     L.wq_pack_sparse24_meta_bytes.argtypes = [i, i]
     L.wq_pack_sparse24_meta_bytes.restype = sz
     L.wq_pack_sparse24.argtypes = [i, i, i, i, p, p, p, p, p, p]
+    L.moe_fp8_gemm_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.moe_fp8_gemm_workspace_bytes.restype = sz
+    L.moe_fp8_w8a8_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), C.c_float, C.c_float, p]
+    L.wq_pack_fp8_bytes.argtypes = [i, i, i]
+    L.wq_pack_fp8_bytes.restype = sz
+    L.wq_pack_fp8.argtypes = [i, i, i, p, p, p, i, p, p]
     for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm",
               "moe_w8a16_gemm_noalloc", "sparse24_w4a16_gemm",
               "sparse24_w8a16_gemm",
               "wq_quantize_w8", "dense_w4a16_gemm", "dense_w8a16_gemm", "wq_pack_w4",
-              "wq_pack_w8", "wq_pack_sparse24"):
+              "wq_pack_w8", "wq_pack_sparse24", "moe_fp8_w8a8_gemm", "wq_pack_fp8"):
         getattr(L, f).restype = i
     _lib = L
     return L

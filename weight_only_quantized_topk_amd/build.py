@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwqmoe.so")
-SOURCES = ["abi.cpp", "route_align.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_n256.hip", "sparse24.hip", "quant.hip", "dense_decode.hip", "gemm_tiny.hip"]
+SOURCES = ["abi.cpp", "route_align.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_n256.hip", "sparse24.hip", "quant.hip", "dense_decode.hip", "gemm_tiny.hip", "gemm_fp8.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

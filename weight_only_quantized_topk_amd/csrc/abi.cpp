@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -430,6 +431,127 @@ wq_status moe_w8a16_gemm_noalloc(const wq_moe_gemm_desc* d, void* stream) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) W8A8 grouped GEMM
+// ---------------------------------------------------------------------------
+static int fp8_down_slabs(int M, int topk, int E, int n_out, int k_in) {
+    const int T = M * topk;
+    return std::max(wq::fp8_down_split(T, E, n_out, k_in, 64), wq::fp8_down_split(T, E, n_out, k_in, 128));
+}
+
+size_t moe_fp8_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, int k_in) {
+    if (M < 0 || topk <= 0 || E <= 0 || n_out <= 0 || k_in <= 0) return 0;
+    if (stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_RAW) return round256((size_t)M * k_in);  // x codes
+    if (stage == WQ_STAGE_DOWN)
+        return round256((size_t)fp8_down_slabs(M, topk, E, n_out, k_in) * M * topk * n_out * sizeof(float));
+    return 0;
+}
+
+static wq_status fp8_gemm(const wq_moe_gemm_desc* d, float in_scale, float out_scale, void* stream) {
+    const char* who = "moe_fp8_w8a8_gemm";
+    WQ_REQUIRE(d != nullptr, WQ_ERR_INVALID, "%s: desc is NULL", who);
+    WQ_REQUIRE(d->struct_size >= sizeof(wq_moe_gemm_desc), WQ_ERR_INVALID, "%s: struct_size %zu < %zu", who,
+               d->struct_size, sizeof(wq_moe_gemm_desc));
+    const int stage = d->stage;
+    WQ_REQUIRE(stage == WQ_STAGE_GATE_UP || stage == WQ_STAGE_DOWN || stage == WQ_STAGE_RAW, WQ_ERR_INVALID,
+               "%s: bad stage %d", who, stage);
+    WQ_REQUIRE(d->act_dtype == WQ_F16 || d->act_dtype == WQ_BF16, WQ_ERR_INVALID, "%s: bad act dtype", who);
+    WQ_REQUIRE(d->M >= 0 && d->topk >= 1 && d->E >= 1 && d->topk <= d->E, WQ_ERR_INVALID,
+               "%s: bad M/topk/E (%d/%d/%d)", who, d->M, d->topk, d->E);
+    WQ_REQUIRE(d->E <= 1024, WQ_ERR_UNSUPPORTED, "%s: E > 1024", who);
+    WQ_REQUIRE((int64_t)d->M * d->topk <= MAX_PAIRS, WQ_ERR_UNSUPPORTED, "%s: M*topk > 2^24", who);
+    WQ_REQUIRE(d->n_out > 0 && d->k_in > 0, WQ_ERR_INVALID, "%s: bad n_out/k_in", who);
+    WQ_REQUIRE(d->k_in % wq::FP8_KCHUNK == 0, WQ_ERR_UNSUPPORTED, "%s: k_in %d not a multiple of %d", who, d->k_in,
+               wq::FP8_KCHUNK);
+    WQ_REQUIRE(d->n_out % (stage == WQ_STAGE_GATE_UP ? 32 : 16) == 0, WQ_ERR_UNSUPPORTED,
+               "%s: n_out %d not a multiple of %d", who, d->n_out, stage == WQ_STAGE_GATE_UP ? 32 : 16);
+    WQ_REQUIRE(d->group_size == -1, WQ_ERR_UNSUPPORTED, "%s: FP8 weights take per-column scales (-1)", who);
+    WQ_REQUIRE(d->d_k_perm == nullptr, WQ_ERR_INVALID, "%s: no act-order for FP8 weights", who);
+    WQ_REQUIRE(std::isfinite(in_scale) && in_scale > 0.0f, WQ_ERR_INVALID, "%s: in_scale must be finite and > 0",
+               who);
+    WQ_REQUIRE(stage != WQ_STAGE_GATE_UP || (std::isfinite(out_scale) && out_scale > 0.0f), WQ_ERR_INVALID,
+               "%s: out_scale must be finite and > 0", who);
+    WQ_REQUIRE(valid_block_size(d->block_size), WQ_ERR_UNSUPPORTED, "%s: block_size %d", who, d->block_size);
+    const size_t need_cap = moe_align_capacity(d->M, d->topk, d->E, d->block_size);
+    WQ_REQUIRE(d->capacity >= need_cap && d->capacity % (size_t)d->block_size == 0 &&
+                   d->capacity <= (size_t)0x7fffffff,
+               WQ_ERR_INVALID, "%s: capacity %zu (need >= %zu, multiple of block_size)", who, d->capacity, need_cap);
+    const size_t ws = moe_fp8_gemm_workspace_bytes(stage, d->M, d->topk, d->E, d->n_out, d->k_in);
+    WQ_REQUIRE(d->workspace_bytes >= ws, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who, d->workspace_bytes,
+               ws);
+    const bool large = wq::fp8_prefill_supported(d->n_out, d->k_in, d->block_size);
+    // the large-batch kernel addresses its activation codes with 32-bit byte offsets
+    const size_t a_rows = stage == WQ_STAGE_DOWN ? d->capacity : (size_t)d->M;
+    WQ_REQUIRE(!large || a_rows * (size_t)d->k_in <= (size_t)0xffffffffu, WQ_ERR_UNSUPPORTED,
+               "%s: activations of %zu rows x %d codes exceed 4 GiB (large-batch kernel)", who, a_rows, d->k_in);
+    if (d->M == 0) return ok();
+    WQ_TRY(check_ptr(d->d_a, "a"));
+    WQ_TRY(check_ptr(d->d_w_packed, "w_packed"));
+    WQ_TRY(check_ptr(d->d_scales, "scales"));
+    WQ_TRY(check_ptr(d->d_sorted_token_ids, "sorted_token_ids"));
+    WQ_TRY(check_ptr(d->d_expert_ids, "expert_ids"));
+    WQ_TRY(check_ptr(d->d_num_tokens_post_padded, "num_tokens_post_padded"));
+    WQ_TRY(check_ptr(d->d_out, "out"));
+    if (stage == WQ_STAGE_DOWN) WQ_TRY(check_ptr(d->d_topk_weights, "topk_weights"));
+    WQ_TRY(check_ptr(d->d_workspace, "workspace"));
+    WQ_TRY(check_dev(d->d_a, "a"));
+    WQ_TRY(check_dev(d->d_w_packed, "w_packed"));
+    WQ_TRY(check_dev(d->d_scales, "scales"));
+    WQ_TRY(check_dev(d->d_sorted_token_ids, "sorted_token_ids"));
+    WQ_TRY(check_dev(d->d_expert_ids, "expert_ids"));
+    WQ_TRY(check_dev(d->d_num_tokens_post_padded, "num_tokens_post_padded"));
+    WQ_TRY(check_dev(d->d_out, "out"));
+    if (stage == WQ_STAGE_DOWN) WQ_TRY(check_dev(d->d_topk_weights, "topk_weights"));
+    WQ_TRY(check_dev(d->d_workspace, "workspace"));
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = d->act_dtype == WQ_BF16;
+    wq::Fp8GemmArgs g{};
+    g.w = static_cast<const uint8_t*>(d->d_w_packed);
+    g.s = static_cast<const float*>(d->d_scales);
+    g.sorted = d->d_sorted_token_ids;
+    g.expert_ids = d->d_expert_ids;
+    g.ntpp = d->d_num_tokens_post_padded;
+    g.topk_w = d->d_topk_weights;
+    g.out = d->d_out;
+    g.M = d->M;
+    g.topk = d->topk;
+    g.E = d->E;
+    g.n_out = d->n_out;
+    g.k_in = d->k_in;
+    g.block_size = d->block_size;
+    g.cap = (int)d->capacity;
+    g.in_scale = in_scale;
+    g.out_scale = out_scale;
+    if (stage == WQ_STAGE_DOWN) {
+        g.a = static_cast<const uint8_t*>(d->d_a);  // H codes in sorted order
+        g.a_direct = 1;
+        g.out = d->d_workspace;                     // fp32 Y slabs
+    } else {
+        uint8_t* xq = static_cast<uint8_t*>(d->d_workspace);
+        wq::launch_fp8_quant(static_cast<const uint16_t*>(d->d_a), d->M, d->k_in, bf16, in_scale, xq, s);
+        WQ_TRY(after_launch(who));
+        g.a = xq;
+        g.a_direct = 0;
+    }
+    const int ks = wq::launch_gemm_fp8(stage, g, s);
+    WQ_TRY(after_launch(who));
+    if (stage == WQ_STAGE_DOWN) {
+        wq::launch_combine(static_cast<const float*>(d->d_workspace), d->M, d->topk, d->n_out, ks, bf16,
+                           static_cast<uint16_t*>(d->d_out), s);
+        WQ_TRY(after_launch(who));
+    }
+    return ok();
+}
+
+wq_status moe_fp8_w8a8_gemm(const wq_moe_gemm_desc* d, float in_scale, float out_scale, void* stream) {
+    try {
+        return fp8_gemm(d, in_scale, out_scale, stream);
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_fp8_w8a8_gemm: unexpected exception");
+    }
+}
+
 static wq_status sparse24_gemm(int bits, const void* d_x, int M, int K, int N, const void* d_vals, const void* d_meta,
                                const void* d_scales, int group_size, void* d_y, int act_dtype, void* stream,
                                const char* who) {
@@ -813,6 +935,51 @@ wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t
         return ok();
     } catch (...) {
         return fail(WQ_ERR_INVALID, "pack_w8: unexpected exception");
+    }
+}
+
+size_t wq_pack_fp8_bytes(int E, int n_out, int k_in) {
+    if (E <= 0 || n_out <= 0 || k_in <= 0 || n_out % 16 || k_in % wq::FP8_KCHUNK) return 0;
+    return (size_t)E * n_out * k_in;
+}
+
+// E4M3 codes: tiles of 16 rows x 128 channels (2 KiB), lane l's 32 bytes =
+// row l % 16, channels [32 (l / 16), +32) of the chunk
+wq_status wq_pack_fp8(int E, int n_out, int k_in, const uint8_t* codes, const float* scales, const int32_t* row_perm,
+                      int flags, void* packed, float* scales_packed) {
+    try {
+        WQ_REQUIRE(E > 0 && n_out > 0 && k_in > 0, WQ_ERR_INVALID, "pack_fp8: bad sizes");
+        const bool il = (flags & WQ_PACK_INTERLEAVE_GATE_UP) != 0;
+        WQ_REQUIRE(n_out % (il ? 32 : 16) == 0, WQ_ERR_UNSUPPORTED, "pack_fp8: n_out %d", n_out);
+        WQ_REQUIRE(k_in % wq::FP8_KCHUNK == 0, WQ_ERR_UNSUPPORTED, "pack_fp8: k_in %d not a multiple of %d", k_in,
+                   wq::FP8_KCHUNK);
+        WQ_REQUIRE(codes && scales && packed && scales_packed, WQ_ERR_INVALID, "pack_fp8: NULL buffer");
+        for (size_t i = 0, n = (size_t)E * n_out * k_in; i < n; ++i)
+            WQ_REQUIRE((codes[i] & 0x7f) != 0x7f, WQ_ERR_INVALID, "pack_fp8: NaN code at %zu", i);
+        for (size_t i = 0, n = (size_t)E * n_out; i < n; ++i)
+            WQ_REQUIRE(std::isfinite(scales[i]), WQ_ERR_INVALID, "pack_fp8: non-finite scale at %zu", i);
+        const int rows_perm = il ? n_out / 2 : n_out;
+        WQ_TRY(check_row_perm(E, rows_perm, row_perm));
+        const int C = k_in / wq::FP8_KCHUNK;
+        const size_t expert_bytes = (size_t)n_out * k_in;
+        uint8_t* out = static_cast<uint8_t*>(packed);
+        parallel_for(E * (n_out / 16), [&](int job) {
+            const int e = job / (n_out / 16), t = job % (n_out / 16);
+            const int32_t* pe = row_perm ? row_perm + (size_t)e * rows_perm : nullptr;
+            for (int l = 0; l < 64; ++l) {
+                const int p = t * 16 + (l & 15);
+                const uint8_t* qr = codes + ((size_t)e * n_out + logical_row(p, n_out, il, pe)) * k_in;
+                for (int c = 0; c < C; ++c)
+                    std::memcpy(out + (size_t)e * expert_bytes + (((size_t)t * C + c) * 64 + l) * 32,
+                                qr + (size_t)wq::FP8_KCHUNK * c + 32 * (l >> 4), 32);
+            }
+            if (t == 0)
+                for (int pp = 0; pp < n_out; ++pp)
+                    scales_packed[(size_t)e * n_out + pp] = scales[(size_t)e * n_out + logical_row(pp, n_out, il, pe)];
+        });
+        return ok();
+    } catch (...) {
+        return fail(WQ_ERR_INVALID, "pack_fp8: unexpected exception");
     }
 }
 

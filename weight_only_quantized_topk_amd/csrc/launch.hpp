@@ -46,6 +46,41 @@ struct GemmArgs {
     int cap;
 };
 
+// ---------------------------------------------------------------------------
+// FP8 (OCP E4M3) W8A8 grouped GEMM.  Packed weights: per expert, tiles of 16
+// output rows x 128 input channels = 2 KiB, lane l's 32 bytes = row l % 16,
+// channels [32 (l / 16), +32) of the chunk; one float32 scale per packed row.
+// Activations are E4M3 codes (x quantised by launch_fp8_quant, H by the
+// GATE_UP epilogue).
+// ---------------------------------------------------------------------------
+constexpr int FP8_KCHUNK = 128;
+constexpr int FP8_CHUNK_BYTES = 2048;
+
+struct Fp8GemmArgs {
+    const uint8_t* a;         // E4M3 rows: quantised x (GATE_UP / RAW) or H (DOWN)
+    const uint8_t* w;         // packed E4M3 weights, all experts
+    const float* s;           // per-row weight scales [E, n_out] in packed row order
+    const int32_t* sorted;
+    const int32_t* expert_ids;
+    const int32_t* ntpp;
+    const float* topk_w;      // DOWN
+    void* out;                // H codes (uint8) / Y or Z (f32)
+    int M, topk, E, n_out, k_in;
+    int block_size;
+    int a_direct;             // 1: A row = sorted position (H); 0: A row = token of the pair (x)
+    int cap;
+    float in_scale;           // scale of the A operand's codes (a1 for x, a2 for H)
+    float out_scale;          // GATE_UP: scale H is quantised with (a2)
+};
+
+// q[r, k] = E4M3 code of x[r, k] / scale (float32 division, clamped to +-448, nearest even)
+void launch_fp8_quant(const uint16_t* x, int64_t rows, int k, bool bf16, float scale, uint8_t* q, hipStream_t s);
+// grouped E4M3 GEMM, small-batch (weights streamed once per pass of token blocks) or
+// large-batch (token tiles in LDS, 16x16x128 MFMAs); returns the K slices DOWN wrote
+bool fp8_prefill_supported(int n_out, int k_in, int block_size);
+int fp8_down_split(int T, int E, int n_out, int k_in, int block_size);
+int launch_gemm_fp8(int stage, const Fp8GemmArgs& g, hipStream_t s);
+
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
 void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);

@@ -193,3 +193,96 @@ def fused_moe(x, logits, p: PackedMoE, topk: int, renormalize: bool = True, bloc
     r = MoERunner(p, x.shape[0], topk, renormalize, block_size, device=x.device)
     out = r(x, logits, stream=stream)
     return (out, r.aux()) if keep else out
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) W8A8 layer
+# ----------------------------------------------------------------------------
+@dataclass
+class PackedFp8MoE:
+    E: int
+    K: int
+    N: int
+    act: object     # torch dtype of the layer input and output
+    a1: float       # static scale of the layer input
+    a2: float       # static scale of H
+    w1: object      # packed E4M3 gate/up weights (device uint8)
+    s1: object      # float32 [E, 2N] packed row order
+    w2: object
+    s2: object
+
+    @property
+    def act_code(self) -> int:
+        return ops.act_code(self.act)
+
+
+def pack_moe_fp8(w1: np.ndarray, s1: np.ndarray, w2: np.ndarray, s2: np.ndarray, act, a1: float, a2: float,
+                 device="cuda") -> PackedFp8MoE:
+    """Canonical E4M3 codes (w1 [E,2N,K], w2 [E,K,N]) and float32 per-column
+    scales (s1 [E,2N], s2 [E,K]) -> device-resident packed layout."""
+    import torch
+    E, n2, K = w1.shape
+    w1p, s1p = ops.pack_fp8(w1, s1, interleave_gate_up=True)
+    w2p, s2p = ops.pack_fp8(w2, s2)
+
+    def dev(a):
+        return torch.from_numpy(a).to(device)
+
+    return PackedFp8MoE(E, K, n2 // 2, act, float(a1), float(a2), dev(w1p), dev(s1p), dev(w2p), dev(s2p))
+
+
+class Fp8MoERunner:
+    """The FP8 W8A8 hot path for one batch shape, buffers allocated up front:
+    route -> align -> GATE_UP (x quantised with a1, H written as E4M3 codes of
+    h / a2) -> DOWN (routed-weight sum, rounded once to the activation type)."""
+
+    def __init__(self, p: PackedFp8MoE, M: int, topk: int, renormalize: bool = True,
+                 block_size: Optional[int] = None, device="cuda"):
+        import torch
+        self.p, self.M, self.topk, self.renormalize = p, M, topk, renormalize
+        self.bs = choose_block_size(M, topk, p.E, 8) if block_size is None else block_size
+        self.cap = ops.moe_align_capacity(M, topk, p.E, self.bs)
+        dev = torch.device(device)
+        self.w = torch.empty((M, topk), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((M, topk), dtype=torch.int32, device=dev)
+        self.st = torch.empty(max(self.cap, 1), dtype=torch.int32, device=dev)
+        self.ex = torch.empty(max(self.cap // self.bs, 1), dtype=torch.int32, device=dev)
+        self.nt = torch.empty(4, dtype=torch.int32, device=dev)
+        ws1 = ops.moe_fp8_gemm_workspace_bytes(WQ_STAGE_GATE_UP, M, topk, p.E, 2 * p.N, p.K)
+        ws2 = ops.moe_fp8_gemm_workspace_bytes(WQ_STAGE_DOWN, M, topk, p.E, p.K, p.N)
+        self.work1 = torch.empty(max(ws1, 1), dtype=torch.uint8, device=dev)
+        self.work2 = torch.empty(max(ws2, 1), dtype=torch.uint8, device=dev)
+        self.h = torch.empty((max(self.cap, 1), p.N), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((M, p.K), dtype=p.act, device=dev)
+
+    def route_align(self, logits, stream=None):
+        ops.moe_route_align(logits, self.topk, self.renormalize, self.bs, self.w, self.ids, self.st, self.ex,
+                            self.nt, self.cap, stream=stream)
+
+    def gate_up(self, x, stream=None):
+        q = self.p
+        ops.moe_fp8_w8a8_gemm(WQ_STAGE_GATE_UP, x, self.M, self.topk, q.E, 2 * q.N, q.K, q.w1, q.s1, self.st,
+                              self.ex, self.nt, self.cap, self.bs, None, self.h, self.work1, q.a1, q.a2, stream,
+                              q.act_code)
+
+    def down(self, stream=None):
+        q = self.p
+        ops.moe_fp8_w8a8_gemm(WQ_STAGE_DOWN, self.h, self.M, self.topk, q.E, q.K, q.N, q.w2, q.s2, self.st,
+                              self.ex, self.nt, self.cap, self.bs, self.w, self.out, self.work2, q.a2, 1.0, stream,
+                              q.act_code)
+
+    __call__ = MoERunner.__call__
+    capture = MoERunner.capture
+    replay = MoERunner.replay
+
+    def aux(self):
+        return {"topk_weights": self.w, "topk_ids": self.ids, "sorted_token_ids": self.st, "expert_ids": self.ex,
+                "num_tokens_post_padded": self.nt, "h": self.h, "block_size": self.bs, "capacity": self.cap}
+
+
+def fused_moe_fp8(x, logits, p: PackedFp8MoE, topk: int, renormalize: bool = True,
+                  block_size: Optional[int] = None, stream=None, keep=False):
+    """x [M, K] act, logits [M, E] float32 -> out [M, K] act (FP8 W8A8 experts)."""
+    r = Fp8MoERunner(p, x.shape[0], topk, renormalize, block_size, device=x.device)
+    out = r(x, logits, stream=stream)
+    return (out, r.aux()) if keep else out

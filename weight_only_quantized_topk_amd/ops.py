@@ -19,7 +19,8 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
 __all__ = [
     "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
     "moe_w8a16_gemm_noalloc", "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
-    "pack_w4", "pack_w8", "pack_sparse24", "act_code",
+    "pack_w4", "pack_w8", "pack_sparse24", "act_code", "moe_fp8_gemm_workspace_bytes", "moe_fp8_w8a8_gemm",
+    "pack_fp8",
 ]
 
 
@@ -158,6 +159,40 @@ def moe_w8a16_gemm_noalloc(stage, a, M, topk, E, n_out, k_in, w_packed, scales, 
                  None, stream, act_dtype)
 
 
+def moe_fp8_gemm_workspace_bytes(stage: int, M: int, topk: int, E: int, n_out: int, k_in: int) -> int:
+    return int(load().moe_fp8_gemm_workspace_bytes(stage, M, topk, E, n_out, k_in))
+
+
+def moe_fp8_w8a8_gemm(stage, a, M, topk, E, n_out, k_in, w_packed, scales, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, capacity, block_size, topk_weights, out, workspace, in_scale: float,
+                      out_scale: float = 1.0, stream=None, act_dtype=WQ_BF16):
+    """FP8 (E4M3) W8A8 grouped GEMM: GATE_UP (x in act dtype -> H codes), DOWN
+    (H codes -> out in act dtype) or RAW (x -> fp32); in_scale / out_scale are
+    the static activation scales (a1, a2 for GATE_UP; a2 for DOWN)."""
+    d = WqMoeGemmDesc()
+    d.struct_size = C.sizeof(WqMoeGemmDesc)
+    d.stage = stage
+    d.act_dtype = act_dtype
+    d.d_a = _ptr(a)
+    d.M, d.topk, d.E, d.n_out, d.k_in = M, topk, E, n_out, k_in
+    d.d_w_packed = _ptr(w_packed)
+    d.d_scales = _ptr(scales)
+    d.group_size = -1
+    d.d_k_perm = None
+    d.d_sorted_token_ids = _ptr(sorted_token_ids)
+    d.d_expert_ids = _ptr(expert_ids)
+    d.d_num_tokens_post_padded = _ptr(num_tokens_post_padded)
+    d.capacity = capacity
+    d.block_size = block_size
+    d.d_topk_weights = _ptr(topk_weights)
+    d.d_out = _ptr(out)
+    d.d_workspace = _ptr(workspace)
+    d.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().moe_fp8_w8a8_gemm(C.byref(d), float(in_scale), float(out_scale), _stream(stream)),
+          "moe_fp8_w8a8_gemm")
+    return out
+
+
 def _sparse24(fn, x, vals, meta, scales, N, out, group_size, stream):
     torch = _torch()
     M, K = x.shape
@@ -269,6 +304,25 @@ def pack_w8(q: np.ndarray, scales_bits: np.ndarray, row_perm: Optional[np.ndarra
     flags = WQ_PACK_INTERLEAVE_GATE_UP if interleave_gate_up else 0
     check(L.wq_pack_w8(E, n_out, k_in, _np_ptr(q), _np_ptr(s), _np_ptr(rp), flags, _np_ptr(packed), _np_ptr(sp)),
           "wq_pack_w8")
+    return packed, sp
+
+
+def pack_fp8(codes: np.ndarray, scales: np.ndarray, row_perm: Optional[np.ndarray] = None,
+             interleave_gate_up: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """E4M3 codes uint8 [E, n_out, k_in], scales float32 [E, n_out] -> (packed uint8, scales float32)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    E, n_out, k_in = c.shape
+    s = np.ascontiguousarray(scales, dtype=np.float32).reshape(E, n_out)
+    L = load()
+    nbytes = int(L.wq_pack_fp8_bytes(E, n_out, k_in))
+    if nbytes == 0:
+        raise ValueError("unsupported FP8 shape %s" % (c.shape,))
+    packed = np.empty(nbytes, np.uint8)
+    sp = np.empty_like(s)
+    rp = None if row_perm is None else np.ascontiguousarray(row_perm, dtype=np.int32)
+    flags = WQ_PACK_INTERLEAVE_GATE_UP if interleave_gate_up else 0
+    check(L.wq_pack_fp8(E, n_out, k_in, _np_ptr(c), _np_ptr(s), _np_ptr(rp), flags, _np_ptr(packed), _np_ptr(sp)),
+          "wq_pack_fp8")
     return packed, sp
 
 
