@@ -51,8 +51,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}   # dense
 FLUSH_BYTES = 1 << 30
+PackedFp8MoE = ()  # the FP8 layer's packed type, bound in main() once the package is imported
 # rocprofv3 counter summary of the large-batch gate/up kernel at the default
 # workload; its traffic figure is used only while the kernel sources hash the same
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_prefill_gate_up_mixtral_w8a16_m1024.md")
@@ -105,13 +106,15 @@ def moe_alg_counts(spec, M, ids_np, packed):
     T = M * spec.topk
     E = spec.E
     act = 2
+    fp8 = isinstance(packed, PackedFp8MoE)
     w1_bytes = packed.w1.numel() // E * touched
-    s1_bytes = packed.s1.numel() * 2 // E * touched
+    s1_bytes = packed.s1.numel() * packed.s1.element_size() // E * touched
     w2_bytes = packed.w2.numel() // E * touched
-    s2_bytes = packed.s2.numel() * 2 // E * touched
-    perm_bytes = touched * spec.K * 4 if spec.act_order else 0
+    s2_bytes = packed.s2.numel() * packed.s2.element_size() // E * touched
+    perm_bytes = touched * spec.K * 4 if getattr(spec, "act_order", False) else 0
+    h_bytes = 1 if fp8 else act  # FP8 writes H as 1-byte codes
     g1 = {
-        "bytes": w1_bytes + s1_bytes + M * spec.K * act + T * spec.N * act,
+        "bytes": w1_bytes + s1_bytes + M * spec.K * act + T * spec.N * h_bytes,
         "flops": 2 * T * (2 * spec.N) * spec.K,
     }
     layer = {
@@ -121,10 +124,12 @@ def moe_alg_counts(spec, M, ids_np, packed):
     return touched, g1, layer
 
 
-def rates(nbytes, flops, ms):
+def rates(nbytes, flops, ms, peak_tf=2500.0):
+    """GB/s and TFLOP/s of a launch, with fractions of the HBM peak and of the
+    dense MFMA peak of its data type (2.5 PFLOP/s bf16/fp16, 5.0 fp8)."""
     gbps = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
-    return {"GBps": gbps, "TFLOPs": tf, "frac_hbm": gbps / HBM_PEAK_GBPS, "frac_mfma": tf / 2500.0}
+    return {"GBps": gbps, "TFLOPs": tf, "frac_hbm": gbps / HBM_PEAK_GBPS, "frac_mfma": tf / peak_tf}
 
 
 def rounded(d):
@@ -236,7 +241,8 @@ def measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup):
     toks = gen.make_tokens(spec, m)
     x = torch.from_numpy(toks.x.view(np.int16)).cuda().view(act)
     lg = torch.from_numpy(toks.logits).cuda()
-    runner = wq.MoERunner(packed, m, spec.topk, spec.renormalize)
+    fp8 = isinstance(packed, PackedFp8MoE)
+    runner = (wq.Fp8MoERunner if fp8 else wq.MoERunner)(packed, m, spec.topk, spec.renormalize)
     spans, wall = timer.run(lambda marks: runner(x, lg, marks=marks), steps, warmup, 3)
     ra, g1e, lay = spans[:, 0], spans[:, 1] - spans[:, 0], spans[:, 2]
     down = spans[:, 2] - spans[:, 1]
@@ -261,8 +267,9 @@ def measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup):
              down_ms=float(down.mean()), touched_experts=touched, block_size=runner.bs,
              gate_up_alg_bytes=g1["bytes"], gate_up_alg_flops=g1["flops"],
              layer_alg_bytes=layer["bytes"], layer_alg_flops=layer["flops"])
-    r.update({"gate_up_" + k: v for k, v in rates(g1["bytes"], g1["flops"], r["gate_up_ms"]).items()})
-    r.update({"layer_" + k: v for k, v in rates(layer["bytes"], layer["flops"], ms).items()})
+    peak = MFMA_PEAK_TFLOPS["fp8" if fp8 else spec.act]
+    r.update({"gate_up_" + k: v for k, v in rates(g1["bytes"], g1["flops"], r["gate_up_ms"], peak).items()})
+    r.update({"layer_" + k: v for k, v in rates(layer["bytes"], layer["flops"], ms, peak).items()})
     return toks, r
 
 
@@ -320,53 +327,68 @@ def measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup):
     return r
 
 
-def bench_rows(torch, wq, gen, timer, steps, warmup):
-    """The other workloads at their batch sizes: layer time, stage times and
-    both roofline fractions (HBM on algorithmic bytes, MFMA on algorithmic flops)."""
-    rows = []
-    for cid in (3, 5):
-        spec = gen.CONFIGS[cid]
-        act = torch.float16 if spec.act == "f16" else torch.bfloat16
-        log("bench: rows: generating and packing %s" % spec.name)
-        wts = gen.make_moe_weights(spec)
-        packed = wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2, act, spec.group_size, wts.g1, wts.g2)
-        del wts
-        for m in spec.m_sweep:
+ROW_NAMES = ("mixtral-w4a16-actorder", "deepseekv2-w8a16", "mixtral-fp8-w8a8", "sparse24-w4a16", "sparse24-w8a16",
+             "dense-w4a16", "quantize-w8")
+
+
+def bench_row(name, torch, wq, gen, timer, steps, warmup, ms=None):
+    """One of the other workloads at its batch sizes (or `ms`): layer time,
+    stage times and both roofline fractions (HBM on algorithmic bytes, MFMA on
+    algorithmic flops)."""
+    out = []
+    if name in ("mixtral-w4a16-actorder", "deepseekv2-w8a16", "mixtral-fp8-w8a8"):
+        if name == "mixtral-fp8-w8a8":
+            spec = gen.CFG_FP8  # the pages' comparison method, the same Mixtral shape and batch sizes
+            log("bench: rows: generating and packing %s" % spec.name)
+            fw = gen.make_fp8_weights(spec)
+            packed = wq.pack_moe_fp8(fw.w1, fw.s1, fw.w2, fw.s2, torch.bfloat16, spec.a1, spec.a2)
+            del fw
+        else:
+            spec = gen.CONFIGS[3 if name == "mixtral-w4a16-actorder" else 5]
+            act = torch.float16 if spec.act == "f16" else torch.bfloat16
+            log("bench: rows: generating and packing %s" % spec.name)
+            wts = gen.make_moe_weights(spec)
+            packed = wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2, act, spec.group_size, wts.g1, wts.g2)
+            del wts
+        for m in (ms or spec.m_sweep):
             _, r = measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup)
             log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
-            rows.append(dict(workload=spec.name, **rounded(r)))
+            out.append(dict(workload=spec.name, **rounded(r)))
         del packed
-        torch.cuda.empty_cache()
-    spec = gen.CFG4
-    log("bench: rows: generating and packing %s" % spec.name)
-    sw = gen.make_sparse_weights(spec)
-    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s)
-    dev = (torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(), torch.from_numpy(sp.view(np.int16)).cuda())
-    for m in spec.m_sweep:
-        r = measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup)
-        log("bench: rows: %s M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
-        rows.append(dict(workload=spec.name, **rounded(r)))
-    del dev
-    spec8 = spec.with_(bits=8)                 # the 2:4 support's 8-bit variant, same shape
-    log("bench: rows: generating and packing %s (8-bit)" % spec.name)
-    sw = gen.make_sparse_weights(spec8)
-    vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, bits=8)
-    dev = (torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(), torch.from_numpy(sp.view(np.int16)).cuda())
-    for m in spec.m_sweep:
-        r = measure_sparse(torch, wq, gen, timer, spec8, dev, m, steps, warmup)
-        log("bench: rows: %s 8-bit M=%d %.4f ms/step" % (spec.name, m, r["ms_per_step"]))
-        rows.append(dict(workload="yi34b-mlp-sparse24-w8a16", **rounded(r)))
-    del dev
-    log("bench: rows: generating and packing the dense int4 layer")
-    ddev = dense_weights(torch, wq, spec)
-    for m in spec.m_sweep:
-        r = measure_dense(torch, wq, gen, timer, spec, ddev, m, steps, warmup)
-        log("bench: rows: dense M=%d %.4f ms/step" % (m, r["ms_per_step"]))
-        rows.append(dict(workload="yi34b-mlp-dense-w4a16", **rounded(r)))
-    del ddev
-    rows.append(dict(workload="experts-int8-quantize-mixtral-w1", **rounded(measure_quant(torch, wq, timer, steps,
-                                                                                         warmup))))
-    log("bench: rows: quantizer %.4f ms" % rows[-1]["ms_per_step"])
+    elif name in ("sparse24-w4a16", "sparse24-w8a16"):
+        spec = gen.CFG4 if name == "sparse24-w4a16" else gen.CFG4.with_(bits=8)  # 8-bit: the 2:4 support's variant
+        log("bench: rows: generating and packing %s (%d-bit)" % (spec.name, spec.bits))
+        sw = gen.make_sparse_weights(spec)
+        vp, mp, sp = wq.pack_sparse24(sw.vals, sw.idx, sw.s, bits=spec.bits)
+        dev = (torch.from_numpy(vp).cuda(), torch.from_numpy(mp).cuda(), torch.from_numpy(sp.view(np.int16)).cuda())
+        for m in (ms or spec.m_sweep):
+            r = measure_sparse(torch, wq, gen, timer, spec, dev, m, steps, warmup)
+            log("bench: rows: %s %d-bit M=%d %.4f ms/step" % (spec.name, spec.bits, m, r["ms_per_step"]))
+            out.append(dict(workload=spec.name if spec.bits == 4 else "yi34b-mlp-sparse24-w8a16", **rounded(r)))
+        del dev
+    elif name == "dense-w4a16":
+        spec = gen.CFG4
+        log("bench: rows: generating and packing the dense int4 layer")
+        ddev = dense_weights(torch, wq, spec)
+        for m in (ms or spec.m_sweep):
+            r = measure_dense(torch, wq, gen, timer, spec, ddev, m, steps, warmup)
+            log("bench: rows: dense M=%d %.4f ms/step" % (m, r["ms_per_step"]))
+            out.append(dict(workload="yi34b-mlp-dense-w4a16", **rounded(r)))
+        del ddev
+    elif name == "quantize-w8":
+        out.append(dict(workload="experts-int8-quantize-mixtral-w1", **rounded(measure_quant(torch, wq, timer, steps,
+                                                                                             warmup))))
+        log("bench: rows: quantizer %.4f ms" % out[-1]["ms_per_step"])
+    else:
+        raise ValueError("unknown row %r (one of %s)" % (name, ", ".join(ROW_NAMES)))
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_rows(torch, wq, gen, timer, steps, warmup):
+    rows = []
+    for name in ROW_NAMES:
+        rows += bench_row(name, torch, wq, gen, timer, steps, warmup)
     return rows
 
 
@@ -425,6 +447,41 @@ def measure_quant(torch, wq, timer, steps, warmup):
     return r
 
 
+def summarize_counters(paths, calib_kernel="__amd_rocclr_copyBuffer", calib_bytes=None):
+    """Counter summary of rocprofv3 --pmc CSV files (counter_collection.csv):
+    per (kernel, grid size), the mean value per dispatch of every counter.
+    With calib_bytes (the bytes one dispatch of calib_kernel moves), FETCH_SIZE
+    and WRITE_SIZE (KiB) are also scaled by known_KiB / counted_KiB of that
+    kernel (the calibration copy of --copy-calibration) and given in bytes."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+                acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    scale = {}
+    if calib_bytes:
+        # the calibration copy is the calib_kernel dispatch with the largest count
+        # (the runtime also copies small host buffers with it)
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            counted = [float(np.mean(cs[c])) for (name, _, _), cs in acc.items() if name.startswith(calib_kernel) and c in cs]
+            if counted and max(counted) > 0:
+                scale[c] = (calib_bytes / 1024.0) / max(counted)
+    out = []
+    for (name, grid, wg), counters in sorted(acc.items(), key=lambda kv: kv[0]):
+        row = {"kernel": name, "grid": grid, "workgroup": wg}
+        for c, v in sorted(counters.items()):
+            row[c] = float(np.mean(v))
+            row[c + "_dispatches"] = len(v)
+            if c in scale:
+                row[c + "_bytes"] = row[c] * 1024.0 * scale[c]
+                row[c + "_scale"] = scale[c]
+        out.append(row)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,10 +495,24 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="how the last-level cache is emptied before every step (1 GiB read or written)")
+    ap.add_argument("--row", choices=ROW_NAMES, default=None,
+                    help="time only this one of the other workloads (at --m, else its batch sizes) and print its "
+                         "results as one JSON line (for profiling a single kernel)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a device-to-device copy of MIB MiB twice: the known-size reference that "
                          "scales hardware byte counters (FETCH_SIZE / WRITE_SIZE) read under a profiler")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV", default=None,
+                    help="print a per-kernel summary (one JSON line per kernel and grid) of rocprofv3 --pmc CSV "
+                         "files and exit; FETCH_SIZE / WRITE_SIZE are scaled by the --copy-calibration copy "
+                         "when --calib-mib gives its size")
+    ap.add_argument("--calib-mib", type=int, default=None, help="size of the calibration copy (MiB)")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        for row in summarize_counters(args.summarize_counters,
+                                      calib_bytes=(args.calib_mib << 20) if args.calib_mib else None):
+            print(json.dumps(row))
+        return 0
 
     if args.gpus != 1:
         print("bench.py: the benchmark runs on one GPU; --gpus %d is not supported (the layer is not sharded "
@@ -452,6 +523,8 @@ def main(argv=None):
     import torch
     import gen
     import weight_only_quantized_topk_amd as wq
+    global PackedFp8MoE
+    PackedFp8MoE = wq.PackedFp8MoE
 
     wq.load()  # fails loudly without the HIP library
     torch.cuda.set_device(0)
@@ -465,6 +538,10 @@ def main(argv=None):
         log("bench: copied %d bytes twice (counter calibration)" % n)
         del src, dst
     timer = Timer(torch, args.flush)
+    if args.row:
+        res = bench_row(args.row, torch, wq, gen, timer, args.steps, args.warmup, [args.m] if args.m else None)
+        print(json.dumps({"row": args.row, "results": res}), flush=True)
+        return 0
     spec = gen.CONFIGS[args.config]
     M = args.m or max(spec.m_sweep)
     act = torch.float16 if spec.act == "f16" else torch.bfloat16

@@ -378,7 +378,7 @@ wq_status wq_pack_w8(int E, int n_out, int k_in, const int8_t* q, const uint16_t
 /*
  * FP8 packer: codes uint8 [E, n_out, k_in] (E4M3, no NaN), scales float32
  * [E, n_out] -> packed (wq_pack_fp8_bytes: E * n_out * k_in bytes, tiles of 16
- * rows x 128 channels) and scales_packed float32 [E, n_out] in packed row
+ * rows x 128 channels, 2 KiB each) and scales_packed float32 [E, n_out] in packed row
  * order; row_perm and flags as for wq_pack_w8.  Limits: n_out % 16 == 0 (% 32
  * with interleave), k_in % 128 == 0.
  */

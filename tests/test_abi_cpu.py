@@ -335,3 +335,59 @@ def test_packer_rejects_bad_input():
     idx[0, 0], idx[0, 1] = 2, 1
     with pytest.raises(wq.WqError):
         wq.pack_sparse24(np.zeros((16, 128), np.int8), idx, np.ones((2, 16), np.uint16))
+
+
+def test_pack_fp8_layout():
+    """The FP8 packer: tiles of 16 rows x 128 channels (2 KiB); lane l's 32
+    channels [32 (l / 16), +32) of row l % 16 in two halves, at 16 l and
+    1024 + 16 l of the tile; gate/up interleave as for the int8 packer; float32
+    scales in packed row order."""
+    rng = np.random.default_rng(3)
+    E, n_out, k_in = 2, 64, 256
+    codes = rng.integers(0, 256, size=(E, n_out, k_in), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0  # no NaN codes
+    scales = rng.uniform(0.5, 2.0, size=(E, n_out)).astype(np.float32)
+    for il in (False, True):
+        packed, sp = wq.pack_fp8(codes, scales, interleave_gate_up=il)
+        C = k_in // 128
+        t = packed.reshape(E, n_out // 16, C, 2, 64, 16)   # e, tile, chunk, half, lane, byte
+        rows = logical_rows(n_out, il)
+        for e in range(E):
+            for p in range(n_out):
+                lr = rows[p]
+                assert sp[e, p] == scales[e, lr]
+                got = np.empty(k_in, np.uint8)
+                for l in range(64):
+                    if l % 16 != p % 16:
+                        continue
+                    for c in range(C):
+                        for h in range(2):
+                            k0 = 128 * c + 32 * (l // 16) + 16 * h
+                            got[k0:k0 + 16] = t[e, p // 16, c, h, l]
+                assert np.array_equal(got, codes[e, lr]), (il, e, p)
+    bad = codes.copy()
+    bad[0, 0, 0] = 0x7F
+    with pytest.raises(wq.WqError):
+        wq.pack_fp8(bad, scales)
+
+
+def test_fp8_gemm_validation():
+    """moe_fp8_w8a8_gemm rejects bad scales, shapes and formats before any device work."""
+    L = wq.load()
+    assert L.moe_fp8_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 8, 1024, 256) == 1024  # x codes, 256-rounded
+    assert L.moe_fp8_gemm_workspace_bytes(wq.WQ_STAGE_DOWN, 4, 2, 8, 256, 512) == 4 * 2 * 256 * 4
+    def st(**kw):
+        scales = kw.pop("scales", (1 / 64, 1 / 16))
+        kw.setdefault("group_size", -1)
+        d = _desc(**kw)
+        d.d_workspace, d.workspace_bytes = FAKE, 1 << 30
+        return L.moe_fp8_w8a8_gemm(C.byref(d), scales[0], scales[1], None)
+    assert st(k_in=192) == wq.WQ_ERR_UNSUPPORTED          # k_in % 128
+    assert st(group_size=128) == wq.WQ_ERR_UNSUPPORTED
+    assert st(d_k_perm=FAKE) == wq.WQ_ERR_INVALID
+    assert st(scales=(0.0, 1.0)) == wq.WQ_ERR_INVALID      # in_scale must be > 0
+    assert st(scales=(float("nan"), 1.0)) == wq.WQ_ERR_INVALID
+    assert st(scales=(1.0, -1.0)) == wq.WQ_ERR_INVALID     # GATE_UP needs out_scale > 0
+    assert st(n_out=1008) == wq.WQ_ERR_UNSUPPORTED         # gate/up n_out % 32
+    assert st(d_a=None) == wq.WQ_ERR_INVALID
+    assert st(M=0) == wq.WQ_OK

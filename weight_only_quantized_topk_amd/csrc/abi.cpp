@@ -943,8 +943,10 @@ size_t wq_pack_fp8_bytes(int E, int n_out, int k_in) {
     return (size_t)E * n_out * k_in;
 }
 
-// E4M3 codes: tiles of 16 rows x 128 channels (2 KiB), lane l's 32 bytes =
-// row l % 16, channels [32 (l / 16), +32) of the chunk
+// E4M3 codes: tiles of 16 rows x 128 channels (2 KiB).  Lane l's MFMA operand
+// is row l % 16, channels [32 (l / 16), +32) of the chunk; its first 16
+// channels sit at bytes 16 l of the chunk and the other 16 at 1024 + 16 l, so
+// each of a wave's two 128-bit loads reads one contiguous KiB
 wq_status wq_pack_fp8(int E, int n_out, int k_in, const uint8_t* codes, const float* scales, const int32_t* row_perm,
                       int flags, void* packed, float* scales_packed) {
     try {
@@ -970,8 +972,9 @@ wq_status wq_pack_fp8(int E, int n_out, int k_in, const uint8_t* codes, const fl
                 const int p = t * 16 + (l & 15);
                 const uint8_t* qr = codes + ((size_t)e * n_out + logical_row(p, n_out, il, pe)) * k_in;
                 for (int c = 0; c < C; ++c)
-                    std::memcpy(out + (size_t)e * expert_bytes + (((size_t)t * C + c) * 64 + l) * 32,
-                                qr + (size_t)wq::FP8_KCHUNK * c + 32 * (l >> 4), 32);
+                    for (int h = 0; h < 2; ++h)
+                        std::memcpy(out + (size_t)e * expert_bytes + ((size_t)t * C + c) * 2048 + 1024 * h + 16 * l,
+                                    qr + (size_t)wq::FP8_KCHUNK * c + 32 * (l >> 4) + 16 * h, 16);
             }
             if (t == 0)
                 for (int pp = 0; pp < n_out; ++pp)

@@ -12,8 +12,9 @@
 //  - fp8_decode_kernel (block 16 / 32): the small-batch shape of the int8
 //    path -- a workgroup per (up to RMAX 16-row token blocks of one expert,
 //    16 or 32 weight rows), its waves splitting the input channels, the
-//    weights streamed once from HBM (2 KiB chunk = 32 bytes per lane = one
-//    MFMA A operand), the token codes (B operand) read from L2.
+//    weights streamed once from HBM (a 2 KiB chunk is one MFMA A operand per
+//    lane, loaded by two contiguous 1 KiB wave loads), the token codes (B
+//    operand) read from L2.
 //  - fp8_prefill_kernel (blocks of 64 / 128+): BN weight rows x BM token rows
 //    per workgroup; the weights are loaded straight into the A registers one
 //    K step ahead, the token rows of a step staged in one of two LDS buffers.
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
     const uint8_t* wt[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-        wt[t] = g.w + (size_t)e * expert_bytes + (size_t)(NT * unit + t) * C * FP8_CHUNK_BYTES + lane * 32;
+        wt[t] = g.w + (size_t)e * expert_bytes + (size_t)(NT * unit + t) * C * FP8_CHUNK_BYTES + lane * 16;
     const float* se = g.s + (size_t)e * g.n_out;
     const int rowq = 4 * (lane >> 4);
 
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 wv[d][t] = cat8(ldg128_stream(wt[t] + (size_t)c * FP8_CHUNK_BYTES),
-                                ldg128_stream(wt[t] + (size_t)c * FP8_CHUNK_BYTES + 16));
+                                ldg128_stream(wt[t] + (size_t)c * FP8_CHUNK_BYTES + 1024));
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 xv[d][r] = cat8(ldg128(arow[r] + c * FP8_KCHUNK), ldg128(arow[r] + c * FP8_KCHUNK + 16));
@@ -303,10 +304,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t fp8_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
 
-// 16-byte piece ch of token row `row` sits at piece ch ^ ((row >> 1) & 7):
-// the 16 lanes of one B read (16 consecutive rows, one piece) and of one
-// store (2 rows, 8 pieces) hit 16 distinct 16-byte bank groups
+// A token row of one K step is 8 pieces of 16 bytes (channels 16 p .. 16 p +
+// 15).  Lane group g of an MFMA reads channels [32 g, 32 g + 32), pieces 2 g
+// and 2 g + 1, so piece p is kept in slot (p >> 1) + 4 (p & 1): the first
+// read of lane group g is slot g, the second slot 4 + g.  Slot ch of row `row`
+// sits at ch ^ ((row >> 1) & 7) of the row.  A B read (16 rows x one slot
+// per lane group) and a store (rows x all 8 slots) then fall on distinct
+// 16-byte bank groups for each 32 lanes (with the two reads of a lane in
+// slots g and 2 g + 1 instead, 2 LDS conflict cycles per LDS instruction
+// were counted)
 __device__ __forceinline__ int fp8_lds_off(int row, int ch) { return row * FP8_ROWB + ((ch ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ int fp8_slot(int piece) { return (piece >> 1) + 4 * (piece & 1); }
 
 template <int STAGE, int NW, int RT, int BM, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g) {
@@ -344,14 +352,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g
     const int rt0 = ntile * (BN / TILE_ROWS) + __builtin_amdgcn_readfirstlane(wave) * RT;
     const int tile_stride = C * FP8_CHUNK_BYTES;
     const __amdgpu_buffer_rsrc_t wres = fp8_rsrc(g.w + (size_t)e * expert_bytes + (size_t)rt0 * tile_stride);
-    const int wlane = lane * 32;
+    const int wlane = lane * 16;
     u32x8 wA[RT], wB[RT];  // the A operands of two K steps
     auto wload = [&](int step, u32x8 (&w)[RT]) {
 #pragma unroll
         for (int t = 0; t < RT; ++t)
             w[t] = cat8(__builtin_amdgcn_raw_buffer_load_b128(wres, wlane, t * tile_stride + step * FP8_CHUNK_BYTES, 0),
-                        __builtin_amdgcn_raw_buffer_load_b128(wres, wlane + 16, t * tile_stride + step * FP8_CHUNK_BYTES,
-                                                              0));
+                        __builtin_amdgcn_raw_buffer_load_b128(wres, wlane + 1024,
+                                                              t * tile_stride + step * FP8_CHUNK_BYTES, 0));
     };
     // token pieces: pad rows read a valid row (their outputs are dropped, H pad rows written as 0)
     const __amdgpu_buffer_rsrc_t ares = fp8_rsrc(g.a);
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g
 #pragma unroll
         for (int i = 0; i < TPIECES; ++i) {
             const int id = tid + NT * i;
-            *reinterpret_cast<u32x4*>(buf + fp8_lds_off(id >> 3, id & 7)) = tv[i];
+            *reinterpret_cast<u32x4*>(buf + fp8_lds_off(id >> 3, fp8_slot(id & 7))) = tv[i];
         }
     };
 
@@ -389,11 +397,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g
     const bool full = jact > TJ / 2;  // else the second half of the token tiles is padding only
     constexpr int HALF = TJ / 2;
 
-    // B operand of token tile j: the lane's 32 bytes of its row, pieces 2 g4 and 2 g4 + 1
+    // B operand of token tile j: the lane's 32 bytes of its row, pieces 2 g4 and 2 g4 + 1 (slots g4, 4 + g4)
     auto bread = [&](int j, const uint8_t* cur) {
         const int r = 16 * j + brow;
-        return cat8(*reinterpret_cast<const u32x4*>(cur + fp8_lds_off(r, 2 * g4)),
-                    *reinterpret_cast<const u32x4*>(cur + fp8_lds_off(r, 2 * g4 + 1)));
+        return cat8(*reinterpret_cast<const u32x4*>(cur + fp8_lds_off(r, g4)),
+                    *reinterpret_cast<const u32x4*>(cur + fp8_lds_off(r, 4 + g4)));
     };
     auto body = [&](int step, const uint8_t* cur, uint8_t* nxt, u32x8 (&a)[RT]) {
         tstore(nxt);

@@ -48,8 +48,9 @@ struct GemmArgs {
 
 // ---------------------------------------------------------------------------
 // FP8 (OCP E4M3) W8A8 grouped GEMM.  Packed weights: per expert, tiles of 16
-// output rows x 128 input channels = 2 KiB, lane l's 32 bytes = row l % 16,
-// channels [32 (l / 16), +32) of the chunk; one float32 scale per packed row.
+// output rows x 128 input channels = 2 KiB; lane l's 32-byte MFMA operand (row
+// l % 16, channels [32 (l / 16), +32) of the chunk) is split in two 16-byte
+// halves at bytes 16 l and 1024 + 16 l; one float32 scale per packed row.
 // Activations are E4M3 codes (x quantised by launch_fp8_quant, H by the
 // GATE_UP epilogue).
 // ---------------------------------------------------------------------------
