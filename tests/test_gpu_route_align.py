@@ -104,12 +104,15 @@ def test_align_deterministic():
 
 
 @pytest.mark.parametrize("M,E,topk", [(1, 8, 2), (7, 8, 2), (16, 160, 6), (17, 160, 6), (64, 8, 2), (300, 160, 6),
-                                      (12, 1024, 8), (33, 1024, 8), (16, 2, 2)])
-@pytest.mark.parametrize("bs", [16, 64, 128])
+                                      (12, 1024, 8), (33, 1024, 8), (16, 2, 2),
+                                      # single-wave sort: up to 64 pairs over up to 64 experts
+                                      (1, 1, 1), (16, 64, 4), (11, 33, 5), (3, 4, 4), (16, 8, 2), (8, 65, 8)])
+@pytest.mark.parametrize("bs", [16, 64, 128, 256])
 @pytest.mark.parametrize("renorm", [True, False])
 def test_route_align_fused_equals_two_calls(M, E, topk, bs, renorm):
-    """moe_route_align (one kernel up to 16 tokens, two above) gives exactly
-    the outputs of moe_route followed by moe_align."""
+    """moe_route_align (one kernel up to 16 tokens -- one wave sorting the
+    pairs when there are at most 64 of them over at most 64 experts -- two
+    above) gives exactly the outputs of moe_route followed by moe_align."""
     need_gpu()
     rng = np.random.default_rng(1000 + M + E + bs)
     logits = rng.standard_normal((M, E)).astype(np.float32)

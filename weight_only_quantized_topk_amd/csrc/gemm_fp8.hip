@@ -407,16 +407,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g
         tstore(nxt);
         tload(min(step + 2, step_end - 1));
         u32x8 bx = bread(0, cur), by;
+        // MFMAs of token tiles j >= jact (padding only) are skipped
         static_for<0, HALF>([&](auto J) {
             constexpr int j = decltype(J)::value;
             if constexpr (j % 2 == 0) {
                 by = bread(j + 1, cur);
+                if (j == 0 || j < jact) {
 #pragma unroll
-                for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], bx, acc[t][j]);
+                    for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], bx, acc[t][j]);
+                }
             } else {
                 if constexpr (j + 1 < TJ) bx = bread(j + 1, cur);
+                if (j < jact) {
 #pragma unroll
-                for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], by, acc[t][j]);
+                    for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], by, acc[t][j]);
+                }
             }
         });
         if (full) {
@@ -424,12 +429,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g
                 constexpr int j = decltype(J)::value;
                 if constexpr (j % 2 == 0) {
                     if constexpr (j + 1 < TJ) by = bread(j + 1, cur);
+                    if (j < jact) {
 #pragma unroll
-                    for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], bx, acc[t][j]);
+                        for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], bx, acc[t][j]);
+                    }
                 } else {
                     if constexpr (j + 1 < TJ) bx = bread(j + 1, cur);
+                    if (j < jact) {
 #pragma unroll
-                    for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], by, acc[t][j]);
+                        for (int t = 0; t < RT; ++t) acc[t][j] = mfma_e4m3(a[t], by, acc[t][j]);
+                    }
                 }
             });
         }

@@ -27,9 +27,10 @@
 //    output rows 4 (l/16) + r of a weight tile for token row l % 16.  With the
 //    gate/up interleave of the packer, weight tile 2q holds 16 gate rows and
 //    tile 2q + 1 the matching up rows, so SiLU(gate) * up is lane-local.
-//  - When the valid rows of a BM slice (a prefix: the alignment pads each
-//    expert at the end) fit in its first half, the MFMAs of the second half
-//    are skipped (one uniform branch per K step).
+//  - The valid rows of a BM slice are a prefix (the alignment pads each
+//    expert at the end): the MFMAs of 16-row token tiles past them are skipped
+//    (one uniform branch per tile), and when they fit in the slice's first
+//    half the LDS reads of the second half too.
 //
 // DOWN may split K over gridDim.z slices when its output grid is too small to
 // fill the chip: slice z writes its partial sums to its own fp32 slab of Y and
@@ -159,7 +160,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
     int jact = 0;  // token tiles holding a valid row (a prefix: the alignment pads each expert at the end)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) jact += __builtin_amdgcn_readfirstlane(g.sorted[row0 + 16 * j]) < T ? 1 : 0;
-    const bool full = jact > TJ / 2;  // else the second half of the token tiles is padding only
+    // the MFMAs of token tiles j >= jact (padding only) are skipped, one
+    // uniform branch per tile; the second half's LDS reads too when jact <= TJ/2
+    // (DeepSeek-V2 shape, 4096 tokens: 75 of its 293 token tiles hold at most 16 rows)
+    const bool full = jact > TJ / 2;
     // One K step multiplies this step's weights (dequantized during the
     // previous step, in registers) by the token tile in `cur`, and spreads the
     // dequantization of the next step's weights over the MFMAs of the first
@@ -209,10 +213,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
             constexpr int j = decltype(J)::value;
             if constexpr (j % 2 == 0) {
                 bread(j + 1, cur, by);
-                mma(J, bx, ac);
+                if (j == 0 || j < jact) mma(J, bx, ac);
             } else {
                 bread(j + 1, cur, bx);
-                mma(J, by, ac);
+                if (j < jact) mma(J, by, ac);
             }
             static_for<j * PIECES / HALF, (j + 1) * PIECES / HALF>([&](auto P) {
                 deq(an, P);
@@ -227,10 +231,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
                 constexpr int j = decltype(J)::value;
                 if constexpr ((j - HALF) % 2 == 0) {
                     if constexpr (j + 1 < TJ) bread(j + 1, cur, by);
-                    mma(J, HALF % 2 == 0 ? bx : by, ac);
+                    if (j < jact) mma(J, HALF % 2 == 0 ? bx : by, ac);
                 } else {
                     if constexpr (j + 1 < TJ) bread(j + 1, cur, bx);
-                    mma(J, HALF % 2 == 0 ? by : bx, ac);
+                    if (j < jact) mma(J, HALF % 2 == 0 ? by : bx, ac);
                 }
             });
         }

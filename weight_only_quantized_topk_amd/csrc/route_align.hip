@@ -230,6 +230,60 @@ __global__ __launch_bounds__(ALIGN_THREADS) void route_align_kernel(const float*
     align_body(sids, M * topk, E, BS, nbits, sorted, expert_ids, ntpp, cap, smem);
 }
 
+// ---------------------------------------------------------------------------
+// moe_route + moe_align for the smallest batches (at most 64 pairs over at
+// most 64 experts): one wave per token routes it (as route_kernel does, so
+// the weights are the same bits), and after the only barrier wave 0 sorts
+// the pairs alone -- lane i holds pair i, lane e expert e: ranks and counts by
+// shuffles, the padded offsets by a wave scan -- with no further block-wide
+// synchronisation (the 1024-thread align took 7-8 us for one token).
+// ---------------------------------------------------------------------------
+constexpr int ROUTE_ALIGN_WAVE_MAX = 64;  // pairs and experts
+
+__global__ __launch_bounds__(1024) void route_align_wave_kernel(const float* __restrict__ logits, int M, int E,
+                                                                int topk, int renormalize, float* __restrict__ w_out,
+                                                                int32_t* __restrict__ ids_out, int BS,
+                                                                int32_t* __restrict__ sorted,
+                                                                int32_t* __restrict__ expert_ids,
+                                                                int32_t* __restrict__ ntpp, int cap) {
+    __shared__ int sids[ROUTE_ALIGN_WAVE_MAX];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    for (int m = wave; m < M; m += nw)
+        route_token(logits + (size_t)m * E, E, topk, renormalize, lane, w_out + (size_t)m * topk,
+                    ids_out + (size_t)m * topk, sids + m * topk);
+    __syncthreads();
+    if (wave != 0) return;
+    const int T = M * topk;
+    const int my_e = lane < T ? sids[lane] : -1;  // pair lane's expert
+    int rank = 0, cnt = 0;                         // rank among its expert's pairs; count of expert `lane`
+    for (int i = 0; i < T; ++i) {
+        const int ei = __shfl(my_e, i, 64);
+        rank += (i < lane && ei == my_e) ? 1 : 0;
+        cnt += (ei == lane) ? 1 : 0;
+    }
+    const int c_e = lane < E ? cnt : 0;
+    const int p_e = (c_e + BS - 1) / BS * BS;
+    int incl = p_e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    const int o_e = incl - p_e;
+    const int total = __shfl(incl, 63, 64);
+    if (lane < E) {
+        for (int b = o_e / BS; b < (o_e + p_e) / BS; ++b) expert_ids[b] = lane;
+        for (int p = o_e + c_e; p < o_e + p_e; ++p) sorted[p] = T;
+    }
+    const int base = __shfl(o_e, my_e < 0 ? 0 : my_e, 64);
+    if (lane < T) sorted[base + rank] = lane;
+    for (int p = total + lane; p < cap; p += 64) sorted[p] = T;
+    for (int b = total / BS + lane; b < cap / BS; b += 64) expert_ids[b] = -1;
+    if (lane == 0) *ntpp = total;
+}
+
 static int id_bits(int E) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
@@ -272,6 +326,12 @@ bool route_align_fused(int M, int topk) { return M <= ROUTE_ALIGN_MAX_M && M * t
 
 void launch_route_align(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids, int BS,
                         int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, int cap, hipStream_t s) {
+    if (M * topk <= ROUTE_ALIGN_WAVE_MAX && E <= ROUTE_ALIGN_WAVE_MAX) {
+        const int waves = std::min(M, ALIGN_WAVES);
+        hipLaunchKernelGGL(route_align_wave_kernel, dim3(1), dim3(64 * waves), 0, s, logits, M, E, topk, renormalize, w,
+                           ids, BS, sorted, expert_ids, ntpp, cap);
+        return;
+    }
     const size_t lds = sizeof(int) * ((size_t)E * (1 + ALIGN_WAVES) + (size_t)M * topk);
     if (lds > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&route_align_kernel),
