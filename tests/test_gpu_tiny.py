@@ -5,7 +5,9 @@ int4 per-column and int8 weights; the int4 RAW stage of one token, with and
 without act-order (the permutation applied while staging); the int4 GATE_UP
 stage of one token (which runs the small-batch kernel after the gather); and
 a token's top-k naming one expert more than once (more rows than the LDS
-holds, and more than one block per expert), against the oracle.  Float comparisons:
+holds, and more than one block per expert); one token's DOWN with the top-k
+sum folded in (top-k 1 to 4, block sizes 16 and 256, one expert named twice),
+against the oracle.  Float comparisons:
 relative Frobenius error <= 5e-3 and max abs error <= 3e-2 * max |ref|; the
 RAW stage on exact-integer inputs bit for bit."""
 import numpy as np
@@ -112,6 +114,38 @@ def test_down_repeated_expert(bs):
     ids[1, 3:5] = 5
     w = np.random.default_rng(1160).uniform(0.1, 1.0, ids.shape).astype(np.float32)
     check_down(spec, wts, p, ids, w, bs, "repeated expert bs=%d" % bs)
+
+
+# one token with the top-k sum folded into DOWN: every compiled top-k (1-4),
+# int8 and int4 group-128, block sizes up to 256
+TOPK_SPECS = {"w8t1": W8.with_(name="w8-tiny-top1", topk=1), "w8t3": W8.with_(name="w8-tiny-top3", topk=3),
+              "w8t4": W8.with_(name="w8-tiny-top4", topk=4), "w4t3": W4.with_(name="w4-tiny-top3", topk=3),
+              "w4t4": W4PC.with_(name="w4pc-tiny-top4", topk=4)}
+
+
+@pytest.mark.parametrize("key", sorted(TOPK_SPECS))
+@pytest.mark.parametrize("bs", [16, 256])
+def test_down_one_token_topk(key, bs):
+    need_gpu()
+    if key not in _cache:
+        spec = TOPK_SPECS[key]
+        wts = gen.make_moe_weights(spec, seed_config=1180 + sorted(TOPK_SPECS).index(key))
+        _cache[key] = (spec, wts, wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2,
+                                              torch.float16 if spec.act == "f16" else torch.bfloat16,
+                                              spec.group_size, wts.g1, wts.g2))
+    spec, wts, p = _cache[key]
+    toks = gen.make_tokens(spec, 1, seed_config=1190 + bs)
+    w, ids = oracle.route(toks.logits, spec.topk, spec.renormalize)
+    check_down(spec, wts, p, ids, w, bs, "%s one token bs=%d" % (key, bs))
+
+
+def test_down_one_token_same_expert_twice():
+    """One token whose two slots name the same expert (two rows of one block)."""
+    need_gpu()
+    spec, wts, p = setup("w8")
+    ids = np.array([[5, 5]], np.int32)
+    w = np.array([[0.625, 0.375]], np.float32)
+    check_down(spec, wts, p, ids, w, 16, "one token, expert 5 twice")
 
 
 def run_gate_up(spec, p, xd, ids, bs):

@@ -376,6 +376,11 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     g.a_direct = (stage == WQ_STAGE_DOWN) ? 1 : 0;
     g.cap = (int)d->capacity;
 
+    if (stage == WQ_STAGE_DOWN && wq::tiny_down_combine_supported(wbits, d->M, d->topk, d->n_out, d->k_in)) {
+        // one token: the top-k sum is folded into the DOWN kernel
+        wq::launch_tiny_down_combine(wbits, bf16, g, static_cast<uint16_t*>(d->d_out), s);
+        return after_launch(who);
+    }
     const int slabs = stage == WQ_STAGE_DOWN ? down_slabs(d->M, d->topk, d->E, d->n_out, d->k_in) : 1;
     const bool tiny = wq::tiny_supported(wbits, stage, d->M, d->k_in, g.groups, slabs);
     const bool large = !tiny && wq::prefill_supported(d->n_out, d->k_in, d->block_size);

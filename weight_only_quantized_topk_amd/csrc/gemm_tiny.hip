@@ -326,4 +326,209 @@ int launch_gemm_tiny(int wbits, bool bf16, int stage, const GemmArgs& g, const i
     return by_stage(std::integral_constant<int, 8>{}, std::false_type{});
 }
 
+
+// ---------------------------------------------------------------------------
+// DOWN of one token with the top-k weighted sum folded in.  The token's topk
+// pairs sit at some positions of sorted_token_ids (found by one wave's scan);
+// the H rows at those positions are staged in LDS, and one workgroup per 16
+// output columns streams the 16-row weight tile of every chosen expert, NW
+// waves splitting the 1 KiB chunks (wave w takes chunks w, w + NW, ...), DEPTH
+// chunks per expert in flight.  Every MFMA B column carries the same H row, so
+// column 0 of the result is the token's: the waves' column-0 partial sums meet
+// in LDS and are added in wave order, scaled per column (int8, or int4 with
+// one scale per column), multiplied by the pair's routed weight and summed over
+// the pairs in slot order -- the output row in the activation type, with no
+// per-pair fp32 rows and no combine launch.  A pair missing from the sorted
+// order, or one whose block names no valid expert, adds nothing.
+// ---------------------------------------------------------------------------
+template <int WBITS, bool BF16, int TK, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void tiny_down_combine_kernel(GemmArgs g, uint16_t* __restrict__ out) {
+    constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
+    constexpr int KSTEPS = KCHUNK / 32;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ int spos[TK];
+    __shared__ int sexp[TK];
+    __shared__ f32x4 red[NW][TK][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tile = blockIdx.x;
+    const int K = g.k_in;
+    const int C = K / KCHUNK;
+    const int BS = g.block_size;
+
+    if (wave == 0) {
+        // positions of pairs 0 .. TK - 1 (the token's slots) in the sorted order
+        const int ntpp = min(*g.ntpp, g.cap);
+        int pos[TK];
+#pragma unroll
+        for (int j = 0; j < TK; ++j) pos[j] = -1;
+        for (int base = 0; base < ntpp; base += 64) {
+            const int p = base + lane;
+            const int v = p < ntpp ? g.sorted[p] : -1;
+#pragma unroll
+            for (int j = 0; j < TK; ++j) {
+                const uint64_t hit = __ballot(v == j);
+                if (hit != 0 && pos[j] < 0) pos[j] = base + __builtin_ctzll(hit);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            if (lane == j) {
+                const int e = pos[j] >= 0 ? g.expert_ids[pos[j] / BS] : -1;
+                const bool ok = e >= 0 && e < g.E;
+                spos[j] = ok ? pos[j] : -1;
+                sexp[j] = ok ? e : 0;
+            }
+        }
+    }
+    __syncthreads();
+
+    const size_t expert_bytes = (size_t)(g.n_out / TILE_ROWS) * C * CHUNK_BYTES;
+    const uint8_t* wt[TK];
+    const uint16_t* se[TK];
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+        const int e = sexp[j];
+        wt[j] = g.w + (size_t)e * expert_bytes + (size_t)tile * C * CHUNK_BYTES + lane * 16;
+        se[j] = g.s + (size_t)e * g.groups * g.n_out;
+    }
+    const bool grouped = (WBITS == 4) && g.groups > 1;
+    const int rowq = 4 * (lane >> 4);
+
+    // chunks wave + NW * i, i < nw; indices clamp to the wave's last chunk
+    const int nw = wave < C ? (C - 1 - wave) / NW + 1 : 0;
+    const int clast = wave < C ? wave + (nw - 1) * NW : C - 1;
+    u32x4 wv[DEPTH][TK];
+    u32x2 sv[DEPTH][TK];  // int4 group-128: the chunk's scales of this lane's 4 rows, loaded with it
+    auto wload = [&](int i, int slot) {
+        const int c = min(wave + NW * i, clast);
+#pragma unroll
+        for (int j = 0; j < TK; ++j) wv[slot][j] = ldg128_stream(wt[j] + (size_t)c * CHUNK_BYTES);
+        if constexpr (WBITS == 4) {
+            const size_t gc = grouped ? (size_t)c : 0;  // per-column scales: a harmless reread of group 0
+#pragma unroll
+            for (int j = 0; j < TK; ++j)
+                sv[slot][j] = *reinterpret_cast<const u32x2*>(se[j] + gc * g.n_out + tile * TILE_ROWS + rowq);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) wload(d, d);
+
+    // stage the TK H rows (a missing pair's row reads as zeros)
+    const int xrow_b = 2 * K + 16;
+    const int kp = K / 8;  // 16-byte pieces per row
+    for (int q = tid; q < TK * kp; q += NW * 64) {
+        const int j = q / kp, pc = q - j * kp;
+        const int p = spos[j];
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (p >= 0) v = ldg128(g.a + (size_t)p * K + 8 * pc);
+        *reinterpret_cast<u32x4*>(lds + (size_t)j * xrow_b + 16 * pc) = v;
+    }
+    __syncthreads();
+
+    f32x4 acc[TK];
+#pragma unroll
+    for (int j = 0; j < TK; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto body = [&](int i, auto U) {
+        constexpr int u = decltype(U)::value;
+        const int c = min(wave + NW * i, clast);
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            const uint8_t* xc = lds + (size_t)j * xrow_b + (size_t)c * (2 * KCHUNK) + 16 * (lane >> 4);
+            u32x4 b[KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) b[ks] = *reinterpret_cast<const u32x4*>(xc + 64 * ks);
+            if constexpr (WBITS == 4) {
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) part = mfma16x16x32<false>(dequant_w4_f16(wv[u][j][ks]), b[ks], part);
+                if (grouped) {
+                    acc[j][0] += part[0] * f16_to_f32((uint16_t)(sv[u][j][0] & 0xffffu));
+                    acc[j][1] += part[1] * f16_to_f32((uint16_t)(sv[u][j][0] >> 16));
+                    acc[j][2] += part[2] * f16_to_f32((uint16_t)(sv[u][j][1] & 0xffffu));
+                    acc[j][3] += part[3] * f16_to_f32((uint16_t)(sv[u][j][1] >> 16));
+                } else {
+                    acc[j] += part;
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    acc[j] = mfma16x16x32<BF16>(dequant_w8x8<BF16>(wv[u][j][2 * ks], wv[u][j][2 * ks + 1]), b[ks],
+                                                acc[j]);
+            }
+        }
+        wload(i + DEPTH, u);
+    };
+    int i0 = 0;
+    for (; i0 + DEPTH <= nw; i0 += DEPTH) static_for<0, DEPTH>([&](auto U) { body(i0 + decltype(U)::value, U); });
+    static_for<0, DEPTH - 1>([&](auto U) {
+        if (i0 + decltype(U)::value < nw) body(i0 + decltype(U)::value, U);
+    });
+
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int j = 0; j < TK; ++j) red[wave][j][lane >> 4] = acc[j];
+    }
+    __syncthreads();
+    if (tid < 4) {
+        const int row = tile * TILE_ROWS + 4 * tid;
+        f32x4 res = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            if (spos[j] < 0) continue;
+            f32x4 o = red[0][j][tid];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) o += red[w][j][tid];
+            if (!grouped) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] *= act_to_f32<BF16>(se[j][row + i]);
+            }
+            res += o * g.topk_w[j];
+        }
+        u32x2 st;
+        st[0] = (uint32_t)f32_to_act<BF16>(res[0]) | ((uint32_t)f32_to_act<BF16>(res[1]) << 16);
+        st[1] = (uint32_t)f32_to_act<BF16>(res[2]) | ((uint32_t)f32_to_act<BF16>(res[3]) << 16);
+        *reinterpret_cast<u32x2*>(out + row) = st;
+    }
+}
+
+static size_t down_combine_lds(int topk, int k_in) { return (size_t)topk * (2 * (size_t)k_in + 16); }
+
+// one token, top-k up to 4, a long reduction (>= 64 chunks per tile), whole
+// H rows in LDS
+bool tiny_down_combine_supported(int wbits, int M, int topk, int n_out, int k_in) {
+    const int c = k_in / (wbits == 4 ? WFmt<4>::KCHUNK : WFmt<8>::KCHUNK);
+    return M == 1 && topk >= 1 && topk <= 4 && c >= 64 && n_out % TILE_ROWS == 0 &&
+           down_combine_lds(topk, k_in) <= 128 * 1024;
+}
+
+template <int WBITS, bool BF16, int TK>
+static void launch_down_combine_tk(const GemmArgs& g, uint16_t* out, hipStream_t s) {
+    constexpr int NW = 16, DEPTH = 3;
+    auto kern = tiny_down_combine_kernel<WBITS, BF16, TK, NW, DEPTH>;
+    const size_t dyn = down_combine_lds(TK, g.k_in);
+    if (dyn > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)dyn);
+    hipLaunchKernelGGL(kern, dim3(g.n_out / TILE_ROWS), dim3(NW * 64), dyn, s, g, out);
+}
+
+template <int WBITS, bool BF16>
+static void launch_down_combine_w(const GemmArgs& g, uint16_t* out, hipStream_t s) {
+    switch (g.topk) {
+        case 1: launch_down_combine_tk<WBITS, BF16, 1>(g, out, s); break;
+        case 2: launch_down_combine_tk<WBITS, BF16, 2>(g, out, s); break;
+        case 3: launch_down_combine_tk<WBITS, BF16, 3>(g, out, s); break;
+        default: launch_down_combine_tk<WBITS, BF16, 4>(g, out, s); break;
+    }
+}
+
+void launch_tiny_down_combine(int wbits, bool bf16, const GemmArgs& g, uint16_t* out, hipStream_t s) {
+    if (wbits == 4) launch_down_combine_w<4, false>(g, out, s);
+    else if (bf16) launch_down_combine_w<8, true>(g, out, s);
+    else launch_down_combine_w<8, false>(g, out, s);
+}
+
 }  // namespace wq

@@ -94,6 +94,10 @@ void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipS
 // workspace); launch returns the number of K slices it wrote
 bool tiny_supported(int wbits, int stage, int M, int k_in, int groups, int max_ks);
 int tiny_down_slabs(int M, int k_in);
+// DOWN of one token with the top-k sum folded in: writes the layer output row
+// (activation type) directly
+bool tiny_down_combine_supported(int wbits, int M, int topk, int n_out, int k_in);
+void launch_tiny_down_combine(int wbits, bool bf16, const GemmArgs& g, uint16_t* out, hipStream_t s);
 int launch_gemm_tiny(int wbits, bool bf16, int stage, const GemmArgs& g, const int32_t* perm, int max_ks,
                      hipStream_t s);
 // large-batch path: 512, 256 or 128 weight rows (dequantized in registers) x

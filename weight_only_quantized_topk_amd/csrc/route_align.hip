@@ -3,7 +3,8 @@
 //
 // moe_route: one 64-lane wave per token.  Each lane holds up to 16 logits
 // (E <= 1024).  Top-k is k rounds of a wave-wide arg-max over the experts not
-// yet chosen, comparing (larger logit, then smaller expert index).  The slot
+// yet chosen, comparing (larger logit, then smaller expert index); up to 64
+// experts, each lane's rank in that order is counted directly instead.  The slot
 // weights are exp(l_j - max) / sum, evaluated in double with the sum taken in
 // ascending slot order, rounded once to float.
 //
@@ -29,8 +30,48 @@ namespace wq {
 
 constexpr int ROUTE_MAX_PER_LANE = 16;  // E <= 1024
 
+// (larger logit, then smaller expert index); a NaN logit ranks below every
+// number, so the order is total and the top-k always names topk distinct experts
 __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+    const bool an = va != va, bn = vb != vb;
+    if (an || bn) return (!an && bn) || (an && bn && ea < eb);
     return va > vb || (va == vb && ea < eb);
+}
+
+// E <= 64: lane e holds logit e; its rank is the number of experts ahead of it
+// in the order above (E independent shuffles instead of topk chained arg-max
+// reductions), and the lanes ranked below topk are the slots, in rank order
+__device__ __forceinline__ void route_token_small(const float* __restrict__ l, int E, int topk, int renormalize,
+                                                  int lane, float* __restrict__ w_row, int32_t* __restrict__ ids_row,
+                                                  int* lds_ids) {
+    const float v = lane < E ? l[lane] : 0.0f;
+    int rank = 0;
+    for (int i = 0; i < E; ++i) {
+        const float vi = __shfl(v, i, 64);
+        rank += better(vi, i, v, lane) ? 1 : 0;
+    }
+    const bool sel = lane < E && rank < topk;
+    const int lane0 = __builtin_ctzll(__ballot(lane < E && rank == 0));
+    const double mu = (double)__shfl(v, lane0, 64);
+    const double ex = sel ? exp((double)v - mu) : 0.0;
+    double denom = 0.0;
+    if (renormalize) {
+        // ascending slot order
+        for (int j = 0; j < topk; ++j) {
+            const int lj = __builtin_ctzll(__ballot(lane < E && rank == j));
+            denom += __shfl(ex, lj, 64);
+        }
+    } else {
+        double part = lane < E ? exp((double)v - mu) : 0.0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        denom = part;
+    }
+    if (sel) {
+        w_row[rank] = (float)(ex / denom);
+        ids_row[rank] = lane;
+        if (lds_ids) lds_ids[rank] = lane;
+    }
 }
 
 // routes token row `l` (E logits) with one wave; lane j < topk writes slot j's
@@ -38,6 +79,10 @@ __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
 __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int topk, int renormalize, int lane,
                                             float* __restrict__ w_row, int32_t* __restrict__ ids_row,
                                             int* lds_ids) {
+    if (E <= 64) {
+        route_token_small(l, E, topk, renormalize, lane, w_row, ids_row, lds_ids);
+        return;
+    }
     float v[ROUTE_MAX_PER_LANE];
     uint32_t avail = 0;  // bit i: slot i of this lane holds a not-yet-chosen expert
 #pragma unroll
