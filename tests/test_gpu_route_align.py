@@ -49,6 +49,13 @@ def test_route_edge_cases():
     route_check(rng.standard_normal((70, 160)).astype(np.float32) * 4, 6, False, "no renorm")
     route_check(rng.integers(-2, 3, size=(200, 64)).astype(np.float32), 8, True, "many ties")
     route_check(rng.standard_normal((100003, 8)).astype(np.float32), 2, True, "large M")
+    # the rank-counting top-k (E <= 64) at its edge and the arg-max rounds
+    # above it, with ties
+    for E, topk in ((64, 8), (65, 6), (100, 4), (128, 8), (129, 6), (192, 6), (193, 8), (256, 16), (257, 8)):
+        for renorm in (True, False):
+            lg = rng.standard_normal((37, E)).astype(np.float32)
+            lg[:, ::7] = np.float32(0.25)  # tied logits across the lanes' slots
+            route_check(lg, topk, renorm, "E=%d topk=%d" % (E, topk))
     # M = 0 launches nothing and succeeds
     wq.moe_route(torch.empty((0, 8), dtype=torch.float32, device="cuda"), 2)
 
@@ -106,7 +113,9 @@ def test_align_deterministic():
 @pytest.mark.parametrize("M,E,topk", [(1, 8, 2), (7, 8, 2), (16, 160, 6), (17, 160, 6), (64, 8, 2), (300, 160, 6),
                                       (12, 1024, 8), (33, 1024, 8), (16, 2, 2),
                                       # single-wave sort: up to 64 pairs over up to 64 experts
-                                      (1, 1, 1), (16, 64, 4), (11, 33, 5), (3, 4, 4), (16, 8, 2), (8, 65, 8)])
+                                      (1, 1, 1), (16, 64, 4), (11, 33, 5), (3, 4, 4), (16, 8, 2), (8, 65, 8),
+                                      # more logits per lane, ties
+                                      (64, 160, 6), (48, 256, 8), (40, 192, 6), (20, 129, 3)])
 @pytest.mark.parametrize("bs", [16, 64, 128, 256])
 @pytest.mark.parametrize("renorm", [True, False])
 def test_route_align_fused_equals_two_calls(M, E, topk, bs, renorm):

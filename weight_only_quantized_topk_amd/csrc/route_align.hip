@@ -4,7 +4,8 @@
 // moe_route: one 64-lane wave per token.  Each lane holds up to 16 logits
 // (E <= 1024).  Top-k is k rounds of a wave-wide arg-max over the experts not
 // yet chosen, comparing (larger logit, then smaller expert index); up to 64
-// experts, each lane's rank in that order is counted directly instead.  The slot
+// experts, each expert's rank in that order is counted directly instead (E
+// steps of a few instructions, against topk chains of shuffle reductions).  The slot
 // weights are exp(l_j - max) / sum, evaluated in double with the sum taken in
 // ascending slot order, rounded once to float.
 //
@@ -30,47 +31,87 @@ namespace wq {
 
 constexpr int ROUTE_MAX_PER_LANE = 16;  // E <= 1024
 
-// (larger logit, then smaller expert index); a NaN logit ranks below every
-// number, so the order is total and the top-k always names topk distinct experts
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-    const bool an = va != va, bn = vb != vb;
-    if (an || bn) return (!an && bn) || (an && bn && ea < eb);
-    return va > vb || (va == vb && ea < eb);
+// A logit as an unsigned key in the order of the floats: -0 and +0 equal, and
+// every NaN below every number (so the order is total and the top-k always
+// names topk distinct experts)
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v != v) return 0u;
+    const uint32_t b = __float_as_uint(v + 0.0f);  // -0 -> +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// E <= 64: lane e holds logit e; its rank is the number of experts ahead of it
-// in the order above (E independent shuffles instead of topk chained arg-max
-// reductions), and the lanes ranked below topk are the slots, in rank order
-__device__ __forceinline__ void route_token_small(const float* __restrict__ l, int E, int topk, int renormalize,
-                                                  int lane, float* __restrict__ w_row, int32_t* __restrict__ ids_row,
-                                                  int* lds_ids) {
-    const float v = lane < E ? l[lane] : 0.0f;
-    int rank = 0;
-    for (int i = 0; i < E; ++i) {
-        const float vi = __shfl(v, i, 64);
-        rank += better(vi, i, v, lane) ? 1 : 0;
+// (larger logit, then smaller expert index)
+__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+    const uint32_t ka = order_key(va), kb = order_key(vb);
+    return ka > kb || (ka == kb && ea < eb);
+}
+
+// E <= 64 NV: lane holds logits e = lane + 64 k (k < NV); each one's rank is
+// the number of experts ahead of it in the order above, and the experts ranked
+// below topk are the slots, in rank order.  The count costs E x NV compares
+// per lane, so it is used up to 64 experts only (NV = 1)
+template <int NV>
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ l, int E, int topk, int renormalize,
+                                                 int lane, float* __restrict__ w_row, int32_t* __restrict__ ids_row,
+                                                 int* lds_ids) {
+    float v[NV];
+    uint32_t key[NV];
+    int rank[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        v[k] = (lane + 64 * k < E) ? l[lane + 64 * k] : 0.0f;
+        key[k] = order_key(v[k]);
+        rank[k] = 0;
     }
-    const bool sel = lane < E && rank < topk;
-    const int lane0 = __builtin_ctzll(__ballot(lane < E && rank == 0));
-    const double mu = (double)__shfl(v, lane0, 64);
-    const double ex = sel ? exp((double)v - mu) : 0.0;
+    // expert i's key is read from its lane into a scalar register (a uniform
+    // lane index), compared by every lane without branches
+#pragma unroll
+    for (int k2 = 0; k2 < NV; ++k2) {
+        const int n2 = min(64, E - 64 * k2);
+#pragma unroll 8
+        for (int i = 0; i < n2; ++i) {
+            const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)key[k2], i);
+            const int ei = 64 * k2 + i;
+#pragma unroll
+            for (int k = 0; k < NV; ++k)
+                rank[k] += (ki > key[k] || (ki == key[k] && ei < lane + 64 * k)) ? 1 : 0;
+        }
+    }
+    // the slot-j expert's value (or its exp term) from whichever lane holds it
+    auto from_slot = [&](int j, const double* x) {
+        double r = 0.0;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const uint64_t b = __ballot(lane + 64 * k < E && rank[k] == j);
+            if (b) r = __shfl(x[k], __builtin_ctzll(b), 64);
+        }
+        return r;
+    };
+    double vd[NV], ex[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) vd[k] = (double)v[k];
+    const double mu = from_slot(0, vd);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) ex[k] = (lane + 64 * k < E && rank[k] < topk) ? exp(vd[k] - mu) : 0.0;
     double denom = 0.0;
     if (renormalize) {
-        // ascending slot order
-        for (int j = 0; j < topk; ++j) {
-            const int lj = __builtin_ctzll(__ballot(lane < E && rank == j));
-            denom += __shfl(ex, lj, 64);
-        }
+        for (int j = 0; j < topk; ++j) denom += from_slot(j, ex);  // ascending slot order
     } else {
-        double part = lane < E ? exp((double)v - mu) : 0.0;
+        double part = 0.0;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (lane + 64 * k < E) part += exp(vd[k] - mu);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
         denom = part;
     }
-    if (sel) {
-        w_row[rank] = (float)(ex / denom);
-        ids_row[rank] = lane;
-        if (lds_ids) lds_ids[rank] = lane;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        if (lane + 64 * k < E && rank[k] < topk) {
+            w_row[rank[k]] = (float)(ex[k] / denom);
+            ids_row[rank[k]] = lane + 64 * k;
+            if (lds_ids) lds_ids[rank[k]] = lane + 64 * k;
+        }
     }
 }
 
@@ -79,10 +120,7 @@ __device__ __forceinline__ void route_token_small(const float* __restrict__ l, i
 __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int topk, int renormalize, int lane,
                                             float* __restrict__ w_row, int32_t* __restrict__ ids_row,
                                             int* lds_ids) {
-    if (E <= 64) {
-        route_token_small(l, E, topk, renormalize, lane, w_row, ids_row, lds_ids);
-        return;
-    }
+    if (E <= 64) return route_token_rank<1>(l, E, topk, renormalize, lane, w_row, ids_row, lds_ids);
     float v[ROUTE_MAX_PER_LANE];
     uint32_t avail = 0;  // bit i: slot i of this lane holds a not-yet-chosen expert
 #pragma unroll
@@ -163,8 +201,8 @@ void launch_route(const float* logits, int M, int E, int topk, int renormalize, 
 constexpr int ALIGN_THREADS = 1024;
 constexpr int ALIGN_WAVES = ALIGN_THREADS / 64;
 // the fused route + align kernel serves batches up to 16 tokens (one per wave:
-// routing a token is a chain of dependent latencies, and 4 tokens per wave made
-// the fused kernel slower than the two separate ones)
+// more tokens per wave made it slower than the separate kernels, which spread
+// the tokens over many compute units)
 constexpr int ROUTE_ALIGN_MAX_M = 16;
 constexpr int ROUTE_ALIGN_MAX_T = 1024;
 
