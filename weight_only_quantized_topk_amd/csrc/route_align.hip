@@ -46,72 +46,49 @@ __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
     return ka > kb || (ka == kb && ea < eb);
 }
 
-// E <= 64 NV: lane holds logits e = lane + 64 k (k < NV); each one's rank is
-// the number of experts ahead of it in the order above, and the experts ranked
-// below topk are the slots, in rank order.  The count costs E x NV compares
-// per lane, so it is used up to 64 experts only (NV = 1)
-template <int NV>
+// E <= 64: lane e holds logit e; its rank is the number of experts ahead of it
+// in the order above, and the experts ranked below topk are the slots, in rank
+// order.  Counting costs E compares per lane, so it serves up to 64 experts
 __device__ __forceinline__ void route_token_rank(const float* __restrict__ l, int E, int topk, int renormalize,
                                                  int lane, float* __restrict__ w_row, int32_t* __restrict__ ids_row,
                                                  int* lds_ids) {
-    float v[NV];
-    uint32_t key[NV];
-    int rank[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        v[k] = (lane + 64 * k < E) ? l[lane + 64 * k] : 0.0f;
-        key[k] = order_key(v[k]);
-        rank[k] = 0;
-    }
+    const bool live = lane < E;
+    const float v = live ? l[lane] : 0.0f;
+    const uint32_t key = order_key(v);
     // expert i's key is read from its lane into a scalar register (a uniform
-    // lane index), compared by every lane without branches
-#pragma unroll
-    for (int k2 = 0; k2 < NV; ++k2) {
-        const int n2 = min(64, E - 64 * k2);
-#pragma unroll 8
-        for (int i = 0; i < n2; ++i) {
-            const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)key[k2], i);
-            const int ei = 64 * k2 + i;
-#pragma unroll
-            for (int k = 0; k < NV; ++k)
-                rank[k] += (ki > key[k] || (ki == key[k] && ei < lane + 64 * k)) ? 1 : 0;
-        }
-    }
-    // the slot-j expert's value (or its exp term) from whichever lane holds it
-    auto from_slot = [&](int j, const double* x) {
-        double r = 0.0;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const uint64_t b = __ballot(lane + 64 * k < E && rank[k] == j);
-            if (b) r = __shfl(x[k], __builtin_ctzll(b), 64);
-        }
-        return r;
+    // lane index) and compared by every lane without branches
+    int rank = 0;
+    auto count = [&](int i) {
+        const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)key, i);
+        rank += (ki > key || (ki == key && i < lane)) ? 1 : 0;
     };
-    double vd[NV], ex[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) vd[k] = (double)v[k];
-    const double mu = from_slot(0, vd);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) ex[k] = (lane + 64 * k < E && rank[k] < topk) ? exp(vd[k] - mu) : 0.0;
+    int i = 0;
+    for (; i + 4 <= E; i += 4) {
+        count(i);
+        count(i + 1);
+        count(i + 2);
+        count(i + 3);
+    }
+    for (; i < E; ++i) count(i);
+    const bool sel = live && rank < topk;
+    // the slot-j expert's lane
+    auto slot_lane = [&](int j) { return __builtin_ctzll(__ballot(live && rank == j)); };
+    const double vd = (double)v;
+    const double mu = __shfl(vd, slot_lane(0), 64);
+    const double ex = sel ? exp(vd - mu) : 0.0;
     double denom = 0.0;
     if (renormalize) {
-        for (int j = 0; j < topk; ++j) denom += from_slot(j, ex);  // ascending slot order
+        for (int j = 0; j < topk; ++j) denom += __shfl(ex, slot_lane(j), 64);  // ascending slot order
     } else {
-        double part = 0.0;
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-            if (lane + 64 * k < E) part += exp(vd[k] - mu);
+        double part = live ? exp(vd - mu) : 0.0;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
         denom = part;
     }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        if (lane + 64 * k < E && rank[k] < topk) {
-            w_row[rank[k]] = (float)(ex[k] / denom);
-            ids_row[rank[k]] = lane + 64 * k;
-            if (lds_ids) lds_ids[rank[k]] = lane + 64 * k;
-        }
+    if (sel) {
+        w_row[rank] = (float)(ex / denom);
+        ids_row[rank] = lane;
+        if (lds_ids) lds_ids[rank] = lane;
     }
 }
 
@@ -120,7 +97,7 @@ __device__ __forceinline__ void route_token_rank(const float* __restrict__ l, in
 __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int topk, int renormalize, int lane,
                                             float* __restrict__ w_row, int32_t* __restrict__ ids_row,
                                             int* lds_ids) {
-    if (E <= 64) return route_token_rank<1>(l, E, topk, renormalize, lane, w_row, ids_row, lds_ids);
+    if (E <= 64) return route_token_rank(l, E, topk, renormalize, lane, w_row, ids_row, lds_ids);
     float v[ROUTE_MAX_PER_LANE];
     uint32_t avail = 0;  // bit i: slot i of this lane holds a not-yet-chosen expert
 #pragma unroll
