@@ -3,7 +3,9 @@
     python -m weight_only_quantized_topk_amd.build
 
 Each source is compiled with hipcc into _build/, then linked into
-weight_only_quantized_topk_amd/libwqmoe.so next to this file.
+weight_only_quantized_topk_amd/libwqmoe.so next to this file; the streaming
+read probe (csrc/stream_probe.hip) is built into the program stream_probe
+beside it.
 """
 from __future__ import annotations
 
@@ -17,6 +19,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwqmoe.so")
+# a standalone program (not part of the library): the plain streaming-read
+# bandwidth the weight-streaming kernels are read against
+PROBE_SRC = "stream_probe.hip"
+PROBE = os.path.join(HERE, "stream_probe")
 SOURCES = ["abi.cpp", "route_align.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_n256.hip", "sparse24.hip", "quant.hip", "dense_decode.hip", "gemm_tiny.hip", "gemm_fp8.hip"]
 ARCH = "gfx950"
 
@@ -63,8 +69,14 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    ptmp = PROBE + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-o", ptmp, os.path.join(CSRC, PROBE_SRC)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (PROBE_SRC, r.stdout + r.stderr))
+    os.replace(ptmp, PROBE)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE)
     return LIB
 
 
