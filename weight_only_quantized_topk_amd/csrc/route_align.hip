@@ -9,14 +9,14 @@
 // weights are exp(l_j - max) / sum, evaluated in double with the sum taken in
 // ascending slot order, rounded once to float.
 //
-// moe_align: one 1024-thread workgroup.  (1) per-expert counts with LDS
-// integer atomics (order-free, hence deterministic); (2) padded exclusive scan
-// over experts, expert_ids and pad/tail sentinels written by the expert's own
-// thread; (3) a stable scatter, 1024 pairs at a time: inside a wave, lanes with
-// the same expert are found with one ballot per expert-id bit and ranked with a
-// popcount of the lower lanes; across the 16 waves, per-wave counts in LDS give
-// each wave its offset.  No LDS atomic decides an order, so the output is the
-// unique stable one.
+// moe_align: one 1024-thread workgroup; each of its 16 waves sorts a
+// contiguous run of the pairs.  (1) per-run per-expert counts (inside a wave,
+// lanes with the same expert are found with one ballot per expert-id bit);
+// (2) padded exclusive scan over experts, expert_ids and pad/tail sentinels
+// written by the expert's own thread, and each run's first write position per
+// expert; (3) a stable scatter along each run, a pair ranked by a popcount of
+// the lower lanes holding its expert.  No atomic decides an order, so the
+// output is the unique stable one.
 // moe_route_align: for batches up to 16 tokens one 1024-thread workgroup does
 // both, the expert ids staying in LDS between the two (one launch instead of
 // two, the same outputs).
@@ -184,28 +184,64 @@ constexpr int ROUTE_ALIGN_MAX_M = 16;
 constexpr int ROUTE_ALIGN_MAX_T = 1024;
 
 // the align steps for one 1024-thread workgroup; ids may point to global or
-// LDS memory; smem holds E * (1 + ALIGN_WAVES) ints
+// LDS memory; smem holds E * (1 + ALIGN_WAVES) ints.
+// Wave w owns the contiguous run of pairs [w L, (w + 1) L).  (1) Each wave
+// counts its run per expert (64 pairs a step: the lanes holding one expert
+// are found with one ballot per expert-id bit, the group's lowest lane adds
+// the group size to the wave's row of the table).  (2) One thread per expert
+// adds its column, pads it, and the padded counts are scanned over experts;
+// the column is then turned into each wave's first write position for that
+// expert (the expert's offset plus the counts of the runs before).  (3) Each
+// wave walks its run again and writes pair i at its expert's running
+// position plus its rank among the step's lanes with that expert.  Runs are in
+// pair order and ranks are by lane, so the result is the unique stable order,
+// and the waves need no synchronisation between steps.
 __device__ __forceinline__ void align_body(const int32_t* ids, int T, int E, int BS, int nbits,
                                            int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
                                            int32_t* __restrict__ ntpp, int cap, int* smem) {
-    int* cnt = smem;            // [E]   counts, later the running write position
-    int* wcnt = smem + E;       // [ALIGN_WAVES][E] per-wave counts of the current chunk
+    int* tab = smem;                     // [ALIGN_WAVES][E] counts per run, then write positions
     __shared__ int wsum[ALIGN_WAVES];
     __shared__ int total_s;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int L = ((T + ALIGN_WAVES - 1) / ALIGN_WAVES + 63) / 64 * 64;  // pairs per run
+    const int r0 = wave * L;
+    const int r1 = min(T, r0 + L);
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    for (int e = tid; e < E; e += ALIGN_THREADS) cnt[e] = 0;
+    // the lanes of this step holding the same (valid) expert as this lane
+    auto peers_of = [&](int e, bool valid) {
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        return peers;
+    };
+
+    for (int k = tid; k < ALIGN_WAVES * E; k += ALIGN_THREADS) tab[k] = 0;
     __syncthreads();
-    for (int i = tid; i < T; i += ALIGN_THREADS) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
+    int* row = tab + wave * E;
+    // the run, 64 pairs a step
+    auto walk = [&](auto step) {
+        for (int i0 = r0; i0 < r1; i0 += 64) {
+            const int i = i0 + lane;
+            step(i, (i < r1) ? ids[i] : -1);
+        }
+    };
+    walk([&](int, int e) {
+        const bool valid = (e >= 0 && e < E);
+        const uint64_t peers = peers_of(e, valid);
+        if (valid && (peers & lt_mask) == 0) row[e] += __popcll(peers);
+    });
     __syncthreads();
 
     // exclusive scan of the padded counts (E <= 1024: one expert per thread)
-    const int c_e = (tid < E) ? cnt[tid] : 0;
+    int c_e = 0;
+    if (tid < E)
+        for (int w = 0; w < ALIGN_WAVES; ++w) c_e += tab[w * E + tid];
     const int p_e = (c_e + BS - 1) / BS * BS;
     int incl = p_e;
 #pragma unroll
@@ -219,47 +255,31 @@ __device__ __forceinline__ void align_body(const int32_t* ids, int T, int E, int
     for (int w = 0; w < wave; ++w) wave_off += wsum[w];
     const int o_e = wave_off + incl - p_e;
     if (tid == ALIGN_THREADS - 1) total_s = wave_off + incl;
-    __syncthreads();
-    const int total = total_s;
     if (tid < E) {
-        cnt[tid] = o_e;  // running write position
+        int pos = o_e;  // first write position of each run for this expert
+        for (int w = 0; w < ALIGN_WAVES; ++w) {
+            const int c = tab[w * E + tid];
+            tab[w * E + tid] = pos;
+            pos += c;
+        }
         for (int b = o_e / BS; b < (o_e + p_e) / BS; ++b) expert_ids[b] = tid;
         for (int p = o_e + c_e; p < o_e + p_e; ++p) sorted[p] = T;
     }
+    __syncthreads();
+    const int total = total_s;
     if (tid == 0) *ntpp = total;
     for (int p = total + tid; p < cap; p += ALIGN_THREADS) sorted[p] = T;
     for (int b = total / BS + tid; b < cap / BS; b += ALIGN_THREADS) expert_ids[b] = -1;
 
-    // stable scatter
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < T; base += ALIGN_THREADS) {
-        for (int k = tid; k < ALIGN_WAVES * E; k += ALIGN_THREADS) wcnt[k] = 0;
-        const int i = base + tid;
-        const int e = (i < T) ? ids[i] : -1;
+    // stable scatter, each wave along its own run
+    walk([&](int i, int e) {
         const bool valid = (e >= 0 && e < E);
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = valid && ((e >> b) & 1);
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        __syncthreads();  // wcnt cleared
-        if (valid && rank == 0) wcnt[wave * E + e] = __popcll(peers);
-        __syncthreads();
+        const uint64_t peers = peers_of(e, valid);
         if (valid) {
-            int pos = cnt[e] + rank;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
-            sorted[pos] = i;
+            sorted[row[e] + __popcll(peers & lt_mask)] = i;
+            if ((peers & lt_mask) == 0) row[e] += __popcll(peers);  // after every lane of the group read it
         }
-        __syncthreads();
-        for (int x = tid; x < E; x += ALIGN_THREADS) {
-            int s = 0;
-            for (int w = 0; w < ALIGN_WAVES; ++w) s += wcnt[w * E + x];
-            cnt[x] += s;
-        }
-        __syncthreads();
-    }
+    });
 }
 
 __global__ __launch_bounds__(ALIGN_THREADS) void align_kernel(const int32_t* __restrict__ ids, int T, int E, int BS,
