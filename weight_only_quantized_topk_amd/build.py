@@ -33,13 +33,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# per-source flags.  The large-batch GEMM is scheduled by LLVM's iterative
-# ILP strategy: measured on MI355X, its gate/up launches run 1-2 % faster
-# than under the default scheduler (Mixtral int8 M=1024 0.485 -> 0.478 ms,
-# int4 act-order M=4096 1.77 -> 1.75 ms), with no register spills except in
-# the 256 x 128 shape, which gemm_prefill_n256.hip builds under the default one.
-# WQ_PREFILL_SCHED=default builds it under LLVM's default scheduler instead.
-PREFILL_SCHED = os.environ.get("WQ_PREFILL_SCHED", "iterative-ilp")
+# per-source flags.  WQ_PREFILL_SCHED=iterative-ilp builds the large-batch
+# GEMM (gemm_prefill.hip) under LLVM's iterative ILP scheduling strategy
+# instead of the default one.  An A/B of the two on two MI355X boxes, three
+# alternating runs each, found the default scheduler as fast or faster:
+# Mixtral int8 M=1024 gate/up 0.450 vs 0.453 ms and 0.457 vs 0.459 ms, int4
+# act-order M=4096 gate/up 1.754 vs 1.818 ms (layer 2.74 vs 2.86 ms).
+PREFILL_SCHED = os.environ.get("WQ_PREFILL_SCHED", "default")
 if PREFILL_SCHED not in ("iterative-ilp", "default"):
     raise ValueError("WQ_PREFILL_SCHED must be 'iterative-ilp' or 'default', got %r" % PREFILL_SCHED)
 SOURCE_FLAGS = ({"gemm_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}

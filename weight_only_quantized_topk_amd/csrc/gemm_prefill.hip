@@ -312,9 +312,9 @@ static void launch_prefill_cfg(const GemmArgs& g, int ksplit, hipStream_t s) {
 
 // The 256 x 128 shape for int8 weights, built in a translation unit of its own
 // (gemm_prefill_n256.hip, which includes this file with
-// WQ_PREFILL_KERNEL_ONLY defined) under the default instruction scheduler;
-// this file's kernels are built under LLVM's iterative ILP scheduler, which
-// spills that shape's registers.
+// WQ_PREFILL_KERNEL_ONLY defined) that stays under the default instruction
+// scheduler when this file is built under LLVM's iterative ILP one (a build
+// option), which spills that shape's registers.
 template <int WBITS, bool BF16, int STAGE>
 void launch_prefill_n256(const GemmArgs& g, int ksplit, hipStream_t s);
 

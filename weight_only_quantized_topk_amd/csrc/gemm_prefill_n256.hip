@@ -1,9 +1,9 @@
 // The large-batch GEMM's 256 x 128 workgroup shape (4 waves x 4 row tiles of
 // 16, 2 workgroups per CU; int8 weights, n_out a multiple of 256 but not of
 // 512).  The kernel is the one in gemm_prefill.hip; this translation unit is
-// built under the default instruction scheduler because the iterative ILP
-// scheduler that gemm_prefill.hip is built with spills this shape's registers
-// (76-98 VGPRs), while it runs the 512 x 128 shape 1-2 % faster.
+// always built under the default instruction scheduler: the iterative ILP
+// strategy, which gemm_prefill.hip can be built with (WQ_PREFILL_SCHED),
+// spills this shape's registers (76-98 VGPRs).
 #define WQ_PREFILL_KERNEL_ONLY
 #include "gemm_prefill.hip"
 
