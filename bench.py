@@ -236,6 +236,49 @@ def cpu_baseline(spec, wts, toks, seconds):
             "build": "gcc " + " ".join(oracle.NATIVE_FLAGS[:2] + ["-ffp-contract=off", "-fopenmp"])}
 
 
+def cpu_table(seconds):
+    """The oracle timed on this host for each configuration and batch size
+    (cpu_baseline's sample rule: the first n tokens, n chosen for about
+    `seconds`); the 2:4 layer by its oracle on the first n rows."""
+    import gen
+    out = []
+    for cid in (1, 2, 3, 5):
+        spec = gen.CONFIGS[cid]
+        log("bench: cpu table: generating %s" % spec.name)
+        wts = gen.make_moe_weights(spec)
+        for m in spec.m_sweep:
+            r = cpu_baseline(spec, wts, gen.make_tokens(spec, m), seconds)
+            r.update(config=cid, workload=spec.name, M=m)
+            log("bench: cpu table: %s M=%d %.2f tokens/s" % (spec.name, m, r["value"]))
+            out.append(r)
+        del wts
+    import tempfile
+    import oracle
+    oracle.use_native_build(tempfile.mkdtemp(prefix="wq_oracle_"))
+    spec = gen.CFG4
+    log("bench: cpu table: generating %s" % spec.name)
+    sw = gen.make_sparse_weights(spec)
+    s_f32 = sw.s_f32()
+    model, phys_cores, logical = host_cpu()
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    for m in spec.m_sweep:
+        xf = gen.bits_to_f32("f16", gen.make_sparse_x(spec, m))
+
+        def run(n):
+            t0 = time.perf_counter()
+            oracle.sparse24(xf[:n], sw.vals, sw.idx, s_f32, spec.group_size)
+            return time.perf_counter() - t0
+
+        per = run(1)
+        n = int(max(1, min(m, seconds / max(per, 1e-6))))
+        dt = run(n)
+        out.append({"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                    "sample": "the first %d of the %d rows, %.1f s" % (n, m, dt), "cpu_model": model,
+                    "physical_cores": phys_cores, "logical_cpus": logical, "config": 4, "workload": spec.name, "M": m})
+        log("bench: cpu table: %s M=%d %.2f rows/s" % (spec.name, m, n / dt))
+    return out
+
+
 def measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup):
     act = torch.float16 if spec.act == "f16" else torch.bfloat16
     toks = gen.make_tokens(spec, m)
@@ -506,7 +549,15 @@ def main(argv=None):
                          "files and exit; FETCH_SIZE / WRITE_SIZE are scaled by the --copy-calibration copy "
                          "when --calib-mib gives its size")
     ap.add_argument("--calib-mib", type=int, default=None, help="size of the calibration copy (MiB)")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the oracle on this host for every configuration and batch size (about "
+                         "--cpu-seconds each, on a sample of the batch where the whole would take longer) "
+                         "and print one JSON line; no GPU is used")
     args = ap.parse_args(argv)
+
+    if args.cpu_table:
+        print(json.dumps({"cpu_table": cpu_table(args.cpu_seconds)}), flush=True)
+        return 0
 
     if args.summarize_counters:
         for row in summarize_counters(args.summarize_counters,
