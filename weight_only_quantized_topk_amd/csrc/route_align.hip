@@ -3,7 +3,8 @@
 //
 // moe_route: one 64-lane wave per token.  Each lane holds up to 16 logits
 // (E <= 1024).  Top-k is k rounds of a wave-wide arg-max over the experts not
-// yet chosen, comparing (larger logit, then smaller expert index); up to 64
+// yet chosen, comparing (larger logit, then smaller expert index) as one
+// 64-bit value, reduced within rows of 16 lanes by DPP; up to 64
 // experts, each expert's rank in that order is counted directly instead (E
 // steps of a few instructions, against topk chains of shuffle reductions).  The slot
 // weights are exp(l_j - max) / sum, evaluated in double with the sum taken in
@@ -40,10 +41,42 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// (larger logit, then smaller expert index)
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-    const uint32_t ka = order_key(va), kb = order_key(vb);
-    return ka > kb || (ka == kb && ea < eb);
+// the logit of a key (a NaN for key 0; -0 comes back as +0)
+__device__ __forceinline__ float key_value(uint32_t k) {
+    if (k == 0u) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// a candidate expert as one unsigned 64-bit value, larger = better: the key
+// above, then the smaller expert index (its complement in the low half); 0
+// stands for no candidate (every real one has a low half >= ~1023)
+__device__ __forceinline__ uint64_t cand(uint32_t key, int e) { return ((uint64_t)key << 32) | (uint32_t)~e; }
+
+// larger of a lane's candidate and its partner's under a DPP lane pattern
+template <int CTRL>
+__device__ __forceinline__ uint64_t cand_max_dpp(uint64_t c) {
+    const int hi = (int)(uint32_t)(c >> 32), lo = (int)(uint32_t)c;
+    const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false) << 32) |
+                       (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+    return o > c ? o : c;
+}
+
+// the largest candidate of the wave, in every lane: within each row of 16
+// lanes by DPP (swap neighbours, swap pairs, mirror in 8, mirror in 16: each
+// step pairs every lane with one holding the other half of its group), then
+// across the rows by two shuffles
+__device__ __forceinline__ uint64_t wave_max_cand(uint64_t c) {
+    c = cand_max_dpp<0xB1>(c);   // quad_perm [1,0,3,2]
+    c = cand_max_dpp<0x4E>(c);   // quad_perm [2,3,0,1]
+    c = cand_max_dpp<0x141>(c);  // row_half_mirror
+    c = cand_max_dpp<0x140>(c);  // row_mirror
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+        const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(c >> 32), off, 64) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)c, off, 64);
+        c = o > c ? o : c;
+    }
+    return c;
 }
 
 // E <= 64: lane e holds logit e; its rank is the number of experts ahead of it
@@ -99,42 +132,30 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
                                             int* lds_ids) {
     if (E <= 64) return route_token_rank(l, E, topk, renormalize, lane, w_row, ids_row, lds_ids);
     float v[ROUTE_MAX_PER_LANE];
+    uint32_t key[ROUTE_MAX_PER_LANE];
     uint32_t avail = 0;  // bit i: slot i of this lane holds a not-yet-chosen expert
 #pragma unroll
     for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
         const int e = lane + 64 * i;
         v[i] = (e < E) ? l[e] : 0.0f;
+        key[i] = order_key(v[i]);
         if (e < E) avail |= 1u << i;
     }
     float sel_v = 0.0f;  // lane j < topk ends up holding slot j's logit
     int sel_e = 0;
     for (int j = 0; j < topk; ++j) {
-        // lane-local best; ascending i means ascending expert index
-        float bv = 0.0f;
-        int be = 0x7fffffff;
+        // lane-local best candidate (0: none), then the wave-wide maximum
+        uint64_t c = 0;
 #pragma unroll
         for (int i = 0; i < ROUTE_MAX_PER_LANE; ++i) {
-            if ((avail >> i) & 1u) {
-                const int e = lane + 64 * i;
-                if (be == 0x7fffffff || better(v[i], e, bv, be)) {
-                    bv = v[i];
-                    be = e;
-                }
-            }
+            const uint64_t ci = ((avail >> i) & 1u) ? cand(key[i], lane + 64 * i) : 0;
+            c = ci > c ? ci : c;
         }
-        // wave-wide arg-max
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (oe != 0x7fffffff && (be == 0x7fffffff || better(ov, oe, bv, be))) {
-                bv = ov;
-                be = oe;
-            }
-        }
+        c = wave_max_cand(c);
+        const int be = (int)~(uint32_t)c;
         if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
         if (lane == j) {
-            sel_v = bv;
+            sel_v = key_value((uint32_t)(c >> 32));
             sel_e = be;
         }
     }
