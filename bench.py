@@ -286,9 +286,20 @@ def measure_moe(torch, wq, gen, timer, spec, packed, m, steps, warmup):
     lg = torch.from_numpy(toks.logits).cuda()
     fp8 = isinstance(packed, PackedFp8MoE)
     runner = (wq.Fp8MoERunner if fp8 else wq.MoERunner)(packed, m, spec.topk, spec.renormalize)
+    # the stage times: events recorded between route+align, GATE_UP and DOWN
     spans, wall = timer.run(lambda marks: runner(x, lg, marks=marks), steps, warmup, 3)
-    ra, g1e, lay = spans[:, 0], spans[:, 1] - spans[:, 0], spans[:, 2]
+    ra, g1e = spans[:, 0], spans[:, 1] - spans[:, 0]
     down = spans[:, 2] - spans[:, 1]
+
+    # the layer time launched eagerly: the same step with no event between its
+    # stages (each recorded event is a packet the stream waits on)
+    def plain(marks):
+        runner(x, lg)
+        if marks:
+            marks[0].record()
+
+    pspans, wall = timer.run(plain, steps, warmup, 1)
+    lay = pspans[:, 0]
     # the same step replayed as one captured HIP graph (no per-launch host work)
     runner.capture(x, lg)
 
