@@ -8,6 +8,7 @@
  *   moe_route             router softmax + top-k
  *   moe_align             token sort and pad per expert
  *   moe_route_align       both in one call (one kernel for small batches)
+ *   moe_route_gate_up     route + sort + the GATE_UP GEMM (one kernel for the smallest batches)
  *   moe_w4a16_gemm        grouped GEMM, int4 GPTQ-style weights, fp16 activations
  *   moe_w8a16_gemm        grouped GEMM, int8 per-column weights, bf16/fp16 activations
  *   sparse24_w4a16_gemm   2:4-sparse int4 dense linear layer, fp16 activations
@@ -200,6 +201,29 @@ size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, in
                                 int act_order);
 wq_status moe_w4a16_gemm(const wq_moe_gemm_desc* d, void* stream);
 wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
+
+/*
+ * moe_route_gate_up: moe_route_align followed by the GATE_UP stage of
+ * moe_w4a16_gemm (wbits = 4) or moe_w8a16_gemm (wbits = 8), in one call.  For
+ * batches of at most 16 (token, slot) pairs over at most 64 experts, blocks of
+ * 16 or 32 rows, a capacity of at most 1024 rows and no act-order permutation,
+ * it is one launch: every workgroup of the small-batch GEMM ranks and sorts the
+ * batch itself (the decode step's route -> sort -> gate/up chain of "Marlin moe
+ * integration", nm-vllm PR 266, with the fused_moe interface of its review
+ * thread); otherwise it runs the two calls' launches in order.  The outputs
+ * are those of the two calls, bit for bit.
+ *   d_logits [M, E] float32, renormalize: as moe_route_align
+ *   d_topk_weights [M, topk] float32, d_topk_ids [M, topk] int32: written
+ *   d: a GATE_UP descriptor (stage WQ_STAGE_GATE_UP) whose d_sorted_token_ids,
+ *      d_expert_ids (capacity / block_size) and d_num_tokens_post_padded are
+ *      written here (cast away const: they are outputs of this call), with
+ *      capacity >= moe_align_capacity(M, topk, E, block_size) and topk <= 16;
+ *      every other field as for the GEMM call
+ * Errors: those of moe_route_align and of the GEMM call; WQ_ERR_INVALID for
+ * another stage or wbits.  M = 0 writes the empty sort and launches no GEMM.
+ */
+wq_status moe_route_gate_up(const float* d_logits, int renormalize, float* d_topk_weights, int32_t* d_topk_ids,
+                            const wq_moe_gemm_desc* d, int wbits, void* stream);
 
 /*
  * moe_w8a16_gemm_noalloc -- for callers that cannot allocate device memory

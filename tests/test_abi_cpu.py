@@ -189,6 +189,27 @@ def test_gemm_validation(fn, kw, expect):
     assert msg
 
 
+@pytest.mark.parametrize("wbits,kw,lp,expect,needle", [
+    (8, dict(group_size=-1, stage=wq.WQ_STAGE_DOWN, n_out=256, k_in=512), FAKE, wq.WQ_ERR_INVALID, "GATE_UP"),
+    (8, dict(group_size=-1, topk=17, E=32, capacity=wq.moe_align_capacity(4, 17, 32, 16)), FAKE,
+     wq.WQ_ERR_UNSUPPORTED, "topk"),
+    (5, dict(group_size=-1), FAKE, wq.WQ_ERR_INVALID, "wbits"),
+    (8, dict(group_size=-1), None, wq.WQ_ERR_INVALID, "logits"),
+    (8, dict(group_size=-1), FAKE + 4, wq.WQ_ERR_INVALID, "logits"),
+    (4, dict(act_dtype=wq.WQ_BF16), FAKE, wq.WQ_ERR_UNSUPPORTED, "fp16"),
+    (8, dict(group_size=-1, capacity=16), FAKE, wq.WQ_ERR_INVALID, "capacity"),
+])
+def test_route_gate_up_validation(wbits, kw, lp, expect, needle):
+    """moe_route_gate_up rejects a stage other than GATE_UP, a top-k beyond
+    the router's 16, a bad wbits, a NULL or misaligned logits pointer and the
+    GEMM's own bad arguments, before any device work."""
+    d = _desc(**kw)
+    p = C.c_void_p(FAKE)
+    st, msg = _status("moe_route_gate_up", C.c_void_p(lp) if lp else None, 1, p, p, C.byref(d), wbits, None)
+    assert st == expect, msg
+    assert needle in msg
+
+
 def test_gemm_workspace_sizes():
     L = wq.load()
     assert L.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, 4, 2, 8, 1024, 256, 128, 0) == 0

@@ -114,6 +114,47 @@ def test_moe_gemm_refuses_host_memory(bits, stage):
     assert not bool((out == 3.0).all())
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_route_gate_up_refuses_host_memory(bits):
+    """moe_route_gate_up (one kernel at this size) refuses host logits, host
+    routing outputs and a host H buffer, and writes nothing."""
+    need_gpu()
+    spec = W8 if bits == 8 else W4
+    wts = gen.make_moe_weights(spec, seed_config=50 + bits)
+    p = wq.pack_moe(bits, wts.w1q, wts.s1, wts.w2q, wts.s2, torch.bfloat16 if bits == 8 else torch.float16,
+                    spec.group_size)
+    M, bs = 2, 16
+    toks = gen.make_tokens(spec, M, seed_config=51)
+    cap = wq.moe_align_capacity(M, spec.topk, spec.E, bs)
+    x = dev_u16(toks.x, spec.act)
+    lg = torch.from_numpy(toks.logits).cuda()
+    w = torch.full((M, spec.topk), -7.0, device="cuda")
+    ids = torch.full((M, spec.topk), -7, dtype=torch.int32, device="cuda")
+    st = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    ex = torch.full((cap // bs,), -7, dtype=torch.int32, device="cuda")
+    nt = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    h = torch.full((cap, spec.N), 3.0, dtype=p.act, device="cuda")
+    gs = spec.group_size if bits == 4 else -1
+
+    def call(lg_=lg, w_=w, st_=st, h_=h):
+        wq.moe_route_gate_up(bits, lg_, True, w_, ids, x, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1, p.s1, gs,
+                             None, st_, ex, nt, cap, bs, h_, None, None, p.act_code)
+
+    name = "moe_route_gate_up w%d" % bits
+    expect_device_error(lambda: call(lg_=pinned(lg)), name + ", host logits")
+    expect_device_error(lambda: call(w_=pinned(w)), name + ", host topk_weights")
+    expect_device_error(lambda: call(st_=pinned(st)), name + ", host sorted_token_ids")
+    h_host = pinned(h)
+    expect_device_error(lambda: call(h_=h_host), name + ", host H")
+    assert bool((h_host == 3.0).all())
+    for t in (w, ids, st, ex, nt):
+        assert bool((t == -7).all())
+    assert bool((h == 3.0).all())
+    call()
+    torch.cuda.synchronize()
+    assert int(nt[0]) > 0 and not bool((h == 3.0).all())
+
+
 def test_sparse24_and_dense_refuse_host_memory():
     need_gpu()
     spec = gen.CFG4.with_(name="sparse-devcheck", K=512, N=256)

@@ -17,7 +17,7 @@ WQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "wq_version", "wq_status_string", "wq_last_error",
-    "moe_route", "moe_align_capacity", "moe_align", "moe_route_align",
+    "moe_route", "moe_align_capacity", "moe_align", "moe_route_align", "moe_route_gate_up",
     "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm", "moe_w8a16_gemm_noalloc",
     "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "wq_quantize_w8",
     "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
@@ -89,6 +89,7 @@ def load():
     L.moe_w4a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.moe_w8a16_gemm.argtypes = [C.POINTER(WqMoeGemmDesc), p]
     L.moe_w8a16_gemm_noalloc.argtypes = [C.POINTER(WqMoeGemmDesc), p]
+    L.moe_route_gate_up.argtypes = [p, i, p, p, C.POINTER(WqMoeGemmDesc), i, p]
     L.sparse24_w4a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
     L.sparse24_w8a16_gemm.argtypes = [p, i, i, i, p, p, p, i, p, i, p]
     L.wq_quantize_w8.argtypes = [p, C.c_int64, i, i, p, p, p]
@@ -113,7 +114,7 @@ def load():
     L.wq_pack_fp8_bytes.argtypes = [i, i, i]
     L.wq_pack_fp8_bytes.restype = sz
     L.wq_pack_fp8.argtypes = [i, i, i, p, p, p, i, p, p]
-    for f in ("moe_route", "moe_align", "moe_route_align", "moe_w4a16_gemm", "moe_w8a16_gemm",
+    for f in ("moe_route", "moe_align", "moe_route_align", "moe_route_gate_up", "moe_w4a16_gemm", "moe_w8a16_gemm",
               "moe_w8a16_gemm_noalloc", "sparse24_w4a16_gemm",
               "sparse24_w8a16_gemm",
               "wq_quantize_w8", "dense_w4a16_gemm", "dense_w8a16_gemm", "wq_pack_w4",

@@ -221,6 +221,26 @@ wq_status moe_align(const int32_t* d_topk_ids, int M, int topk, int E, int block
     }
 }
 
+// the launches of moe_route_align (arguments already validated)
+static wq_status launch_routing(const float* d_logits, int M, int E, int topk, int renormalize, int block_size,
+                               float* d_topk_weights, int32_t* d_topk_ids, int32_t* d_sorted_token_ids,
+                               int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded, size_t capacity,
+                               hipStream_t s, const char* who) {
+    const int rn = renormalize ? 1 : 0;
+    if (M > 0 && wq::route_align_fused(M, topk)) {
+        wq::launch_route_align(d_logits, M, E, topk, rn, d_topk_weights, d_topk_ids, block_size, d_sorted_token_ids,
+                               d_expert_ids, d_num_tokens_post_padded, (int)capacity, s);
+    } else {
+        if (M > 0) {
+            wq::launch_route(d_logits, M, E, topk, rn, d_topk_weights, d_topk_ids, s);
+            WQ_TRY(after_launch(who));
+        }
+        wq::launch_align(d_topk_ids, M * topk, E, block_size, d_sorted_token_ids, d_expert_ids,
+                         d_num_tokens_post_padded, (int)capacity, s);
+    }
+    return after_launch(who);
+}
+
 wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int renormalize, int block_size,
                           float* d_topk_weights, int32_t* d_topk_ids, int32_t* d_sorted_token_ids,
                           int32_t* d_expert_ids, int32_t* d_num_tokens_post_padded, size_t capacity, void* stream) {
@@ -252,20 +272,9 @@ wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int ren
         WQ_TRY(check_dev(d_sorted_token_ids, "sorted_token_ids"));
         WQ_TRY(check_dev(d_expert_ids, "expert_ids"));
         WQ_TRY(check_dev(d_num_tokens_post_padded, "num_tokens_post_padded"));
-        hipStream_t s = (hipStream_t)stream;
-        const int rn = renormalize ? 1 : 0;
-        if (M > 0 && wq::route_align_fused(M, topk)) {
-            wq::launch_route_align(d_logits, M, E, topk, rn, d_topk_weights, d_topk_ids, block_size,
-                                   d_sorted_token_ids, d_expert_ids, d_num_tokens_post_padded, (int)capacity, s);
-        } else {
-            if (M > 0) {
-                wq::launch_route(d_logits, M, E, topk, rn, d_topk_weights, d_topk_ids, s);
-                WQ_TRY(after_launch("moe_route_align"));
-            }
-            wq::launch_align(d_topk_ids, M * topk, E, block_size, d_sorted_token_ids, d_expert_ids,
-                             d_num_tokens_post_padded, (int)capacity, s);
-        }
-        return after_launch("moe_route_align");
+        return launch_routing(d_logits, M, E, topk, renormalize, block_size, d_topk_weights, d_topk_ids,
+                              d_sorted_token_ids, d_expert_ids, d_num_tokens_post_padded, capacity,
+                              (hipStream_t)stream, "moe_route_align");
     } catch (...) {
         return fail(WQ_ERR_HIP, "moe_route_align: unexpected exception");
     }
@@ -286,9 +295,20 @@ size_t moe_gemm_workspace_bytes(int stage, int M, int topk, int E, int n_out, in
     return b;
 }
 
+// A GATE_UP call that also routes the batch (moe_route_gate_up): the logits
+// and the routing outputs; the desc's sorted_token_ids / expert_ids /
+// num_tokens_post_padded are then written, not read.
+struct RouteRequest {
+    const float* logits;
+    int renormalize;
+    float* topk_weights;
+    int32_t* topk_ids;
+};
+
 // noalloc: the workspace is the library's scratch array (d_workspace must be
 // NULL and workspace_bytes 0; a need above its size is refused)
-static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, const char* who, bool noalloc = false) {
+static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, const char* who, bool noalloc = false,
+                          const RouteRequest* route = nullptr) {
     WQ_REQUIRE(d != nullptr, WQ_ERR_INVALID, "%s: desc is NULL", who);
     WQ_REQUIRE(d->struct_size >= sizeof(wq_moe_gemm_desc), WQ_ERR_INVALID, "%s: struct_size %zu < %zu", who,
                d->struct_size, sizeof(wq_moe_gemm_desc));
@@ -319,6 +339,10 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     const bool act_order = d->d_k_perm != nullptr;
     WQ_REQUIRE(!act_order || (wbits == 4 && stage != WQ_STAGE_DOWN), WQ_ERR_INVALID,
                "%s: k_perm only applies to int4 GATE_UP/RAW", who);
+    if (route) {
+        WQ_REQUIRE(stage == WQ_STAGE_GATE_UP, WQ_ERR_INVALID, "%s: routing goes with the GATE_UP stage", who);
+        WQ_REQUIRE(d->topk <= 16, WQ_ERR_UNSUPPORTED, "%s: topk = %d > 16", who, d->topk);
+    }
     const size_t ws = moe_gemm_workspace_bytes(stage, d->M, d->topk, d->E, d->n_out, d->k_in, d->capacity, act_order);
     if (noalloc) {
         WQ_REQUIRE(d->d_workspace == nullptr && d->workspace_bytes == 0, WQ_ERR_INVALID,
@@ -330,7 +354,20 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
         WQ_REQUIRE(d->workspace_bytes >= ws, WQ_ERR_INVALID, "%s: workspace %zu < required %zu", who,
                    d->workspace_bytes, ws);
     }
-    if (d->M == 0) return ok();
+    if (d->M == 0) {
+        if (!route) return ok();
+        // no tokens: the routing arrays are still written (an empty sort)
+        WQ_TRY(check_ptr(d->d_sorted_token_ids, "sorted_token_ids"));
+        WQ_TRY(check_ptr(d->d_expert_ids, "expert_ids"));
+        WQ_TRY(check_ptr(d->d_num_tokens_post_padded, "num_tokens_post_padded"));
+        WQ_TRY(check_dev(d->d_sorted_token_ids, "sorted_token_ids"));
+        WQ_TRY(check_dev(d->d_expert_ids, "expert_ids"));
+        WQ_TRY(check_dev(d->d_num_tokens_post_padded, "num_tokens_post_padded"));
+        return launch_routing(nullptr, 0, d->E, d->topk, route->renormalize, d->block_size, nullptr, nullptr,
+                              const_cast<int32_t*>(d->d_sorted_token_ids), const_cast<int32_t*>(d->d_expert_ids),
+                              const_cast<int32_t*>(d->d_num_tokens_post_padded), d->capacity, (hipStream_t)stream,
+                              who);
+    }
     WQ_TRY(check_ptr(d->d_a, "a"));
     WQ_TRY(check_ptr(d->d_w_packed, "w_packed"));
     WQ_TRY(check_ptr(d->d_scales, "scales"));
@@ -341,6 +378,14 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     if (act_order) WQ_TRY(check_ptr(d->d_k_perm, "k_perm"));
     if (stage == WQ_STAGE_DOWN) WQ_TRY(check_ptr(d->d_topk_weights, "topk_weights"));
     if (ws && !noalloc) WQ_TRY(check_ptr(d->d_workspace, "workspace"));
+    if (route) {
+        WQ_TRY(check_ptr(route->logits, "logits"));
+        WQ_TRY(check_ptr(route->topk_weights, "topk_weights"));
+        WQ_TRY(check_ptr(route->topk_ids, "topk_ids"));
+        WQ_TRY(check_dev(route->logits, "logits"));
+        WQ_TRY(check_dev(route->topk_weights, "topk_weights"));
+        WQ_TRY(check_dev(route->topk_ids, "topk_ids"));
+    }
 
     WQ_TRY(check_dev(d->d_a, "a"));
     WQ_TRY(check_dev(d->d_w_packed, "w_packed"));
@@ -387,6 +432,27 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     WQ_REQUIRE(!large || wq::prefill_fits(d->capacity, d->k_in), WQ_ERR_UNSUPPORTED,
                "%s: activations of %zu rows x %d channels exceed 4 GiB (large-batch kernel)", who, d->capacity,
                d->k_in);
+    if (route) {
+        if (!act_order && !tiny && !large &&
+            wq::decode_route_supported(stage, d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
+            // one launch: the small-batch kernel routes and sorts the batch itself
+            wq::RouteArgs ra;
+            ra.logits = route->logits;
+            ra.renormalize = route->renormalize ? 1 : 0;
+            ra.w_out = route->topk_weights;
+            ra.ids_out = route->topk_ids;
+            // the desc's routing arrays are outputs of this call
+            ra.sorted_out = const_cast<int32_t*>(d->d_sorted_token_ids);
+            ra.expert_ids_out = const_cast<int32_t*>(d->d_expert_ids);
+            ra.ntpp_out = const_cast<int32_t*>(d->d_num_tokens_post_padded);
+            wq::launch_gemm_decode_route(wbits, bf16, g, ra, s);
+            return after_launch(who);
+        }
+        WQ_TRY(launch_routing(route->logits, d->M, d->E, d->topk, route->renormalize, d->block_size,
+                              route->topk_weights, route->topk_ids, const_cast<int32_t*>(d->d_sorted_token_ids),
+                              const_cast<int32_t*>(d->d_expert_ids),
+                              const_cast<int32_t*>(d->d_num_tokens_post_padded), d->capacity, s, who));
+    }
     if (act_order && !tiny) {
         uint16_t* a1 = static_cast<uint16_t*>(workspace);
         wq::launch_gather_perm(g.a, d->d_k_perm, g.sorted, g.expert_ids, g.ntpp, d->M, d->topk, d->k_in,
@@ -425,6 +491,17 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream) {
         return moe_gemm(d, 8, stream, "moe_w8a16_gemm");
     } catch (...) {
         return fail(WQ_ERR_HIP, "moe_w8a16_gemm: unexpected exception");
+    }
+}
+
+wq_status moe_route_gate_up(const float* d_logits, int renormalize, float* d_topk_weights, int32_t* d_topk_ids,
+                            const wq_moe_gemm_desc* d, int wbits, void* stream) {
+    try {
+        WQ_REQUIRE(wbits == 4 || wbits == 8, WQ_ERR_INVALID, "moe_route_gate_up: wbits %d not 4 or 8", wbits);
+        const RouteRequest rr{d_logits, renormalize, d_topk_weights, d_topk_ids};
+        return moe_gemm(d, wbits, stream, "moe_route_gate_up", false, &rr);
+    } catch (...) {
+        return fail(WQ_ERR_HIP, "moe_route_gate_up: unexpected exception");
     }
 }
 

@@ -25,6 +25,7 @@
 // heuristics).
 #include "common.hpp"
 #include "launch.hpp"
+#include "route_common.hpp"
 
 #include <algorithm>
 #include <type_traits>
@@ -34,8 +35,13 @@ namespace wq {
 // Kernel shape: NP weight-row tiles per workgroup (pairs of gate+up tiles for
 // the fused stage), NW waves splitting the input channels, DEPTH 1 KiB chunks
 // per tile in flight per wave, up to RMAX 16-row token blocks per pass.
-template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH>
-__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
+// FR: the workgroup first routes and sorts the batch itself (every workgroup
+// the same, in LDS; the first one also writes the routing arrays for the
+// later stages), so route, sort and gate/up are one launch.  For batches of at
+// most FR_MAX_PAIRS pairs over at most 64 experts and a capacity of at most
+// FR_MAX_CAP rows.
+template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH, bool FR = false>
+__global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g, RouteArgs ra) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;  // 16-row tiles per workgroup
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     constexpr int KSTEPS = KCHUNK / 32;
@@ -50,6 +56,38 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
     const int spb = BS / 16;
     __shared__ f32x4 red[NW][NT][RMAX][64];
 
+    // the routing arrays: the caller's, or (FR) computed here into LDS
+    const int32_t* sorted_ids = g.sorted;
+    const int32_t* block_expert = g.expert_ids;
+    int ntpp;
+    if constexpr (FR) {
+        __shared__ int fr_sorted[FR_MAX_CAP];
+        __shared__ int fr_blocks[FR_MAX_CAP / 16];
+        __shared__ int fr_ids[FR_MAX_PAIRS];
+        __shared__ float fr_w[FR_MAX_PAIRS];
+        __shared__ int fr_ntpp;
+        for (int m = wave; m < g.M; m += NW)  // E <= 64: the rank-counting top-k
+            route_token_rank(ra.logits + (size_t)m * g.E, g.E, g.topk, ra.renormalize, lane, fr_w + m * g.topk,
+                             fr_ids + m * g.topk, nullptr);
+        __syncthreads();
+        if (wave == 0) align_wave(fr_ids, T, g.E, BS, g.cap, lane, fr_sorted, fr_blocks, &fr_ntpp);
+        __syncthreads();
+        if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+            for (int i = threadIdx.x; i < T; i += 64 * NW) {
+                ra.w_out[i] = fr_w[i];
+                ra.ids_out[i] = fr_ids[i];
+            }
+            for (int i = threadIdx.x; i < g.cap; i += 64 * NW) ra.sorted_out[i] = fr_sorted[i];
+            for (int i = threadIdx.x; i < g.cap / BS; i += 64 * NW) ra.expert_ids_out[i] = fr_blocks[i];
+            if (threadIdx.x == 0) *ra.ntpp_out = fr_ntpp;
+        }
+        sorted_ids = fr_sorted;
+        block_expert = fr_blocks;
+        ntpp = fr_ntpp;
+    } else {
+        ntpp = *g.ntpp;
+    }
+
     // 16-row sub-block sbi of sorted_token_ids (grid y, then z past 65535), in block b.  The lanes read the
     // expert ids of blocks b - 31 .. b + 32 at once; the used blocks of one
     // expert are contiguous, so the lanes holding b's expert form one run
@@ -57,20 +95,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
     const int sbi = blockIdx.y + 65535 * blockIdx.z;
     const int b = sbi / spb;
     const int bi = b - 31 + lane;
-    const int ecand = (bi >= 0 && bi < g.cap / BS) ? g.expert_ids[bi] : -1;
-    const int ntpp = *g.ntpp;
+    const int ecand = (bi >= 0 && bi < g.cap / BS) ? block_expert[bi] : -1;
     if (sbi * 16 >= ntpp) return;
     const int nbu = ntpp / BS;
     const int e = __shfl(ecand, 31);
     const uint64_t run = __ballot(bi >= 0 && bi < nbu && ecand == e);
-    const int b0 = (run & 1ull) ? lower_bound_i32(g.expert_ids, 0, b - 31, e) : b - 31 + __builtin_ctzll(run);
-    const int b1 = (run >> 63) ? lower_bound_i32(g.expert_ids, b + 33, nbu, e + 1) : b - 31 + 64 - __builtin_clzll(run);
+    const int b0 = (run & 1ull) ? lower_bound_i32(block_expert, 0, b - 31, e) : b - 31 + __builtin_ctzll(run);
+    const int b1 = (run >> 63) ? lower_bound_i32(block_expert, b + 33, nbu, e + 1) : b - 31 + 64 - __builtin_clzll(run);
     const int sb_first = b0 * spb;
     const int j = sbi - sb_first;  // sub-block index within the expert
     if (j % RMAX != 0) return;     // one workgroup per RMAX sub-blocks
     // live 16-row sub-blocks of the expert's last block (those whose first row
     // is a real pair: a prefix of the block)
-    const int q = __popcll(__ballot(lane < spb && g.sorted[(b1 - 1) * BS + 16 * min(lane, spb - 1)] < T));
+    const int q = __popcll(__ballot(lane < spb && sorted_ids[(b1 - 1) * BS + 16 * min(lane, spb - 1)] < T));
     const int S = (b1 - 1 - b0) * spb + q;
 
     const int C = g.k_in / KCHUNK;
@@ -97,10 +134,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
             // outputs dropped), so every load below is unconditional
             const int p_first = (sb_first + s0 + r) * 16;
             const int p = p_first + (lane & 15);
-            const int pair = g.sorted[p];
+            const int pair = sorted_ids[p];
             avalid[r] = pair < T;
             const int pl = avalid[r] ? p : p_first;
-            const int row = g.a_direct ? pl : g.sorted[pl] / g.topk;
+            const int row = g.a_direct ? pl : sorted_ids[pl] / g.topk;
             arow[r] = g.a + (size_t)row * g.k_in + 8 * (lane >> 4);
         }
 
@@ -199,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
             const int pp = item / R;  // tile (or gate/up tile pair) within the workgroup
             const int r = item % R;
             const int p = (sb_first + s0 + r) * 16 + (lane & 15);
-            const int pair = g.sorted[p];
+            const int pair = sorted_ids[p];
             if constexpr (STAGE == STAGE_GATE_UP) {
                 const int tg = 2 * pp, tu = 2 * pp + 1;  // gate and up tile within the workgroup
                 f32x4 gv = red[0][tg][r][lane], uv = red[0][tu][r][lane];
@@ -275,12 +312,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g) {
     }
 }
 
-template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH>
-static void launch_decode_cfg(const GemmArgs& g, hipStream_t s) {
+template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH, bool FR = false>
+static void launch_decode_cfg(const GemmArgs& g, hipStream_t s, const RouteArgs& ra = RouteArgs{}) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;
     const int nsb = g.cap / 16;  // 16-row sub-blocks, over grid y (at most 65535) and z
     const dim3 grid(g.n_out / (TILE_ROWS * NT), std::min(nsb, 65535), (nsb + 65534) / 65535);
-    hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH>), grid, dim3(64 * NW), 0, s, g);
+    hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH, FR>), grid, dim3(64 * NW), 0, s,
+                       g, ra);
 }
 
 // Shapes by batch, measured on MI355X with the last-level cache flushed before
@@ -341,6 +379,28 @@ static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
         if (!GU && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 4, 2, 4, 2>(g, s);
         else launch_decode_cfg<WBITS, BF16, STAGE, 4, 1, 4, 2>(g, s);
     }
+}
+
+// the GATE_UP shapes launch_decode_r picks for up to 16 pairs, with the routing done in the kernel
+bool decode_route_supported(int stage, int M, int topk, int E, int cap, int block_size) {
+    const long T = (long)M * topk;
+    return stage == STAGE_GATE_UP && M >= 1 && T <= 16 && T <= FR_MAX_PAIRS && E >= 1 && E <= 64 &&
+           cap <= FR_MAX_CAP && (block_size == 16 || block_size == 32);
+}
+
+template <int WBITS, bool BF16>
+static void launch_decode_route_w(const GemmArgs& g, const RouteArgs& ra, hipStream_t s) {
+    const int T = g.M * g.topk;
+    const bool np2_ok = (g.n_out % (TILE_ROWS * 2 * 2)) == 0;
+    if (WBITS == 4 && np2_ok && T <= 4) launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 2, 2, 2, true>(g, s, ra);
+    else if (WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 2, 4, 2, true>(g, s, ra);
+    else launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 1, 4, 2, true>(g, s, ra);
+}
+
+void launch_gemm_decode_route(int wbits, bool bf16, const GemmArgs& g, const RouteArgs& ra, hipStream_t s) {
+    if (wbits == 4) launch_decode_route_w<4, false>(g, ra, s);
+    else if (bf16) launch_decode_route_w<8, true>(g, ra, s);
+    else launch_decode_route_w<8, false>(g, ra, s);
 }
 
 template <int WBITS, bool BF16>

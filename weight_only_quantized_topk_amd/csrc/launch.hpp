@@ -85,6 +85,26 @@ int launch_gemm_fp8(int stage, const Fp8GemmArgs& g, hipStream_t s);
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
 void launch_gemm_decode(int wbits, bool bf16, int stage, const GemmArgs& g, hipStream_t s);
+
+// The small-batch GATE_UP launch that routes and sorts the batch itself (one
+// launch for moe_route_align + GATE_UP): the logits, the softmax mode and the
+// routing arrays it writes (topk weights and ids, sorted_token_ids,
+// expert_ids, num_tokens_post_padded; g.sorted / g.expert_ids / g.ntpp are
+// not read).
+struct RouteArgs {
+    const float* logits = nullptr;
+    int renormalize = 0;
+    float* w_out = nullptr;
+    int32_t* ids_out = nullptr;
+    int32_t* sorted_out = nullptr;
+    int32_t* expert_ids_out = nullptr;
+    int32_t* ntpp_out = nullptr;
+};
+constexpr int FR_MAX_PAIRS = 64;   // M * topk
+constexpr int FR_MAX_CAP = 1024;   // capacity rows held in LDS
+// up to 16 pairs over at most 64 experts, blocks of 16 or 32 rows
+bool decode_route_supported(int stage, int M, int topk, int E, int cap, int block_size);
+void launch_gemm_decode_route(int wbits, bool bf16, const GemmArgs& g, const RouteArgs& ra, hipStream_t s);
 // batches of at most 4 tokens: one workgroup per (used block, 16 or 32 weight
 // rows), the block's token rows staged in LDS (through the act-order
 // permutation perm [E, k_in] when not NULL, GATE_UP / RAW only); DOWN in up

@@ -121,10 +121,19 @@ class MoERunner:
         self.work2 = torch.empty(ws2, dtype=torch.uint8, device=dev) if ws2 else None
         self.h = torch.empty((max(self.cap, 1), p.N), dtype=p.act, device=dev)
         self.out = torch.empty((M, p.K), dtype=p.act, device=dev)
+        # the smallest batches route inside the GATE_UP launch (moe_route_gate_up)
+        self.route_in_gate_up = (not act_order and M * topk <= 16 and p.E <= 64 and self.bs in (16, 32)
+                                 and self.cap <= 1024)
 
     def route_align(self, logits, stream=None):
         ops.moe_route_align(logits, self.topk, self.renormalize, self.bs, self.w, self.ids, self.st, self.ex,
                             self.nt, self.cap, stream=stream)
+
+    def route_gate_up(self, x, logits, stream=None):
+        q = self.p
+        ops.moe_route_gate_up(q.bits, logits, self.renormalize, self.w, self.ids, x, self.M, self.topk, q.E, 2 * q.N,
+                              q.K, q.w1, q.s1, q.group_size if q.bits == 4 else -1, q.k_perm1, self.st, self.ex,
+                              self.nt, self.cap, self.bs, self.h, self.work1, stream, q.act_code)
 
     def gate_up(self, x, stream=None):
         p = self
@@ -147,10 +156,16 @@ class MoERunner:
                                p.bs, p.w, p.out, p.work2, stream, q.act_code)
 
     def __call__(self, x, logits, marks=None, stream=None):
-        self.route_align(logits, stream)
-        if marks:
-            marks[0].record()
-        self.gate_up(x, stream)
+        if getattr(self, "route_in_gate_up", False):
+            # one launch for route, sort and GATE_UP (timed as GATE_UP)
+            if marks:
+                marks[0].record()
+            self.route_gate_up(x, logits, stream)
+        else:
+            self.route_align(logits, stream)
+            if marks:
+                marks[0].record()
+            self.gate_up(x, stream)
         if marks:
             marks[1].record()
         self.down(stream)

@@ -18,6 +18,7 @@ from ._lib import (WQ_BF16, WQ_F16, WQ_PACK_INTERLEAVE_GATE_UP, WQ_STAGE_DOWN, W
 
 __all__ = [
     "moe_route", "moe_align", "moe_route_align", "moe_align_capacity", "moe_gemm_workspace_bytes", "moe_w4a16_gemm", "moe_w8a16_gemm",
+    "moe_route_gate_up",
     "moe_w8a16_gemm_noalloc", "sparse24_w4a16_gemm", "sparse24_w8a16_gemm", "quantize_w8", "dense_gemm_workspace_bytes", "dense_w4a16_gemm", "dense_w8a16_gemm",
     "pack_w4", "pack_w8", "pack_sparse24", "act_code", "moe_fp8_gemm_workspace_bytes", "moe_fp8_w8a8_gemm",
     "pack_fp8",
@@ -107,9 +108,9 @@ def moe_gemm_workspace_bytes(stage: int, M: int, topk: int, E: int, n_out: int, 
     return int(load().moe_gemm_workspace_bytes(stage, M, topk, E, n_out, k_in, capacity, int(bool(act_order))))
 
 
-def _gemm(fn_name: str, stage: int, a, M: int, topk: int, E: int, n_out: int, k_in: int, w_packed, scales,
-          group_size: int, k_perm, sorted_token_ids, expert_ids, num_tokens_post_padded, capacity: int,
-          block_size: int, topk_weights, out, workspace, stream, act_dtype: int):
+def _desc(stage: int, a, M: int, topk: int, E: int, n_out: int, k_in: int, w_packed, scales, group_size: int,
+          k_perm, sorted_token_ids, expert_ids, num_tokens_post_padded, capacity: int, block_size: int, topk_weights,
+          out, workspace, act_dtype: int):
     d = WqMoeGemmDesc()
     d.struct_size = C.sizeof(WqMoeGemmDesc)
     d.stage = stage
@@ -129,7 +130,28 @@ def _gemm(fn_name: str, stage: int, a, M: int, topk: int, E: int, n_out: int, k_
     d.d_out = _ptr(out)
     d.d_workspace = _ptr(workspace)
     d.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return d
+
+
+def _gemm(fn_name: str, stage: int, a, M: int, topk: int, E: int, n_out: int, k_in: int, w_packed, scales,
+          group_size: int, k_perm, sorted_token_ids, expert_ids, num_tokens_post_padded, capacity: int,
+          block_size: int, topk_weights, out, workspace, stream, act_dtype: int):
+    d = _desc(stage, a, M, topk, E, n_out, k_in, w_packed, scales, group_size, k_perm, sorted_token_ids, expert_ids,
+              num_tokens_post_padded, capacity, block_size, topk_weights, out, workspace, act_dtype)
     check(getattr(load(), fn_name)(C.byref(d), _stream(stream)), fn_name)
+    return out
+
+
+def moe_route_gate_up(wbits: int, logits, renormalize: bool, topk_weights, topk_ids, a, M, topk, E, n_out, k_in,
+                      w_packed, scales, group_size, k_perm, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                      capacity, block_size, out, workspace=None, stream=None, act_dtype=WQ_BF16):
+    """moe_route_align followed by the GATE_UP stage of moe_w{wbits}a16_gemm in
+    one call (one kernel for the smallest batches); writes topk_weights,
+    topk_ids, sorted_token_ids, expert_ids, num_tokens_post_padded and out."""
+    d = _desc(WQ_STAGE_GATE_UP, a, M, topk, E, n_out, k_in, w_packed, scales, group_size, k_perm, sorted_token_ids,
+              expert_ids, num_tokens_post_padded, capacity, block_size, None, out, workspace, act_dtype)
+    check(load().moe_route_gate_up(_ptr(logits), int(bool(renormalize)), _ptr(topk_weights), _ptr(topk_ids),
+                                   C.byref(d), wbits, _stream(stream)), "moe_route_gate_up")
     return out
 
 
