@@ -273,8 +273,12 @@ wq_status moe_w8a16_gemm_noalloc(const wq_moe_gemm_desc* d, void* stream);
  *  RAW      d_a = x as for GATE_UP; d_out = fp32 [M*topk, n_out] (testing).
  *  d_scales float32 [E, n_out] from wq_pack_fp8 (packed row order);
  *  group_size -1; d_k_perm NULL; in_scale (and for GATE_UP out_scale) finite
- *  and > 0; the workspace (moe_fp8_gemm_workspace_bytes) holds the x codes
- *  (GATE_UP / RAW) or the fp32 per-pair rows of DOWN.
+ *  and > 0; the workspace (moe_fp8_gemm_workspace_bytes) is scratch for the
+ *  x codes (GATE_UP / RAW) or the fp32 per-pair rows of DOWN.  One token
+ *  (M == 1) on the small-batch kernel: GATE_UP quantises x inside the GEMM
+ *  (k_in <= 32768), and DOWN with top-k <= 4 and k_in >= 4096 adds the
+ *  top-k rows inside the GEMM (the H code rows in LDS, topk * (k_in + 16)
+ *  bytes <= 128 KiB); neither then uses the workspace.
  * Blocks of 64 or a multiple of 128 (n_out % 128 == 0) take the large-batch
  * kernel (v_mfma_scale_f32_16x16x128_f8f6f4, token rows in LDS), which
  * refuses more than 4 GiB of activation codes; other blocks the small-batch

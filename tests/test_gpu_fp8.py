@@ -14,8 +14,9 @@ shapes that span several tiles with ragged token counts, on both kernels
     sums carry about 1e-4 relative error where the oracle's are exact, and an
     H value that close to an E4M3 rounding boundary may land on the other
     side: 0.1 % of the values here);
-  - DOWN from the oracle's H codes, and the whole layer, within the float
-    tolerance (relative Frobenius error <= 5e-3, max abs error <= 3e-2 max |ref|);
+  - DOWN from the oracle's H codes (for one token also with the top-k sum
+    folded into the GEMM: top-k 1 to 4, an expert named twice), and the whole
+    layer, within the float tolerance (relative Frobenius error <= 5e-3, max abs error <= 3e-2 max |ref|);
   - determinism, bit for bit."""
 import numpy as np
 import pytest
@@ -283,3 +284,58 @@ def test_layer_deterministic_and_equivariant(bs):
     c = wq.fused_moe_fp8(x[perm].contiguous(), lg[perm].contiguous(), p, spec.topk, block_size=bs)
     torch.cuda.synchronize()
     assert torch.equal(c, a[perm])
+
+
+# one token with the top-k sum folded into DOWN (32 or more 2 KiB chunks per
+# tile): every compiled top-k (1-4), small and large blocks, an expert named twice
+@pytest.mark.parametrize("topk", [1, 2, 3, 4])
+@pytest.mark.parametrize("bs", [16, 256])
+@pytest.mark.parametrize("twice", [False, True])
+def test_down_one_token(topk, bs, twice):
+    need_gpu()
+    if twice and topk == 1:
+        pytest.skip("one slot cannot name an expert twice")
+    spec0, wts, p = setup("f8k")
+    spec = spec0.with_(topk=topk)
+    toks = gen.make_tokens(spec, 1, seed_config=1370 + topk)
+    rng = np.random.default_rng(1380 + topk + 10 * twice)
+    ids = rng.permutation(spec.E)[:topk].astype(np.int32).reshape(1, topk)
+    if twice:
+        ids[0, -1] = ids[0, 0]
+    w = rng.uniform(0.1, 1.0, size=(1, topk)).astype(np.float32)
+    res = oracle.fp8_moe_layer(toks.x_f32(), w, ids, wts.w1, wts.s1, wts.w2, wts.s2, spec.a1, spec.a2,
+                               want=("out", "hq"))
+    st, ex, nt, cap = align_dev(ids, spec.E, bs)
+    stn, ntn = st.cpu().numpy(), int(nt.cpu()[0])
+    hs = np.zeros((cap, spec.N), np.uint8)
+    live = stn[:ntn] < topk
+    hs[:ntn][live] = res["hq"][stn[:ntn][live]]
+    say("fp8 one-token down", topk, bs, twice)
+    out, *_ = run_stage(wq.WQ_STAGE_DOWN, p, spec, torch.from_numpy(hs).cuda(), 1, ids, bs, w=w)
+    torch.cuda.synchronize()
+    assert_close_fp(host_f32(out), res["out"], "fp8 one token topk=%d bs=%d twice=%s" % (topk, bs, twice))
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_gate_up_one_token_quantised_in_kernel(act, bs):
+    """One token's GATE_UP quantises x inside the GEMM: its H codes are the
+    oracle's (up to the neighbouring-code rule above), in both 16-bit types."""
+    need_gpu()
+    spec, wts, _ = setup("f8")
+    tdt = torch.bfloat16 if act == "bf16" else torch.float16
+    p = wq.pack_moe_fp8(wts.w1, wts.s1, wts.w2, wts.s2, tdt, spec.a1, spec.a2)
+    toks, w, ids = routed(spec.with_(act=act), 1, seed=1390 + bs)
+    say("fp8 one-token gate_up", act, bs)
+    h, _, st, ex, nt, cap = run_stage(wq.WQ_STAGE_GATE_UP, p, spec, dev_u16(toks.x, act), 1, ids, bs, act=tdt)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_moe_layer(toks.x_f32(), w, ids, wts.w1, wts.s1, wts.w2, wts.s2, spec.a1, spec.a2, want=("out", "hq"))["hq"]
+    hg = h.cpu().numpy()
+    stn, ntn = st.cpu().numpy(), int(nt.cpu()[0])
+    live = np.nonzero(stn[:ntn] < spec.topk)[0]
+    got = np.empty_like(ref)
+    got[stn[live]] = hg[live]
+    diff = got != ref
+    assert int(diff.sum()) <= max(2, ref.size // 100)
+    if diff.any():
+        assert np.all(np.abs(value_rank(got[diff]) - value_rank(ref[diff])) <= 1)

@@ -608,7 +608,15 @@ static wq_status fp8_gemm(const wq_moe_gemm_desc* d, float in_scale, float out_s
     if (stage == WQ_STAGE_DOWN) {
         g.a = static_cast<const uint8_t*>(d->d_a);  // H codes in sorted order
         g.a_direct = 1;
+        if (wq::fp8_down_combine_supported(d->M, d->topk, d->n_out, d->k_in)) {
+            wq::launch_fp8_down_combine(bf16, g, s);  // g.out: the output row
+            return after_launch(who);
+        }
         g.out = d->d_workspace;                     // fp32 Y slabs
+    } else if (wq::fp8_fold_quant_supported(stage, d->M, d->n_out, d->k_in, d->block_size)) {
+        g.x16 = static_cast<const uint16_t*>(d->d_a);  // quantised inside the GEMM
+        g.x_bf16 = bf16 ? 1 : 0;
+        g.a_direct = 0;
     } else {
         uint8_t* xq = static_cast<uint8_t*>(d->d_workspace);
         wq::launch_fp8_quant(static_cast<const uint16_t*>(d->d_a), d->M, d->k_in, bf16, in_scale, xq, s);

@@ -24,6 +24,7 @@
 // projections (testing).
 #include "common.hpp"
 #include "launch.hpp"
+#include "one_token.hpp"
 
 #include <algorithm>
 #include <type_traits>
@@ -88,7 +89,10 @@ void launch_fp8_quant(const uint16_t* x, int64_t rows, int k, bool bf16, float s
 // ---------------------------------------------------------------------------
 // small-batch kernel
 // ---------------------------------------------------------------------------
-template <int STAGE, int RMAX, int NP, int NW, int DEPTH>
+// QX (GATE_UP of one token): the workgroup quantises the token's row into LDS
+// itself (the quantisation kernel's arithmetic, so the same codes) and takes
+// every B operand from there; all rows of the sorted order are that token's.
+template <int STAGE, int RMAX, int NP, int NW, int DEPTH, bool QX = false>
 __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;  // 16-row weight tiles per workgroup
     static_assert(NW * NT * RMAX * 1024 <= 64 * 1024, "LDS reduction buffer");
@@ -101,6 +105,7 @@ __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
     const int BS = g.block_size;
     const int spb = BS / 16;
     __shared__ f32x4 red[NW][NT][RMAX][64];
+    extern __shared__ __attribute__((aligned(16))) uint8_t xq_lds[];  // QX: the token's k_in codes
 
     // the expert's run of blocks around block b (as in the int8 small-batch kernel)
     const int sbi = blockIdx.y + 65535 * blockIdx.z;
@@ -156,8 +161,14 @@ __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
                 wv[d][t] = cat8(ldg128_stream(wt[t] + (size_t)c * FP8_CHUNK_BYTES),
                                 ldg128_stream(wt[t] + (size_t)c * FP8_CHUNK_BYTES + 1024));
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                xv[d][r] = cat8(ldg128(arow[r] + c * FP8_KCHUNK), ldg128(arow[r] + c * FP8_KCHUNK + 16));
+            for (int r = 0; r < R; ++r) {
+                if constexpr (QX) {
+                    const uint8_t* xl = xq_lds + c * FP8_KCHUNK + 32 * (lane >> 4);
+                    xv[d][r] = cat8(*reinterpret_cast<const u32x4*>(xl), *reinterpret_cast<const u32x4*>(xl + 16));
+                } else {
+                    xv[d][r] = cat8(ldg128(arow[r] + c * FP8_KCHUNK), ldg128(arow[r] + c * FP8_KCHUNK + 16));
+                }
+            }
         };
         auto compute = [&](int d) {
 #pragma unroll
@@ -239,6 +250,22 @@ __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
         }
     }
     if (j >= S) return;
+    if constexpr (QX) {
+        for (int i = threadIdx.x; i < g.k_in / 8; i += 64 * NW) {
+            const u32x4 v = ldg128(g.x16 + 8 * i);
+            float f[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint16_t h = (uint16_t)(v[k >> 1] >> (16 * (k & 1)));
+                f[k] = __fdiv_rn(g.x_bf16 ? act_to_f32<true>(h) : act_to_f32<false>(h), g.in_scale);
+            }
+            u32x2 o;
+            o[0] = e4m3x4(f[0], f[1], f[2], f[3]);
+            o[1] = e4m3x4(f[4], f[5], f[6], f[7]);
+            *reinterpret_cast<u32x2*>(xq_lds + 8 * i) = o;
+        }
+        __syncthreads();
+    }
     const int R = min(RMAX, S - j);
     if (R == RMAX) {
         pass(j, std::integral_constant<int, RMAX>{});
@@ -256,12 +283,17 @@ __global__ __launch_bounds__(64 * NW) void fp8_decode_kernel(Fp8GemmArgs g) {
     }
 }
 
-template <int STAGE, int RMAX, int NP, int NW, int DEPTH>
+template <int STAGE, int RMAX, int NP, int NW, int DEPTH, bool QX = false>
 static void launch_fp8_decode_cfg(const Fp8GemmArgs& g, hipStream_t s) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;
     const int nsb = g.cap / 16;
     const dim3 grid(g.n_out / (TILE_ROWS * NT), std::min(nsb, 65535), (nsb + 65534) / 65535);
-    hipLaunchKernelGGL((fp8_decode_kernel<STAGE, RMAX, NP, NW, DEPTH>), grid, dim3(64 * NW), 0, s, g);
+    hipLaunchKernelGGL((fp8_decode_kernel<STAGE, RMAX, NP, NW, DEPTH, QX>), grid, dim3(64 * NW), QX ? g.k_in : 0, s,
+                       g);
+}
+
+bool fp8_fold_quant_supported(int stage, int M, int n_out, int k_in, int block_size) {
+    return stage == STAGE_GATE_UP && M == 1 && k_in <= FP8_FOLD_MAX_K && !fp8_prefill_supported(n_out, k_in, block_size);
 }
 
 // Shapes by the mean rows per touched expert, as for the int8 small-batch
@@ -276,6 +308,12 @@ static void launch_fp8_decode_r(const Fp8GemmArgs& g, hipStream_t s) {
     const int rows = (T + touched - 1) / touched;
     const bool np2_ok = (g.n_out % (TILE_ROWS * NT1 * 2)) == 0;
     const bool short_k = g.k_in / FP8_KCHUNK <= 16;
+    if constexpr (GU) {
+        if (g.x16) {  // one token, quantised in the kernel
+            launch_fp8_decode_cfg<STAGE, 1, 1, 4, 2, true>(g, s);
+            return;
+        }
+    }
     if (g.E >= 64 && T > 16) {
         if (GU && np2_ok) launch_fp8_decode_cfg<STAGE, 2, 2, 4, 2>(g, s);
         else if (!GU && np2_ok) launch_fp8_decode_cfg<STAGE, 2, 2, 2, 2>(g, s);
@@ -553,6 +591,162 @@ static void launch_fp8_prefill_s(const Fp8GemmArgs& g, int ksplit, hipStream_t s
         case F8_T256: launch_fp8_prefill_cfg<STAGE, 4, 4, 64, 2>(g, ksplit, s); break;
         default: launch_fp8_prefill_cfg<STAGE, 4, 2, 64, 2>(g, ksplit, s); break;
     }
+}
+
+// ---------------------------------------------------------------------------
+// DOWN of one token with the top-k weighted sum folded in (the E4M3 twin of
+// the int8 / int4 one-token kernel).  Slot b is block b of the sorted order:
+// its expert's weights start streaming at once, while one wave reads which
+// pairs sit in which block (one_token.hpp); the real H code rows are then
+// staged in LDS, and one workgroup per 16 output columns streams the 16-row
+// tile of every used slot, NW waves splitting the 2 KiB chunks (wave w takes
+// chunks w, w + NW, ...), DEPTH chunks per slot in flight.  B column c of slot
+// b carries the block's c-th real row, so a pair's product is one column of
+// its slot's result; the waves' partial sums of those columns are added in
+// LDS in wave order, scaled as the DOWN epilogue scales a routed row (a2, the
+// column's weight scale, the pair's routed weight) and summed over the pairs
+// in slot order, written as one output row in the activation type: no
+// per-pair fp32 rows, no combine launch.  A pair missing from the sorted
+// order, or one whose block names no valid expert, adds nothing.
+// ---------------------------------------------------------------------------
+template <bool BF16, int TK, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void fp8_down_combine_kernel(Fp8GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ OneTokenPlan<TK> pl;
+    __shared__ f32x4 red[NW][TK][TK][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tile = blockIdx.x;
+    const int K = g.k_in;
+    const int C = K / FP8_KCHUNK;
+
+    int eb[TK];
+    one_token_experts<TK>(g.expert_ids, g.cap, g.block_size, g.E, eb);
+    const size_t expert_bytes = (size_t)g.n_out * K;
+    const uint8_t* wt[TK];
+#pragma unroll
+    for (int b = 0; b < TK; ++b)
+        wt[b] = g.w + (size_t)eb[b] * expert_bytes + (size_t)tile * C * FP8_CHUNK_BYTES + lane * 16;
+
+    const int nw = wave < C ? (C - 1 - wave) / NW + 1 : 0;
+    const int clast = wave < C ? wave + (nw - 1) * NW : C - 1;
+    u32x8 wv[DEPTH][TK];
+    auto wload = [&](int i, int slot) {
+        const size_t off = (size_t)min(wave + NW * i, clast) * FP8_CHUNK_BYTES;
+#pragma unroll
+        for (int b = 0; b < TK; ++b) wv[slot][b] = cat8(ldg128_stream(wt[b] + off), ldg128_stream(wt[b] + off + 1024));
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) wload(d, d);
+
+    if (wave == 0) one_token_plan<TK>(pl, g.sorted, g.expert_ids, g.ntpp, g.cap, g.block_size, g.E, lane);
+    __syncthreads();
+    // every slot's weights stream (an unused one, left when a top-k names an
+    // expert twice, reads a clamped expert's and is not multiplied)
+    bool used[TK];
+#pragma unroll
+    for (int b = 0; b < TK; ++b) used[b] = __builtin_amdgcn_readfirstlane(pl.cnt[b]) > 0;
+
+    // stage the real H code rows (rows past them read as code 0)
+    const int xrow_b = K + 16;
+    const int kp = K / 16;  // 16-byte pieces per row
+    for (int q = tid; q < TK * kp; q += NW * 64) {
+        const int r = q / kp, pc = q - r * kp;
+        const int p = pl.pos[r];
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (p >= 0) v = ldg128(g.a + (size_t)p * K + 16 * pc);
+        *reinterpret_cast<u32x4*>(lds + (size_t)r * xrow_b + 16 * pc) = v;
+    }
+    const uint8_t* xr[TK];  // this lane's B row of each slot
+#pragma unroll
+    for (int b = 0; b < TK; ++b)
+        xr[b] = lds + (size_t)(pl.row0[b] + min(lane & 15, max(pl.cnt[b], 1) - 1)) * xrow_b + 32 * (lane >> 4);
+    __syncthreads();
+
+    f32x4 acc[TK];
+#pragma unroll
+    for (int b = 0; b < TK; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto body = [&](int i, auto U) {
+        constexpr int u = decltype(U)::value;
+        const int c = min(wave + NW * i, clast);
+#pragma unroll
+        for (int b = 0; b < TK; ++b) {
+            if (!used[b]) continue;
+            const uint8_t* xc = xr[b] + (size_t)c * FP8_KCHUNK;
+            const u32x8 bv = cat8(*reinterpret_cast<const u32x4*>(xc), *reinterpret_cast<const u32x4*>(xc + 16));
+            acc[b] = mfma_e4m3(wv[u][b], bv, acc[b]);
+        }
+        wload(i + DEPTH, u);
+    };
+    int i0 = 0;
+    for (; i0 + DEPTH <= nw; i0 += DEPTH) static_for<0, DEPTH>([&](auto U) { body(i0 + decltype(U)::value, U); });
+    static_for<0, DEPTH - 1>([&](auto U) {
+        if (i0 + decltype(U)::value < nw) body(i0 + decltype(U)::value, U);
+    });
+
+    if ((lane & 15) < TK) {
+#pragma unroll
+        for (int b = 0; b < TK; ++b) red[wave][b][lane & 15][lane >> 4] = acc[b];
+    }
+    __syncthreads();
+    if (tid < 4) {
+        const int row = tile * TILE_ROWS + 4 * tid;
+        f32x4 res = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            const int b = pl.slot[j];
+            if (b < 0) continue;
+            const int c = pl.col[j];
+            f32x4 o = red[0][b][c][tid];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) o += red[w][b][c][tid];
+            const float* se = g.s + (size_t)min(max(g.expert_ids[b], 0), g.E - 1) * g.n_out + row;
+            const float rw = g.topk_w[j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = o[i] * g.in_scale * se[i] * rw;
+            res += o;
+        }
+        u32x2 st;
+        st[0] = (uint32_t)f32_to_act<BF16>(res[0]) | ((uint32_t)f32_to_act<BF16>(res[1]) << 16);
+        st[1] = (uint32_t)f32_to_act<BF16>(res[2]) | ((uint32_t)f32_to_act<BF16>(res[3]) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + row) = st;
+    }
+}
+
+static size_t fp8_down_combine_lds(int topk, int k_in) { return (size_t)topk * ((size_t)k_in + 16); }
+
+// one token, top-k up to 4, 32 or more 2 KiB chunks per tile, the H code rows in LDS
+bool fp8_down_combine_supported(int M, int topk, int n_out, int k_in) {
+    return M == 1 && topk >= 1 && topk <= 4 && k_in % FP8_KCHUNK == 0 && k_in / FP8_KCHUNK >= 32 &&
+           n_out % TILE_ROWS == 0 && fp8_down_combine_lds(topk, k_in) <= 128 * 1024;
+}
+
+template <bool BF16, int TK>
+static void launch_fp8_down_combine_tk(const Fp8GemmArgs& g, hipStream_t s) {
+    constexpr int NW = 16, DEPTH = TK <= 2 ? 3 : 2;
+    auto kern = fp8_down_combine_kernel<BF16, TK, NW, DEPTH>;
+    const size_t dyn = fp8_down_combine_lds(TK, g.k_in);
+    if (dyn > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)dyn);
+    hipLaunchKernelGGL(kern, dim3(g.n_out / TILE_ROWS), dim3(NW * 64), dyn, s, g);
+}
+
+template <bool BF16>
+static void launch_fp8_down_combine_b(const Fp8GemmArgs& g, hipStream_t s) {
+    switch (g.topk) {
+        case 1: launch_fp8_down_combine_tk<BF16, 1>(g, s); break;
+        case 2: launch_fp8_down_combine_tk<BF16, 2>(g, s); break;
+        case 3: launch_fp8_down_combine_tk<BF16, 3>(g, s); break;
+        default: launch_fp8_down_combine_tk<BF16, 4>(g, s); break;
+    }
+}
+
+void launch_fp8_down_combine(bool bf16, const Fp8GemmArgs& g, hipStream_t s) {
+    if (bf16) launch_fp8_down_combine_b<true>(g, s);
+    else launch_fp8_down_combine_b<false>(g, s);
 }
 
 int launch_gemm_fp8(int stage, const Fp8GemmArgs& g, hipStream_t s) {

@@ -28,6 +28,7 @@
 // vLLM issue 3289, the GEMV/GEMM mix).
 #include "common.hpp"
 #include "launch.hpp"
+#include "one_token.hpp"
 
 namespace wq {
 
@@ -328,27 +329,29 @@ int launch_gemm_tiny(int wbits, bool bf16, int stage, const GemmArgs& g, const i
 
 
 // ---------------------------------------------------------------------------
-// DOWN of one token with the top-k weighted sum folded in.  The token's topk
-// pairs sit at some positions of sorted_token_ids (found by one wave's scan);
-// the H rows at those positions are staged in LDS, and one workgroup per 16
-// output columns streams the 16-row weight tile of every chosen expert, NW
-// waves splitting the 1 KiB chunks (wave w takes chunks w, w + NW, ...), DEPTH
-// chunks per expert in flight.  Every MFMA B column carries the same H row, so
-// column 0 of the result is the token's: the waves' column-0 partial sums meet
-// in LDS and are added in wave order, scaled per column (int8, or int4 with
-// one scale per column), multiplied by the pair's routed weight and summed over
-// the pairs in slot order -- the output row in the activation type, with no
-// per-pair fp32 rows and no combine launch.  A pair missing from the sorted
-// order, or one whose block names no valid expert, adds nothing.
+// DOWN of one token with the top-k weighted sum folded in.  Slot b is block b
+// of the sorted order (at most top-k blocks are used): the weights of its
+// expert start streaming at once, while one wave reads which pairs sit in
+// which block (one_token.hpp); the real H rows are then staged in LDS, and one
+// workgroup per 16 output columns streams the 16-row weight tile of every
+// used slot, NW waves splitting the 1 KiB chunks (wave w takes chunks w, w +
+// NW, ...), DEPTH chunks per slot in flight.  B column c of slot b carries the
+// block's c-th real row (its last one for the other columns), so a pair's
+// product is one column of its slot's result.  The waves' partial sums of the
+// pairs' columns meet in LDS and are added in wave order, scaled per column
+// (int8, or int4 with one scale per column), multiplied by the pair's routed
+// weight and summed over the pairs in slot order -- the output row in the
+// activation type, with no per-pair fp32 rows and no combine launch.  A pair
+// missing from the sorted order, or one whose block names no valid expert,
+// adds nothing.
 // ---------------------------------------------------------------------------
 template <int WBITS, bool BF16, int TK, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void tiny_down_combine_kernel(GemmArgs g, uint16_t* __restrict__ out) {
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     constexpr int KSTEPS = KCHUNK / 32;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ int spos[TK];
-    __shared__ int sexp[TK];
-    __shared__ f32x4 red[NW][TK][4];
+    __shared__ OneTokenPlan<TK> pl;
+    __shared__ f32x4 red[NW][TK][TK][4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -356,43 +359,16 @@ __global__ __launch_bounds__(NW * 64) void tiny_down_combine_kernel(GemmArgs g, 
     const int tile = blockIdx.x;
     const int K = g.k_in;
     const int C = K / KCHUNK;
-    const int BS = g.block_size;
 
-    if (wave == 0) {
-        // positions of pairs 0 .. TK - 1 (the token's slots) in the sorted order
-        const int ntpp = min(*g.ntpp, g.cap);
-        int pos[TK];
-#pragma unroll
-        for (int j = 0; j < TK; ++j) pos[j] = -1;
-        for (int base = 0; base < ntpp; base += 64) {
-            const int p = base + lane;
-            const int v = p < ntpp ? g.sorted[p] : -1;
-#pragma unroll
-            for (int j = 0; j < TK; ++j) {
-                const uint64_t hit = __ballot(v == j);
-                if (hit != 0 && pos[j] < 0) pos[j] = base + __builtin_ctzll(hit);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < TK; ++j) {
-            if (lane == j) {
-                const int e = pos[j] >= 0 ? g.expert_ids[pos[j] / BS] : -1;
-                const bool ok = e >= 0 && e < g.E;
-                spos[j] = ok ? pos[j] : -1;
-                sexp[j] = ok ? e : 0;
-            }
-        }
-    }
-    __syncthreads();
-
+    int eb[TK];
+    one_token_experts<TK>(g.expert_ids, g.cap, g.block_size, g.E, eb);
     const size_t expert_bytes = (size_t)(g.n_out / TILE_ROWS) * C * CHUNK_BYTES;
     const uint8_t* wt[TK];
     const uint16_t* se[TK];
 #pragma unroll
-    for (int j = 0; j < TK; ++j) {
-        const int e = sexp[j];
-        wt[j] = g.w + (size_t)e * expert_bytes + (size_t)tile * C * CHUNK_BYTES + lane * 16;
-        se[j] = g.s + (size_t)e * g.groups * g.n_out;
+    for (int b = 0; b < TK; ++b) {
+        wt[b] = g.w + (size_t)eb[b] * expert_bytes + (size_t)tile * C * CHUNK_BYTES + lane * 16;
+        se[b] = g.s + (size_t)eb[b] * g.groups * g.n_out;
     }
     const bool grouped = (WBITS == 4) && g.groups > 1;
     const int rowq = 4 * (lane >> 4);
@@ -405,58 +381,72 @@ __global__ __launch_bounds__(NW * 64) void tiny_down_combine_kernel(GemmArgs g, 
     auto wload = [&](int i, int slot) {
         const int c = min(wave + NW * i, clast);
 #pragma unroll
-        for (int j = 0; j < TK; ++j) wv[slot][j] = ldg128_stream(wt[j] + (size_t)c * CHUNK_BYTES);
+        for (int b = 0; b < TK; ++b) wv[slot][b] = ldg128_stream(wt[b] + (size_t)c * CHUNK_BYTES);
         if constexpr (WBITS == 4) {
             const size_t gc = grouped ? (size_t)c : 0;  // per-column scales: a harmless reread of group 0
 #pragma unroll
-            for (int j = 0; j < TK; ++j)
-                sv[slot][j] = *reinterpret_cast<const u32x2*>(se[j] + gc * g.n_out + tile * TILE_ROWS + rowq);
+            for (int b = 0; b < TK; ++b)
+                sv[slot][b] = *reinterpret_cast<const u32x2*>(se[b] + gc * g.n_out + tile * TILE_ROWS + rowq);
         }
     };
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) wload(d, d);
 
-    // stage the TK H rows (a missing pair's row reads as zeros)
+    if (wave == 0) one_token_plan<TK>(pl, g.sorted, g.expert_ids, g.ntpp, g.cap, g.block_size, g.E, lane);
+    __syncthreads();
+    // every slot's weights stream (an unused one, left when a top-k names an
+    // expert twice, reads a clamped expert's and is not multiplied)
+    bool used[TK];
+#pragma unroll
+    for (int b = 0; b < TK; ++b) used[b] = __builtin_amdgcn_readfirstlane(pl.cnt[b]) > 0;
+
+    // stage the real H rows (rows past them read as zeros)
     const int xrow_b = 2 * K + 16;
     const int kp = K / 8;  // 16-byte pieces per row
     for (int q = tid; q < TK * kp; q += NW * 64) {
-        const int j = q / kp, pc = q - j * kp;
-        const int p = spos[j];
+        const int r = q / kp, pc = q - r * kp;
+        const int p = pl.pos[r];
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (p >= 0) v = ldg128(g.a + (size_t)p * K + 8 * pc);
-        *reinterpret_cast<u32x4*>(lds + (size_t)j * xrow_b + 16 * pc) = v;
+        *reinterpret_cast<u32x4*>(lds + (size_t)r * xrow_b + 16 * pc) = v;
     }
+    const uint8_t* xr[TK];  // this lane's B row of each slot
+#pragma unroll
+    for (int b = 0; b < TK; ++b)
+        xr[b] = lds + (size_t)(pl.row0[b] + min(lane & 15, max(pl.cnt[b], 1) - 1)) * xrow_b + 16 * (lane >> 4);
     __syncthreads();
 
     f32x4 acc[TK];
 #pragma unroll
-    for (int j = 0; j < TK; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TK; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto body = [&](int i, auto U) {
         constexpr int u = decltype(U)::value;
         const int c = min(wave + NW * i, clast);
 #pragma unroll
-        for (int j = 0; j < TK; ++j) {
-            const uint8_t* xc = lds + (size_t)j * xrow_b + (size_t)c * (2 * KCHUNK) + 16 * (lane >> 4);
-            u32x4 b[KSTEPS];
+        for (int b = 0; b < TK; ++b) {
+            if (!used[b]) continue;
+            const uint8_t* xc = xr[b] + (size_t)c * (2 * KCHUNK);
+            u32x4 bv[KSTEPS];
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) b[ks] = *reinterpret_cast<const u32x4*>(xc + 64 * ks);
+            for (int ks = 0; ks < KSTEPS; ++ks) bv[ks] = *reinterpret_cast<const u32x4*>(xc + 64 * ks);
             if constexpr (WBITS == 4) {
                 f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) part = mfma16x16x32<false>(dequant_w4_f16(wv[u][j][ks]), b[ks], part);
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    part = mfma16x16x32<false>(dequant_w4_f16(wv[u][b][ks]), bv[ks], part);
                 if (grouped) {
-                    acc[j][0] += part[0] * f16_to_f32((uint16_t)(sv[u][j][0] & 0xffffu));
-                    acc[j][1] += part[1] * f16_to_f32((uint16_t)(sv[u][j][0] >> 16));
-                    acc[j][2] += part[2] * f16_to_f32((uint16_t)(sv[u][j][1] & 0xffffu));
-                    acc[j][3] += part[3] * f16_to_f32((uint16_t)(sv[u][j][1] >> 16));
+                    acc[b][0] += part[0] * f16_to_f32((uint16_t)(sv[u][b][0] & 0xffffu));
+                    acc[b][1] += part[1] * f16_to_f32((uint16_t)(sv[u][b][0] >> 16));
+                    acc[b][2] += part[2] * f16_to_f32((uint16_t)(sv[u][b][1] & 0xffffu));
+                    acc[b][3] += part[3] * f16_to_f32((uint16_t)(sv[u][b][1] >> 16));
                 } else {
-                    acc[j] += part;
+                    acc[b] += part;
                 }
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks)
-                    acc[j] = mfma16x16x32<BF16>(dequant_w8x8<BF16>(wv[u][j][2 * ks], wv[u][j][2 * ks + 1]), b[ks],
-                                                acc[j]);
+                    acc[b] = mfma16x16x32<BF16>(dequant_w8x8<BF16>(wv[u][b][2 * ks], wv[u][b][2 * ks + 1]), bv[ks],
+                                                acc[b]);
             }
         }
         wload(i + DEPTH, u);
@@ -467,9 +457,9 @@ __global__ __launch_bounds__(NW * 64) void tiny_down_combine_kernel(GemmArgs g, 
         if (i0 + decltype(U)::value < nw) body(i0 + decltype(U)::value, U);
     });
 
-    if ((lane & 15) == 0) {
+    if ((lane & 15) < TK) {
 #pragma unroll
-        for (int j = 0; j < TK; ++j) red[wave][j][lane >> 4] = acc[j];
+        for (int b = 0; b < TK; ++b) red[wave][b][lane & 15][lane >> 4] = acc[b];
     }
     __syncthreads();
     if (tid < 4) {
@@ -477,13 +467,16 @@ __global__ __launch_bounds__(NW * 64) void tiny_down_combine_kernel(GemmArgs g, 
         f32x4 res = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < TK; ++j) {
-            if (spos[j] < 0) continue;
-            f32x4 o = red[0][j][tid];
+            const int b = pl.slot[j];
+            if (b < 0) continue;
+            const int c = pl.col[j];
+            f32x4 o = red[0][b][c][tid];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) o += red[w][j][tid];
+            for (int w = 1; w < NW; ++w) o += red[w][b][c][tid];
             if (!grouped) {
+                const uint16_t* sb = g.s + (size_t)min(max(g.expert_ids[b], 0), g.E - 1) * g.groups * g.n_out;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] *= act_to_f32<BF16>(se[j][row + i]);
+                for (int i = 0; i < 4; ++i) o[i] *= act_to_f32<BF16>(sb[row + i]);
             }
             res += o * g.topk_w[j];
         }
@@ -506,7 +499,7 @@ bool tiny_down_combine_supported(int wbits, int M, int topk, int n_out, int k_in
 
 template <int WBITS, bool BF16, int TK>
 static void launch_down_combine_tk(const GemmArgs& g, uint16_t* out, hipStream_t s) {
-    constexpr int NW = 16, DEPTH = 3;
+    constexpr int NW = 16, DEPTH = (WBITS == 4 && TK == 4) ? 2 : 3;  // int4 top-4: 3 deep exceeds 128 VGPRs
     auto kern = tiny_down_combine_kernel<WBITS, BF16, TK, NW, DEPTH>;
     const size_t dyn = down_combine_lds(TK, g.k_in);
     if (dyn > 64 * 1024)

@@ -72,8 +72,14 @@ struct Fp8GemmArgs {
     int cap;
     float in_scale;           // scale of the A operand's codes (a1 for x, a2 for H)
     float out_scale;          // GATE_UP: scale H is quantised with (a2)
+    const uint16_t* x16;      // GATE_UP of one token: its 16-bit row, quantised in the kernel (a unused); else null
+    int x_bf16;               // x16's type: 1 bf16, 0 fp16
 };
 
+// GATE_UP of one token on the small-batch kernel: x quantised inside the GEMM
+// (its codes in LDS, k_in bytes), no quantisation launch
+constexpr int FP8_FOLD_MAX_K = 32768;
+bool fp8_fold_quant_supported(int stage, int M, int n_out, int k_in, int block_size);
 // q[r, k] = E4M3 code of x[r, k] / scale (float32 division, clamped to +-448, nearest even)
 void launch_fp8_quant(const uint16_t* x, int64_t rows, int k, bool bf16, float scale, uint8_t* q, hipStream_t s);
 // grouped E4M3 GEMM, small-batch (weights streamed once per pass of token blocks) or
@@ -81,6 +87,10 @@ void launch_fp8_quant(const uint16_t* x, int64_t rows, int k, bool bf16, float s
 bool fp8_prefill_supported(int n_out, int k_in, int block_size);
 int fp8_down_split(int T, int E, int n_out, int k_in, int block_size);
 int launch_gemm_fp8(int stage, const Fp8GemmArgs& g, hipStream_t s);
+// DOWN of one token with the top-k sum folded in: g.out is the [1, n_out]
+// output row in the activation type, no fp32 rows and no combine launch
+bool fp8_down_combine_supported(int M, int topk, int n_out, int k_in);
+void launch_fp8_down_combine(bool bf16, const Fp8GemmArgs& g, hipStream_t s);
 
 // small-batch path: one workgroup per (expert, 16 or 32 weight rows), split-K
 // across its waves, all of the expert's 16-row token blocks per pass
