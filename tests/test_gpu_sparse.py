@@ -197,3 +197,25 @@ def test_sparse_matches_dense_with_zeros_on_gpu():
     torch.cuda.synchronize()
     dense_y = out.cpu().numpy().astype(np.float64)
     assert_close_fp(y_sp, dense_y, "2:4 vs dense-with-zeros")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K", [256, 768])
+def test_sparse_exact_integer_large_batch(bits, K):
+    """The large-batch kernel (M > 128, N a multiple of 256) bit for bit on an
+    exact-integer case: one 256-channel chunk, and three (an odd count, so the
+    chunk loop ends on its first register slot), with a ragged last token tile."""
+    need_gpu()
+    spec = gen.CFG4.with_(K=K, N=256, bits=bits)
+    sw = gen.make_sparse_weights(spec, seed_config=330 + bits)
+    rng = np.random.default_rng(K + bits)
+    M = 150
+    density = 1 / 4 if bits == 4 else 1 / 16  # every sum stays an integer below 2048 (exact in fp16)
+    x = rng.integers(-1, 2, size=(M, spec.K)).astype(np.float32) * (rng.random((M, spec.K)) < density)
+    ones = np.ones((spec.K // 128, spec.N), np.float32)
+    sw.s = gen.round_to("f16", ones)
+    say("sparse large-batch exact", bits, K)
+    y = run_sparse(sw, gen.round_to("f16", x), spec.N, bits=bits)
+    ref = oracle.sparse24(x, sw.vals, sw.idx, ones, 128)
+    assert np.abs(ref).max() < 2048
+    assert np.array_equal(y.astype(np.float64), ref)

@@ -12,7 +12,7 @@
 // metadata decode is a register move: two instructions share one index dword
 // through ABID 0/1.
 //
-// Two kernels:
+// Kernels:
 //  - small and medium batches (M <= 128): one workgroup per 128 (16 tokens)
 //    or 256 output rows (32 or 64 tokens), one 16-row tile per wave; all
 //    waves walk the same 256-channel chunks, whose token tile is staged once
@@ -21,7 +21,10 @@
 //  - large batches: one workgroup per 256 output rows and 64 tokens; the token
 //    tile of each chunk is staged once in LDS and shared by the 4 waves, each
 //    of which multiplies its own 64 weight rows, read straight from the packed
-//    layout into registers one chunk ahead.
+//    layout into registers one chunk ahead -- for 4-bit codes the pipelined
+//    form (sparse24_pipe_kernel: half-chunk LDS double buffer, one barrier per
+//    half chunk, conversions and operand reads overlapped with the MFMAs),
+//    for 8-bit codes the plain one (sparse24_tile_kernel).
 // Token rows are 512-byte LDS rows of 16-byte pieces stored at
 // piece ^ (row & 15), so the B-operand reads of 16 rows hit distinct banks.
 // Weights are scaled in fp16 (q * s rounded once) before the multiply.
@@ -400,6 +403,191 @@ __global__ __launch_bounds__(SP_THREADS, OCC) void sparse24_tile_kernel(const ui
     }
 }
 
+// ------------------------------------------------ large batches, pipelined
+// One workgroup of NW waves: NW * RT 16-row weight tiles x 16 * TJ tokens;
+// wave w owns RT weight tiles and all the token tiles.  The K loop runs in
+// half chunks of 128 dense channels (two smfmac steps):
+//  - the token rows of a half chunk go to one of two LDS buffers (256-byte
+//    rows of 16-byte pieces at piece ^ (row & 15)) while the other is
+//    multiplied: one barrier per half chunk;
+//  - a wave's weights (kept codes, index metadata, the two group scales of
+//    the chunk) come straight from the packed layout into registers, one
+//    chunk ahead (two register slots), and the A operands of the next step
+//    are dequantised between the MFMAs of the current one;
+//  - the B operands of token tile j + 1 are read from LDS before the MFMAs of
+//    tile j are issued.
+// Token tiles wholly past M skip their MFMAs (one uniform branch per tile);
+// rows past M inside a tile read row M - 1 and are not stored.
+constexpr int SPP_HROWB = 256;  // LDS bytes of one token row per half chunk
+#ifndef SPP_BA
+#define SPP_BA 2  // token tiles of B operands read ahead
+#endif
+
+template <int VBITS, int NW, int RT, int TJ, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void sparse24_pipe_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                     int N, const uint8_t* __restrict__ vals,
+                                                                     const uint8_t* __restrict__ meta,
+                                                                     const uint16_t* __restrict__ scales,
+                                                                     int sstride, uint16_t* __restrict__ y) {
+    constexpr int NT = NW * 64;
+    constexpr int BM = 16 * TJ;
+    constexpr int BUF = BM * SPP_HROWB;
+    constexpr int TPIECES = BM * 16 / NT;  // 16-byte token pieces per thread and half chunk
+    static_assert(TPIECES >= 1 && (BM * 16) % NT == 0, "token staging");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nrow = lane & 15, g4 = lane >> 4;
+    const int m0 = blockIdx.y * BM;
+    const int t0 = ((int)blockIdx.x * NW + __builtin_amdgcn_readfirstlane(wave)) * RT;
+    const int C = K / SP_KCHUNK;
+    const int HC = 2 * C;
+    const int jact = min(TJ, (M - m0 + 15) / 16);  // token tiles holding a row below M
+
+    // ------------------------------------------------------------- loaders
+    const size_t tstride = (size_t)C * sp_chunk_bytes<VBITS>();
+    const uint8_t* vt = vals + (size_t)t0 * tstride + lane * sp_lane_bytes<VBITS>();
+    const uint8_t* mt = meta + (size_t)t0 * C * 512 + lane * 8;
+    const uint16_t* sn = scales + 16 * t0 + nrow;
+    SpVals<VBITS> wv[2][RT];
+    u32x2 wm[2][RT];
+    uint32_t ws[2][RT];  // scales of groups 2c (low half) and 2c + 1 (high half) of this lane's row
+    auto wload = [&](int c, auto SL) {
+        constexpr int sl = decltype(SL)::value;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            wv[sl][t] = sp_load<VBITS>(vt + t * tstride + (size_t)c * sp_chunk_bytes<VBITS>());
+            wm[sl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(mt + ((size_t)t * C + c) * 512));
+            ws[sl][t] = (uint32_t)sn[16 * t + (size_t)(2 * c) * sstride] |
+                        ((uint32_t)sn[16 * t + (size_t)(2 * c + 1) * sstride] << 16);
+        }
+    };
+    const uint16_t* xp[TPIECES];
+#pragma unroll
+    for (int i = 0; i < TPIECES; ++i) {
+        const int id = tid + NT * i;
+        xp[i] = x + (size_t)min(m0 + (id >> 4), M - 1) * K + (id & 15) * 8;
+    }
+    u32x4 tv[TPIECES];
+    auto tload = [&](int hc) {
+#pragma unroll
+        for (int i = 0; i < TPIECES; ++i) tv[i] = ldg128(xp[i] + (size_t)hc * 128);
+    };
+    auto tstore = [&](uint8_t* buf) {
+#pragma unroll
+        for (int i = 0; i < TPIECES; ++i) {
+            const int id = tid + NT * i;
+            const int row = id >> 4, pc = id & 15;
+            *reinterpret_cast<u32x4*>(buf + row * SPP_HROWB + ((pc ^ (row & 15)) << 4)) = tv[i];
+        }
+    };
+
+    // --------------------------------------------------------- multipliers
+    f32x4 acc[RT][TJ];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A operands of step S (0..3 within the chunk) of tile t from slot SL
+    auto deq = [&](u32x4 (&an)[RT], auto SL, auto ST, auto TT) {
+        constexpr int sl = decltype(SL)::value, st = decltype(ST)::value, t = decltype(TT)::value;
+        const uint32_t sv = st < 2 ? (ws[sl][t] & 0xffffu) : (ws[sl][t] >> 16);
+        an[t] = sp_dequant<VBITS, st>(wv[sl][t], sv);
+        asm volatile("" : "+v"(an[t]));  // keep the conversion here, between this step's MFMAs
+    };
+    // B operands of token tile j for step S (its 64 channels are pieces 8 (S & 1) .. + 8 of the half row)
+    auto bread = [&](int j, const uint8_t* cur, auto ST, u32x8& b) {
+        constexpr int sh = decltype(ST)::value & 1;
+        const int r = 16 * j + nrow;
+        const int plo = 8 * sh + g4, phi = plo + 4;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(cur + r * SPP_HROWB + ((plo ^ nrow) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(cur + r * SPP_HROWB + ((phi ^ nrow) << 4));
+        b = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    // index metadata of step ST from slot SL
+    auto midx = [&](int (&idx)[RT], auto SL, auto ST) {
+        constexpr int sl = decltype(SL)::value, st = decltype(ST)::value;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) idx[t] = (int)wm[sl][t][st >> 1];
+    };
+    // one smfmac step: MFMAs of step ST with `a` and `idx`; the RT conversions
+    // of `next` spread over the token tiles
+    auto step = [&](const uint8_t* cur, auto ST, const u32x4 (&a)[RT], const int (&idx)[RT], auto&& next) {
+        constexpr int st = decltype(ST)::value;
+        // B operands of token tile j + BA are read before tile j's MFMAs (a
+        // tile's RT MFMAs alone are too short to cover one LDS read)
+        constexpr int BA = SPP_BA < TJ ? SPP_BA : TJ;
+        u32x8 bq[BA + 1];
+        static_for<0, BA>([&](auto J) { bread(decltype(J)::value, cur, ST, bq[decltype(J)::value]); });
+        static_for<0, TJ>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if constexpr (j + BA < TJ) bread(j + BA, cur, ST, bq[(j + BA) % (BA + 1)]);
+            if (j == 0 || j < jact) {
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+                    acc[t][j] = smfmac16x16x64<st & 1>(a[t], bq[j % (BA + 1)], idx[t], acc[t][j]);
+            }
+            static_for<j * RT / TJ, (j + 1) * RT / TJ>([&](auto TT) { next(TT); });
+        });
+    };
+    uint8_t* b0 = lds;
+    uint8_t* b1 = lds + BUF;
+    u32x4 aA[RT], aB[RT];
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // chunk c from slot SL: halves 0 (buffer b0) and 1 (buffer b1); the last
+    // step converts step 0 of chunk c + 1 (slot 1 - SL, loaded one chunk ago)
+    // and, once slot SL is dead, loads chunk c + 2 into it
+    auto chunk = [&](int c, auto SL) {
+        constexpr int sl = decltype(SL)::value;
+        using SN = std::integral_constant<int, 1 - sl>;
+        int ia[RT], ib[RT];
+        tstore(b1);
+        tload(min(2 * c + 2, HC - 1));
+        midx(ia, SL, I0{});
+        step(b0, I0{}, aA, ia, [&](auto TT) { deq(aB, SL, I1{}, TT); });
+        step(b0, I1{}, aB, ia, [&](auto TT) { deq(aA, SL, I2{}, TT); });
+        __syncthreads();
+        tstore(b0);
+        tload(min(2 * c + 3, HC - 1));
+        midx(ib, SL, I2{});
+        step(b1, I2{}, aA, ib, [&](auto TT) { deq(aB, SL, I3{}, TT); });
+        // slot SL is dead once step 3's operands are converted and its
+        // metadata is in `ib`: chunk c + 2 goes into it
+        wload(min(c + 2, C - 1), SL);
+        step(b1, I3{}, aB, ib, [&](auto TT) { deq(aA, SN{}, I0{}, TT); });
+        __syncthreads();
+    };
+    wload(0, I0{});
+    tload(0);
+    tstore(b0);
+    tload(1);
+    wload(min(1, C - 1), I1{});
+    static_for<0, RT>([&](auto TT) { deq(aA, I0{}, I0{}, TT); });
+    __syncthreads();
+    for (int c = 0; c < C; c += 2) {
+        chunk(c, I0{});
+        if (c + 1 < C) chunk(c + 1, I1{});
+    }
+
+    // D[row 4 g4 + r][col nrow]: rows are weight rows, columns tokens
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int m = m0 + 16 * j + nrow;
+        if (m < M) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                u32x2 stv;
+                stv[0] = (uint32_t)f32_to_f16(acc[t][j][0]) | ((uint32_t)f32_to_f16(acc[t][j][1]) << 16);
+                stv[1] = (uint32_t)f32_to_f16(acc[t][j][2]) | ((uint32_t)f32_to_f16(acc[t][j][3]) << 16);
+                *reinterpret_cast<u32x2*>(y + (size_t)m * N + 16 * (t0 + t) + 4 * g4) = stv;
+            }
+        }
+    }
+}
+
 // Workgroup shape: every workgroup stages its token rows once per chunk, so
 // the token traffic from L2 falls as a workgroup covers more weight rows;
 // measured at K = 7168, N = 20480 (4-bit / 8-bit codes): 16 tokens on 8
@@ -427,6 +615,29 @@ static void launch_decode(const uint16_t* x, int M, int K, int N, const uint8_t*
                        scales, sstride, y);
 }
 
+// the pipelined kernel's shape, measured at M = 1024, K = 7168, N = 20480 with
+// 4-bit codes: 4 waves x 4 weight tiles x 4 token tiles, 2 per CU, 232-235 us
+// (the 256 x 64 tile kernel: 243 us); 512 x 64 (8 waves) 256 us, 256 x 128
+// (2 weight tiles per wave) 252 us, 128 x 128 (4 waves) 262 us, 128 x 64 at 3
+// per CU 277 us; B operands read 1-4 token tiles ahead: equal.  8-bit codes
+// take the tile kernel: two chunks of their 32-byte pieces exceed the 256
+// registers of two waves per SIMD (445 against 354 us)
+#ifndef SPP_NW
+#define SPP_NW 4
+#define SPP_RT 4
+#define SPP_TJ 4
+#define SPP_OCC 2
+#endif
+constexpr int SPP_BN = 16 * SPP_NW * SPP_RT;
+
+template <int VBITS, int NW, int RT, int TJ, int OCC>
+static void launch_pipe(const uint16_t* x, int M, int K, int N, const uint8_t* vals, const uint8_t* meta,
+                        const uint16_t* scales, int sstride, uint16_t* y, hipStream_t s) {
+    const dim3 grid(N / (16 * NW * RT), (M + 16 * TJ - 1) / (16 * TJ));
+    hipLaunchKernelGGL((sparse24_pipe_kernel<VBITS, NW, RT, TJ, OCC>), grid, dim3(NW * 64), 0, s, x, M, K, N, vals,
+                       meta, scales, sstride, y);
+}
+
 // batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480:
 // M = 1, 2: 18 -> 13 us; M = 4: 18.6 -> 17.0 us with the decode kernel
 template <int VBITS>
@@ -435,6 +646,8 @@ static void launch_sparse24_b(const uint16_t* x, int M, int K, int N, const uint
     if (M <= 4 && sparse24_decode_lds(M, K) <= SP_DECODE_LDS_MAX) {
         if (M <= 2) launch_decode<VBITS, 2, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
         else launch_decode<VBITS, 4, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
+    } else if (M > 128 && VBITS == 4 && N % SPP_BN == 0) {
+        launch_pipe<VBITS, SPP_NW, SPP_RT, SPP_TJ, SPP_OCC>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else if (M > 128 && N % SPT_BN == 0) {
         const dim3 grid(N / SPT_BN, (M + SPT_BM - 1) / SPT_BM);
         hipLaunchKernelGGL((sparse24_tile_kernel<VBITS, 2>), grid, dim3(SP_THREADS), 0, s, x, M, K, N, vals, meta,
