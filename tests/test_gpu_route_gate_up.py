@@ -1,7 +1,8 @@
 """GPU parity of moe_route_gate_up, the call that routes, sorts and runs the
 GATE_UP stage: for up to 16 pairs over up to 64 experts (blocks of 16 or 32,
 no act-order) one kernel whose every workgroup routes and sorts the batch
-itself, otherwise the separate launches.  Its outputs -- routing weights and
+itself; with act-order (up to 16 tokens, 64 pairs, 64 experts) a routing
+launch that also gathers the permuted rows; otherwise the separate launches.  Its outputs -- routing weights and
 ids, sorted_token_ids, expert_ids, num_tokens_post_padded and every H row up
 to the padded total -- equal those of moe_route_align followed by the GEMM's
 GATE_UP call bit for bit (int8 bf16 and fp16, int4 group-128 and per-column,
@@ -23,6 +24,9 @@ SPECS = {
     "w4pc": gen.CFG3.with_(name="rgu-w4pc", E=8, topk=2, K=256, N=512, act_order=False, group_size=-1),
     "w8e64": gen.CFG2.with_(name="rgu-w8e64", E=64, topk=4, K=256, N=256),
     "w8e5": gen.CFG2.with_(name="rgu-w8e5", E=5, topk=3, K=256, N=256),
+    # act-order int4: the routing launch also gathers the permuted rows
+    "w4ao": gen.CFG3.with_(name="rgu-w4ao", E=8, topk=2, K=256, N=512, act_order=True),
+    "w4aoe64": gen.CFG3.with_(name="rgu-w4aoe64", E=64, topk=4, K=384, N=256, act_order=True),
 }
 _cache = {}
 
@@ -58,7 +62,8 @@ def run_pair(key, M, bs, renorm, ties=False):
     lg = torch.from_numpy(logits).cuda()
     cap = wq.moe_align_capacity(M, spec.topk, spec.E, bs)
     gs = spec.group_size if spec.bits == 4 else -1
-    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, M, spec.topk, spec.E, 2 * spec.N, spec.K, cap, False)
+    ws = wq.moe_gemm_workspace_bytes(wq.WQ_STAGE_GATE_UP, M, spec.topk, spec.E, 2 * spec.N, spec.K, cap,
+                                     p.k_perm1 is not None)
     work = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
     a = buffers(M, spec.topk, spec.E, cap, bs, spec.N, p.act)
     b = buffers(M, spec.topk, spec.E, cap, bs, spec.N, p.act)
@@ -66,14 +71,14 @@ def run_pair(key, M, bs, renorm, ties=False):
     # the two separate calls
     wq.moe_route_align(lg, spec.topk, renorm, bs, a["w"], a["ids"], a["st"], a["ex"], a["nt"], cap)
     if spec.bits == 4:
-        wq.moe_w4a16_gemm(wq.WQ_STAGE_GATE_UP, x, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1, p.s1, gs, None,
-                          a["st"], a["ex"], a["nt"], cap, bs, None, a["h"], work, None, p.act_code)
+        wq.moe_w4a16_gemm(wq.WQ_STAGE_GATE_UP, x, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1, p.s1, gs,
+                          p.k_perm1, a["st"], a["ex"], a["nt"], cap, bs, None, a["h"], work, None, p.act_code)
     else:
         wq.moe_w8a16_gemm(wq.WQ_STAGE_GATE_UP, x, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1, p.s1, a["st"],
                           a["ex"], a["nt"], cap, bs, None, a["h"], work, None, p.act_code)
     # the one call
     wq.moe_route_gate_up(spec.bits, lg, renorm, b["w"], b["ids"], x, M, spec.topk, spec.E, 2 * spec.N, spec.K, p.w1,
-                         p.s1, gs, None, b["st"], b["ex"], b["nt"], cap, bs, b["h"], work, None, p.act_code)
+                         p.s1, gs, p.k_perm1, b["st"], b["ex"], b["nt"], cap, bs, b["h"], work, None, p.act_code)
     torch.cuda.synchronize()
     nt = int(a["nt"][0])
     assert int(b["nt"][0]) == nt
@@ -85,7 +90,7 @@ def run_pair(key, M, bs, renorm, ties=False):
     return nt
 
 
-@pytest.mark.parametrize("key", ["w8bf", "w8f16", "w4g", "w4pc"])
+@pytest.mark.parametrize("key", ["w8bf", "w8f16", "w4g", "w4pc", "w4ao"])
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("bs", [16, 32])
 def test_route_gate_up_equals_two_calls(key, M, bs):
@@ -100,10 +105,14 @@ def test_route_gate_up_softmax_modes_and_ties(key, M, renorm):
     run_pair(key, M, 16, renorm=renorm, ties=True)
 
 
-@pytest.mark.parametrize("key,M,bs", [("w8bf", 9, 16), ("w8bf", 32, 16), ("w4g", 2, 64), ("w8e64", 5, 16)])
+@pytest.mark.parametrize("key,M,bs", [("w8bf", 9, 16), ("w8bf", 32, 16), ("w4g", 2, 64), ("w8e64", 5, 16),
+                                      ("w4ao", 16, 16), ("w4ao", 2, 128), ("w4ao", 17, 16), ("w4aoe64", 16, 16),
+                                      ("w4aoe64", 3, 32)])
 def test_route_gate_up_past_the_one_kernel_limits(key, M, bs):
     """More than 16 pairs, blocks of 64, or 20 pairs over 64 experts: the
-    separate launches, with the same outputs."""
+    separate launches, with the same outputs; act-order int4 at the limits of
+    the routing-and-gather launch (16 tokens, 64 pairs, a capacity of 1024
+    rows, blocks of 128 feeding the large-batch kernel) and past them."""
     need_gpu()
     run_pair(key, M, bs, renorm=True)
 

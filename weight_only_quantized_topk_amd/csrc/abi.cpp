@@ -432,6 +432,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     WQ_REQUIRE(!large || wq::prefill_fits(d->capacity, d->k_in), WQ_ERR_UNSUPPORTED,
                "%s: activations of %zu rows x %d channels exceed 4 GiB (large-batch kernel)", who, d->capacity,
                d->k_in);
+    bool gathered = false;  // the act-order rows already gathered by the routing launch
     if (route) {
         if (!act_order && !tiny && !large &&
             wq::decode_route_supported(stage, d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
@@ -448,12 +449,28 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
             wq::launch_gemm_decode_route(wbits, bf16, g, ra, s);
             return after_launch(who);
         }
-        WQ_TRY(launch_routing(route->logits, d->M, d->E, d->topk, route->renormalize, d->block_size,
-                              route->topk_weights, route->topk_ids, const_cast<int32_t*>(d->d_sorted_token_ids),
-                              const_cast<int32_t*>(d->d_expert_ids),
-                              const_cast<int32_t*>(d->d_num_tokens_post_padded), d->capacity, s, who));
+        if (act_order && !tiny &&
+            wq::route_gather_supported(d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
+            // one launch routes, sorts and gathers the act-order rows
+            uint16_t* a1 = static_cast<uint16_t*>(workspace);
+            wq::launch_route_align_gather(route->logits, d->M, d->E, d->topk, route->renormalize ? 1 : 0,
+                                          route->topk_weights, route->topk_ids,
+                                          d->block_size, const_cast<int32_t*>(d->d_sorted_token_ids),
+                                          const_cast<int32_t*>(d->d_expert_ids),
+                                          const_cast<int32_t*>(d->d_num_tokens_post_padded), (int)d->capacity, g.a,
+                                          d->d_k_perm, d->k_in, a1, s);
+            WQ_TRY(after_launch(who));
+            g.a = a1;
+            g.a_direct = 1;
+            gathered = true;
+        } else {
+            WQ_TRY(launch_routing(route->logits, d->M, d->E, d->topk, route->renormalize, d->block_size,
+                                  route->topk_weights, route->topk_ids, const_cast<int32_t*>(d->d_sorted_token_ids),
+                                  const_cast<int32_t*>(d->d_expert_ids),
+                                  const_cast<int32_t*>(d->d_num_tokens_post_padded), d->capacity, s, who));
+        }
     }
-    if (act_order && !tiny) {
+    if (act_order && !tiny && !gathered) {
         uint16_t* a1 = static_cast<uint16_t*>(workspace);
         wq::launch_gather_perm(g.a, d->d_k_perm, g.sorted, g.expert_ids, g.ntpp, d->M, d->topk, d->k_in,
                                d->block_size, g.cap, a1, s);

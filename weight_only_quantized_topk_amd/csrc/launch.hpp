@@ -112,6 +112,13 @@ struct RouteArgs {
 };
 constexpr int FR_MAX_PAIRS = 64;   // M * topk
 constexpr int FR_MAX_CAP = 1024;   // capacity rows held in LDS
+// routing, sort and the act-order gather (row p of the gathered activations
+// a1 = x of sorted_token_ids[p]'s token permuted by its expert's perm) in one
+// launch, for batches within route_gather_supported
+bool route_gather_supported(int M, int topk, int E, int cap, int BS);
+void launch_route_align_gather(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids,
+                               int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, int cap,
+                               const uint16_t* x, const int32_t* perm, int k_in, uint16_t* a1, hipStream_t s);
 // up to 16 pairs over at most 64 experts, blocks of 16 or 32 rows
 bool decode_route_supported(int stage, int M, int topk, int E, int cap, int block_size);
 void launch_gemm_decode_route(int wbits, bool bf16, const GemmArgs& g, const RouteArgs& ra, hipStream_t s);

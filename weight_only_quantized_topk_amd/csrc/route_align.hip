@@ -204,6 +204,76 @@ __global__ __launch_bounds__(1024) void route_align_wave_kernel(const float* __r
     align_wave(sids, M * topk, E, BS, cap, lane, sorted, expert_ids, ntpp);
 }
 
+// Routing, sort and the act-order gather of a small batch in one launch.
+// Workgroup p routes and sorts the whole batch itself into LDS (rank-counting
+// top-k, one wave per token, then align_wave: the same arithmetic as
+// route_align_wave_kernel, so the same arrays), the first workgroup also
+// writes the routing arrays, and then workgroup p writes row p of the
+// gathered activations: x of the pair's token in its expert's input-channel
+// order (a pad row as zeros), which the gate/up GEMM reads by sorted position.
+// For at most 16 tokens, 64 pairs, 64 experts and a capacity of at most
+// FR_MAX_CAP rows.
+__global__ __launch_bounds__(256) void route_align_gather_kernel(
+    const float* __restrict__ logits, int M, int E, int topk, int renormalize, float* __restrict__ w_out,
+    int32_t* __restrict__ ids_out, int BS, int32_t* __restrict__ sorted_out, int32_t* __restrict__ expert_ids_out,
+    int32_t* __restrict__ ntpp_out, int cap, const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+    int k_in, uint16_t* __restrict__ a1) {
+    __shared__ int s_sorted[FR_MAX_CAP];
+    __shared__ int s_blocks[FR_MAX_CAP / 16];
+    __shared__ int s_ids[FR_MAX_PAIRS];
+    __shared__ float s_w[FR_MAX_PAIRS];
+    __shared__ int s_ntpp;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int T = M * topk;
+    for (int m = wave; m < M; m += 4)
+        route_token_rank(logits + (size_t)m * E, E, topk, renormalize, lane, s_w + m * topk, s_ids + m * topk, nullptr);
+    __syncthreads();
+    if (wave == 0) align_wave(s_ids, T, E, BS, cap, lane, s_sorted, s_blocks, &s_ntpp);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < T; i += 256) {
+            w_out[i] = s_w[i];
+            ids_out[i] = s_ids[i];
+        }
+        for (int i = threadIdx.x; i < cap; i += 256) sorted_out[i] = s_sorted[i];
+        for (int i = threadIdx.x; i < cap / BS; i += 256) expert_ids_out[i] = s_blocks[i];
+        if (threadIdx.x == 0) *ntpp_out = s_ntpp;
+    }
+    const int p = blockIdx.x;
+    if (p >= s_ntpp) return;
+    const int pair = s_sorted[p];
+    uint16_t* dst = a1 + (size_t)p * k_in;
+    if (pair >= T) {
+        for (int k = threadIdx.x * 8; k < k_in; k += 256 * 8) *reinterpret_cast<u32x4*>(dst + k) = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const uint16_t* src = x + (size_t)(pair / topk) * k_in;
+    const int32_t* pe = perm + (size_t)s_blocks[p / BS] * k_in;
+    for (int k = threadIdx.x * 8; k < k_in; k += 256 * 8) {
+        const u32x4 i0 = ldg128(pe + k);
+        const u32x4 i1 = ldg128(pe + k + 4);
+        u32x4 v;
+        v[0] = (uint32_t)src[i0[0]] | ((uint32_t)src[i0[1]] << 16);
+        v[1] = (uint32_t)src[i0[2]] | ((uint32_t)src[i0[3]] << 16);
+        v[2] = (uint32_t)src[i1[0]] | ((uint32_t)src[i1[1]] << 16);
+        v[3] = (uint32_t)src[i1[2]] | ((uint32_t)src[i1[3]] << 16);
+        *reinterpret_cast<u32x4*>(dst + k) = v;
+    }
+}
+
+bool route_gather_supported(int M, int topk, int E, int cap, int BS) {
+    return M >= 1 && M <= ROUTE_ALIGN_MAX_M && M * topk <= FR_MAX_PAIRS && E <= 64 && cap <= FR_MAX_CAP &&
+           cap % BS == 0;
+}
+
+void launch_route_align_gather(const float* logits, int M, int E, int topk, int renormalize, float* w, int32_t* ids,
+                               int BS, int32_t* sorted, int32_t* expert_ids, int32_t* ntpp, int cap,
+                               const uint16_t* x, const int32_t* perm, int k_in, uint16_t* a1, hipStream_t s) {
+    hipLaunchKernelGGL(route_align_gather_kernel, dim3(cap), dim3(256), 0, s, logits, M, E, topk, renormalize, w, ids,
+                       BS, sorted, expert_ids, ntpp, cap, x, perm, k_in, a1);
+}
+
 static int id_bits(int E) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;

@@ -121,9 +121,12 @@ class MoERunner:
         self.work2 = torch.empty(ws2, dtype=torch.uint8, device=dev) if ws2 else None
         self.h = torch.empty((max(self.cap, 1), p.N), dtype=p.act, device=dev)
         self.out = torch.empty((M, p.K), dtype=p.act, device=dev)
-        # the smallest batches route inside the GATE_UP launch (moe_route_gate_up)
-        self.route_in_gate_up = (not act_order and M * topk <= 16 and p.E <= 64 and self.bs in (16, 32)
-                                 and self.cap <= 1024)
+        # the smallest batches route inside the GATE_UP call (moe_route_gate_up: without act-order one launch,
+        # with it the routing launch also gathers the permuted rows)
+        if act_order:
+            self.route_in_gate_up = 1 <= M <= 16 and M * topk <= 64 and p.E <= 64 and self.cap <= 1024
+        else:
+            self.route_in_gate_up = (M * topk <= 16 and p.E <= 64 and self.bs in (16, 32) and self.cap <= 1024)
 
     def route_align(self, logits, stream=None):
         ops.moe_route_align(logits, self.topk, self.renormalize, self.bs, self.w, self.ids, self.st, self.ex,
