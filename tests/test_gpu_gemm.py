@@ -258,8 +258,9 @@ def test_down_many_experts_two_blocks(M):
 def test_down_split_wide_grid_w4():
     """int4, 4096 outputs, k_in 4096, M = 1024 (2048 pairs): the DOWN grid of
     512-row tiles is smaller than one round of resident workgroups, so K is
-    split in 4 slices on the 512 x 128 eight-wave shape (the workspace holds 4
-    fp32 slabs); the output of sampled tokens against the oracle."""
+    split in 3 slices of unequal length (21, 21 and 22 K steps of 64 channels)
+    on the 512 x 128 eight-wave shape (the workspace holds the most slabs any
+    block size takes, 4); the output of sampled tokens against the oracle."""
     need_gpu()
     spec = W4.with_(name="w4-split-wide", K=4096, N=4096)
     wts = gen.make_moe_weights(spec, seed_config=508)

@@ -381,9 +381,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void fp8_prefill_kernel(Fp8GemmArgs g
     }
 
     const int C = g.k_in / FP8_KCHUNK;
-    const int steps_per = C / (int)gridDim.z;
-    const int step0 = (int)blockIdx.z * steps_per;
-    const int step_end = step0 + steps_per;
+    const int step0 = (int)((long)blockIdx.z * C / gridDim.z);  // K slices of unequal length where gridDim.z does not divide C
+    const int step_end = (int)((long)(blockIdx.z + 1) * C / gridDim.z);
     const size_t expert_bytes = (size_t)g.n_out * g.k_in;
     const float* se = g.s + (size_t)e * g.n_out;
 
@@ -560,9 +559,9 @@ bool fp8_prefill_supported(int n_out, int k_in, int block_size) {
     return (block_size == 64 || block_size % 128 == 0) && n_out % 128 == 0 && k_in % FP8_KCHUNK == 0;
 }
 
-// K slices of the large-batch DOWN (1, 2 or 4): the smallest split whose
-// grid, in rounds of resident workgroups of 1/ks of K, takes at least 15 %
-// fewer rounds than the next smaller one, with at least 8 K steps per slice
+// K slices of the large-batch DOWN (1 to 4): the smallest split whose grid,
+// in rounds of resident workgroups of 1/ks of K, takes at least 15 % fewer
+// rounds than the smallest split before it, with at least 8 K steps per slice
 int fp8_down_split(int T, int E, int n_out, int k_in, int block_size) {
     if (!fp8_prefill_supported(n_out, k_in, block_size) || T <= 0) return 1;
     const int steps = k_in / FP8_KCHUNK;
@@ -575,8 +574,8 @@ int fp8_down_split(int T, int E, int n_out, int k_in, int block_size) {
     auto rounds = [&](int ks) { return (double)((wgs * ks + slots - 1) / slots) / ks; };
     int best = 1;
     double best_t = rounds(1);
-    for (int ks = 2; ks <= 4; ks *= 2) {
-        if (steps % ks != 0 || steps / ks < 8) break;
+    for (int ks = 2; ks <= 4; ++ks) {
+        if (steps / ks < 8) break;
         const double t = rounds(ks);
         if (t < 0.85 * best_t) best = ks, best_t = t;
     }

@@ -88,9 +88,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     const int C = g.k_in / KCHUNK;  // packed chunks per 16-row tile
     // K slice of this workgroup (only DOWN is ever split)
-    const int steps_per = g.k_in / PF_BK / (int)gridDim.z;
-    const int step0 = (int)blockIdx.z * steps_per;
-    const int step_end = step0 + steps_per;
+    const int nsteps = g.k_in / PF_BK;
+    const int step0 = (int)((long)blockIdx.z * nsteps / gridDim.z);
+    const int step_end = (int)((long)(blockIdx.z + 1) * nsteps / gridDim.z);
     const size_t expert_bytes = (size_t)(g.n_out / TILE_ROWS) * C * CHUNK_BYTES;
     const uint16_t* se = g.s + (size_t)e * g.groups * g.n_out;
 
@@ -357,9 +357,10 @@ static PrefillShape prefill_shape(int wbits, int stage, int n_out, int block_siz
 static long est_mtiles(int T, int E, int bm) { return ((long)T + (long)std::min(T, E) * (bm / 2) + bm - 1) / bm; }
 
 // K slices of DOWN for blocks of block_size rows: the smallest split in
-// {1, 2, 4} whose grid, counted in rounds of resident workgroups of 1/ks of the
-// full K, takes at least 15 % fewer rounds than the next smaller one, with at
-// least 16 K steps per slice.  Measured (Mixtral int8 DOWN): M = 1024
+// {1, 2, 3, 4} whose grid, counted in rounds of resident workgroups of 1/ks of
+// the full K, takes at least 15 % fewer rounds than the smallest split before
+// it, with at least 16 K steps per slice (slices of unequal length where ks
+// does not divide the steps).  Measured (Mixtral int8 DOWN): M = 1024
 // 337 -> 296 us (4 slices), M = 512 327 -> 184 us (2 slices).
 int prefill_down_split(int T, int E, int n_out, int k_in, int block_size) {
     if (!prefill_supported(n_out, k_in, block_size) || T <= 0) return 1;
@@ -369,8 +370,8 @@ int prefill_down_split(int T, int E, int n_out, int k_in, int block_size) {
     auto rounds = [&](int ks) { return (double)((wgs * ks + si.slots - 1) / si.slots) / ks; };
     int best = 1;
     double best_t = rounds(1);
-    for (int ks = 2; ks <= 4; ks *= 2) {
-        if (steps % ks != 0 || steps / ks < 16) break;
+    for (int ks = 2; ks <= 4; ++ks) {
+        if (steps / ks < 16) break;
         const double t = rounds(ks);
         if (t < 0.85 * best_t) best = ks, best_t = t;
     }
