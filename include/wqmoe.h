@@ -319,18 +319,19 @@ wq_status sparse24_w4a16_gemm(const void* d_x, int M, int K, int N, const void* 
  * integration", nm-vllm PR 266, review thread: the MoE file compared against
  * csrc/quantization/gptq_marlin/gptq_marlin.cu -- and the GEMV/GEMM mix picked
  * by batch-size heuristics of "[WIP] AWQ Faster Kernels", vLLM issue 3289).
- * 1..16 rows without act-order run one small-batch (GEMV-like) kernel; beyond
- * that (or with act-order) the grouped GEMM of this library with one expert and
- * top-1: up to 24 rows the small-batch kernel, up to 192 the large-batch kernel
- * with 64-row tiles, above that 128-row tiles; fp32 accumulation, rounded once
- * to the activation type.
+ * 1..128 rows without act-order run one small-batch kernel (GEMV-like up to 2
+ * rows, then token tiles of 16, 32 or 64 rows shared by 8 weight tiles);
+ * beyond that (or with act-order) the grouped GEMM of this library with one
+ * expert and top-1: up to 24 rows the small-batch kernel, up to 192 the
+ * large-batch kernel with 64-row tiles, above that 128-row tiles; fp32
+ * accumulation, rounded once to the activation type.
  *   d_x [M, K] act dtype; d_y [M, N] act dtype
  *   d_w_packed, d_scales: wq_pack_w4 / wq_pack_w8 output for E = 1, n_out = N,
  *     k_in = K (no gate/up interleave); int4 group_size 128 or -1, int8 -1
  *   d_k_perm: int4 act-order permutation from wq_pack_w4 ([1, K]) or NULL
  *   d_workspace: dense_gemm_workspace_bytes(M, K, N, act_order) bytes, 256-byte
  *     aligned (the routing arrays, the act-order gather, fp32 partial sums);
- *     0 bytes (NULL allowed) for 1..16 rows without act-order: one
+ *     0 bytes (NULL allowed) for 1..128 rows without act-order: one
  *     small-batch kernel (1..2 rows staged in LDS whole when they fit 96 KiB,
  *     else the tokens of each K chunk staged in LDS and shared by the 8
  *     weight tiles of a workgroup)

@@ -115,11 +115,12 @@ def test_dense_validation_and_workspace():
     long K, the fp32 slabs."""
     L = wq.load()
     p = C.c_void_p(FAKE)
-    assert L.dense_gemm_workspace_bytes(1, 4096, 4096, 0) == 0   # 1..16 rows: one kernel, no workspace
+    assert L.dense_gemm_workspace_bytes(1, 4096, 4096, 0) == 0   # 1..128 rows: one kernel, no workspace
     assert L.dense_gemm_workspace_bytes(2, 32768, 4096, 0) == 0  # rows too long for LDS: staged per chunk
     assert L.dense_gemm_workspace_bytes(16, 4096, 4096, 0) == 0
     assert L.dense_gemm_workspace_bytes(1, 4096, 4096, 1) > 0     # act-order gathers through the workspace
-    assert L.dense_gemm_workspace_bytes(17, 4096, 4096, 0) >= 17 * 4096 * 4
+    assert L.dense_gemm_workspace_bytes(128, 4096, 4096, 0) == 0
+    assert L.dense_gemm_workspace_bytes(129, 4096, 4096, 0) >= 129 * 4096 * 4
     assert L.dense_gemm_workspace_bytes(300, 4096, 256, 0) >= 4 * 300 * 256 * 4   # K split in 4
     assert L.dense_gemm_workspace_bytes(300, 4096, 256, 1) > L.dense_gemm_workspace_bytes(300, 4096, 256, 0)
     assert L.dense_gemm_workspace_bytes(0, 4096, 256, 0) == 0
@@ -129,7 +130,7 @@ def test_dense_validation_and_workspace():
     assert _status("dense_w4a16_gemm", *a4(N=200))[0] == wq.WQ_ERR_UNSUPPORTED      # N % 16
     assert _status("dense_w4a16_gemm", *a4(gs=64))[0] == wq.WQ_ERR_UNSUPPORTED
     assert _status("dense_w4a16_gemm", *a4(dt=wq.WQ_BF16))[0] == wq.WQ_ERR_UNSUPPORTED
-    assert _status("dense_w4a16_gemm", *a4(M=17, ws=16))[0] == wq.WQ_ERR_INVALID   # workspace too small
+    assert _status("dense_w4a16_gemm", *a4(M=129, ws=16))[0] == wq.WQ_ERR_INVALID  # workspace too small
     assert _status("dense_w4a16_gemm", *a4(M=-1))[0] == wq.WQ_ERR_INVALID
     assert _status("dense_w4a16_gemm", *a4(x=None))[0] == wq.WQ_ERR_INVALID
     assert _status("dense_w4a16_gemm", *a4(M=0, ws=0))[0] == wq.WQ_OK

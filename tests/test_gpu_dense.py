@@ -1,9 +1,10 @@
 """GPU parity of the dense single-expert W4A16 / W8A16 linear layer
 (dense_w4a16_gemm, dense_w8a16_gemm) against the oracle's projection with one
 expert and top-1: every batch regime of the dispatch (the single-kernel paths
-for 1..2 rows staged whole and for 3..16 rows staged per K chunk, the grouped
-small-batch kernel up to 24 rows and with act-order, 64-row tiles up to 192,
-128-row tiles above, with a K split for a long K and few outputs), int8
+for 1..2 rows staged whole and for 3..128 rows staged per K chunk in token
+groups of 16, 32 or 64 rows -- each size, its boundaries and a second group --
+the grouped small-batch kernel with act-order, 64-row tiles up to 192, 128-row
+tiles above, with a K split for a long K and few outputs), int8
 per-column, int4 group-128, per-column and act-order weights, and output
 counts that leave the last 8-tile workgroup partial.  Relative
 Frobenius error <= 5e-3 and max abs error <= 3e-2 * max |ref|."""
@@ -48,7 +49,7 @@ def setup(key):
 
 
 @pytest.mark.parametrize("key", ["w8", "w4", "w4ao", "w4pc", "w8rag", "w4rag"])
-@pytest.mark.parametrize("M", [1, 2, 4, 5, 13, 16, 40, 150, 300])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 13, 16, 17, 32, 33, 40, 64, 65, 128, 129, 150, 300])
 def test_dense_matches_oracle(key, M):
     need_gpu()
     spec, wts, (wd, sd, kd) = setup(key)
@@ -113,15 +114,15 @@ def test_dense_equals_moe_raw_bits():
     need_gpu()
     spec, wts, (wd, sd, _) = setup("w8")
     n_out, K = wts.w1q.shape[1], wts.w1q.shape[2]
-    M = 20  # grouped small-batch kernel, blocks of 16 (up to 16 rows a kernel of its own runs)
+    M = 150  # the grouped large-batch kernel, blocks of 64, one K slice (up to 128 rows a kernel of its own runs)
     toks = gen.make_tokens(spec, M, seed_config=670)
     x = dev_u16(toks.x, spec.act)
     y = wq.dense_w8a16_gemm(x, n_out, wd, sd)
     ids = torch.zeros((M, 1), dtype=torch.int32, device="cuda")
-    cap = wq.moe_align_capacity(M, 1, 1, 16)
-    st, ex, nt = wq.moe_align(ids, 1, 16, cap)
+    cap = wq.moe_align_capacity(M, 1, 1, 64)
+    st, ex, nt = wq.moe_align(ids, 1, 64, cap)
     raw = torch.empty((M, n_out), dtype=torch.float32, device="cuda")
-    wq.moe_w8a16_gemm(wq.WQ_STAGE_RAW, x, M, 1, 1, n_out, K, wd, sd, st, ex, nt, cap, 16, None, raw,
+    wq.moe_w8a16_gemm(wq.WQ_STAGE_RAW, x, M, 1, 1, n_out, K, wd, sd, st, ex, nt, cap, 64, None, raw,
                       act_dtype=wq.WQ_BF16)
     torch.cuda.synchronize()
     assert torch.equal(y, raw.to(torch.bfloat16))

@@ -720,8 +720,8 @@ struct DenseLayout {
     size_t cap, off_sorted, off_eids, off_ntpp, off_w, off_a1, off_y, total;
 };
 
-// batch-size dispatch of the grouped path (above 16 rows, or with act-order;
-// up to 16 rows without act-order one dense kernel runs, no workspace): the
+// batch-size dispatch of the grouped path (above 128 rows, or with act-order;
+// up to 128 rows without act-order one dense kernel runs, no workspace): the
 // small-batch kernel (blocks of 16 rows) up to 24 rows, the large-batch kernel
 // with 64-row tiles up to 192 (one expert gives few token tiles: 128-row tiles
 // left the GPU part idle, Yi-34B shape int4 M = 128 0.114 -> 0.091 ms, M = 192

@@ -117,18 +117,29 @@ __global__ __launch_bounds__(NW * 64) void dense_decode_kernel(const uint16_t* _
 }
 
 // ----------------------------------------------------------------------------
-// 3..16 token rows (one 16-row token tile): one workgroup per NWV 16-row weight
-// tiles, one tile per wave, every wave walking all of K.  The tokens of one
-// K chunk (16 rows x KCHUNK channels) are staged once in LDS and shared by the
-// NWV waves (double-buffered, one barrier per chunk): a workgroup covering
-// many weight rows stages the token rows few times, where a workgroup per
-// tile would read them from L2 once per tile.  Each wave keeps PF chunks of
-// its weights in flight; token rows at or beyond M read row M - 1 and their
-// outputs are dropped.  Same numerics as the kernel above; no reduction
-// across waves, the output is rounded once to the activation type.
+// 3..128 token rows (R 16-row token tiles per workgroup, grid y over groups
+// of 16 R rows): one workgroup per NWV 16-row weight tiles, one tile per
+// wave, every wave walking all of K.  The tokens of one K chunk (16 R rows x
+// KCHUNK channels) are staged once in LDS and shared by the NWV waves
+// (double-buffered, one barrier per chunk): a workgroup covering many weight
+// rows stages the token rows few times, where a workgroup per tile would read
+// them from L2 once per tile; each chunk's weights are converted once per wave
+// for all R token tiles.  Each wave keeps PF chunks of its weights in flight;
+// token rows at or beyond M read row M - 1 and their outputs are dropped.
+// Same numerics as the kernel above; no reduction across waves, the output is
+// rounded once to the activation type.  Yi-34B shape int4 (K = 7168, N =
+// 20480), against the grouped large-batch path it replaces above 16 rows:
+// M = 32 50.9 -> 34.4 us, M = 64 66.6 -> 47.5 us, M = 128 90.7 -> 79.7 us
+// (4 token tiles on 8 waves; 8 token tiles or 4 waves were slower).
 constexpr int DS_ROWB = 2 * 128 + 16;  // LDS bytes per token row of one chunk (int4 chunk + pad)
+#ifndef DS_NW2
+#define DS_NW2 8
+#define DS_NW4 8
+#define DS_PF4 4
+#define DS_R4 4
+#endif
 
-template <int WBITS, bool BF16, int NWV, int PF>
+template <int WBITS, bool BF16, int NWV, int PF, int R>
 __global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* __restrict__ x, int M, int K, int N,
                                                                 const uint8_t* __restrict__ w,
                                                                 const uint16_t* __restrict__ s, int groups,
@@ -136,10 +147,11 @@ __global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* 
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
     constexpr int KSTEPS = KCHUNK / 32;
     constexpr int NT = NWV * 64;
-    constexpr int PIECES = 16 * KCHUNK / 8;  // 16-byte token pieces per chunk
-    static_assert(PIECES <= NT, "one token piece per thread");
+    constexpr int ROWS = 16 * R;                  // token rows of the workgroup
+    constexpr int PIECES = ROWS * KCHUNK / 8;     // 16-byte token pieces per chunk
+    constexpr int XP = (PIECES + NT - 1) / NT;    // per thread
     static_assert(PF % 2 == 0, "chunk parity = slot parity: the token buffers alternate with it");
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * DS_ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][ROWS * DS_ROWB];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -147,6 +159,7 @@ __global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* 
     const int t_raw = NWV * blockIdx.x + wave;
     const bool tvalid = t_raw < ntiles;
     const int t = tvalid ? t_raw : ntiles - 1;  // surplus waves stream the last tile and store nothing
+    const int m0 = blockIdx.y * ROWS;
     const int C = K / KCHUNK;
     const int rowq = 4 * (lane >> 4);
 
@@ -159,35 +172,61 @@ __global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* 
         if constexpr (WBITS == 4)
             sv[slot] = *reinterpret_cast<const u32x2*>(st + (size_t)(groups > 1 ? c : 0) * N);
     };
-    // token piece of this thread (threads past PIECES reload the last piece)
-    const int q = min(tid, PIECES - 1);
-    const int xr = q / (KCHUNK / 8), xp = q % (KCHUNK / 8);
-    const uint16_t* xsrc = x + (size_t)min(xr, M - 1) * K + 8 * xp;
-    const int xoff = xr * DS_ROWB + 16 * xp;
-    u32x4 xv[2];
-    auto xload = [&](int c, int slot) { xv[slot] = ldg128(xsrc + (size_t)c * KCHUNK); };
-    auto xstore = [&](int slot, int buf) { *reinterpret_cast<u32x4*>(&xs[buf][xoff]) = xv[slot]; };
+    // token pieces of this thread (threads past PIECES reload the last piece;
+    // rows at or beyond M read row M - 1)
+    const uint16_t* xsrc[XP];
+    int xoff[XP];
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+        const int q = min(tid + NT * i, PIECES - 1);
+        const int xr = q / (KCHUNK / 8), xp = q % (KCHUNK / 8);
+        xsrc[i] = x + (size_t)min(m0 + xr, M - 1) * K + 8 * xp;
+        xoff[i] = xr * DS_ROWB + 16 * xp;
+    }
+    u32x4 xv[2][XP];
+    auto xload = [&](int c, int slot) {
+#pragma unroll
+        for (int i = 0; i < XP; ++i) xv[slot][i] = ldg128(xsrc[i] + (size_t)c * KCHUNK);
+    };
+    auto xstore = [&](int slot, int buf) {
+#pragma unroll
+        for (int i = 0; i < XP; ++i) *reinterpret_cast<u32x4*>(&xs[buf][xoff[i]]) = xv[slot][i];
+    };
 
-    const int brow = min(lane & 15, M - 1);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int slot, int buf) {
-        const uint8_t* xb = &xs[buf][brow * DS_ROWB + 16 * (lane >> 4)];
         if constexpr (WBITS == 4) {
-            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+            u32x4 a[KSTEPS];
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-                part = mfma16x16x32<false>(dequant_w4_f16(wv[slot][ks]),
-                                           *reinterpret_cast<const u32x4*>(xb + 64 * ks), part);
+            for (int ks = 0; ks < KSTEPS; ++ks) a[ks] = dequant_w4_f16(wv[slot][ks]);
             const uint32_t lo = sv[slot][0], hi = sv[slot][1];
-            acc[0] += part[0] * f16_to_f32((uint16_t)(lo & 0xffffu));
-            acc[1] += part[1] * f16_to_f32((uint16_t)(lo >> 16));
-            acc[2] += part[2] * f16_to_f32((uint16_t)(hi & 0xffffu));
-            acc[3] += part[3] * f16_to_f32((uint16_t)(hi >> 16));
-        } else {
+            const float s0 = f16_to_f32((uint16_t)(lo & 0xffffu)), s1 = f16_to_f32((uint16_t)(lo >> 16));
+            const float s2 = f16_to_f32((uint16_t)(hi & 0xffffu)), s3 = f16_to_f32((uint16_t)(hi >> 16));
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-                acc = mfma16x16x32<BF16>(dequant_w8x8<BF16>(wv[slot][2 * ks], wv[slot][2 * ks + 1]),
-                                         *reinterpret_cast<const u32x4*>(xb + 64 * ks), acc);
+            for (int r = 0; r < R; ++r) {
+                const uint8_t* xb = &xs[buf][(16 * r + (lane & 15)) * DS_ROWB + 16 * (lane >> 4)];
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    part = mfma16x16x32<false>(a[ks], *reinterpret_cast<const u32x4*>(xb + 64 * ks), part);
+                acc[r][0] += part[0] * s0;
+                acc[r][1] += part[1] * s1;
+                acc[r][2] += part[2] * s2;
+                acc[r][3] += part[3] * s3;
+            }
+        } else {
+            u32x4 a[KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) a[ks] = dequant_w8x8<BF16>(wv[slot][2 * ks], wv[slot][2 * ks + 1]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint8_t* xb = &xs[buf][(16 * r + (lane & 15)) * DS_ROWB + 16 * (lane >> 4)];
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    acc[r] = mfma16x16x32<BF16>(a[ks], *reinterpret_cast<const u32x4*>(xb + 64 * ks), acc[r]);
+            }
         }
     };
     // chunk c: store its tokens (loaded one chunk earlier), load chunk c + 2's
@@ -211,19 +250,24 @@ __global__ __launch_bounds__(NWV * 64) void dense_stream_kernel(const uint16_t* 
         if (c0 + decltype(U)::value < C) body(c0 + decltype(U)::value, U);
     });
 
-    const int m = lane & 15;
-    if (tvalid && m < M) {
+    if (tvalid) {
         const int n0 = t * TILE_ROWS + rowq;
-        float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            o[r] = acc[r];
-            if constexpr (WBITS == 8) o[r] *= act_to_f32<BF16>(s[n0 + r]);
+        for (int r = 0; r < R; ++r) {
+            const int m = m0 + 16 * r + (lane & 15);
+            if (m < M) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = acc[r][i];
+                    if constexpr (WBITS == 8) o[i] *= act_to_f32<BF16>(s[n0 + i]);
+                }
+                u32x2 stv;
+                stv[0] = (uint32_t)f32_to_act<BF16>(o[0]) | ((uint32_t)f32_to_act<BF16>(o[1]) << 16);
+                stv[1] = (uint32_t)f32_to_act<BF16>(o[2]) | ((uint32_t)f32_to_act<BF16>(o[3]) << 16);
+                *reinterpret_cast<u32x2*>(y + (size_t)m * N + n0) = stv;
+            }
         }
-        u32x2 stv;
-        stv[0] = (uint32_t)f32_to_act<BF16>(o[0]) | ((uint32_t)f32_to_act<BF16>(o[1]) << 16);
-        stv[1] = (uint32_t)f32_to_act<BF16>(o[2]) | ((uint32_t)f32_to_act<BF16>(o[3]) << 16);
-        *reinterpret_cast<u32x2*>(y + (size_t)m * N + n0) = stv;
     }
 }
 
@@ -234,7 +278,10 @@ size_t dense_decode_lds(int M, int K) { return (size_t)M * (2 * (size_t)K + 16);
 // 28.7 us, M = 4 34.0 / 29.1 us whole-row / chunk-streaming)
 static bool dense_rows_in_lds(int M, int K) { return M >= 1 && M <= 2 && dense_decode_lds(M, K) <= 96 * 1024; }
 
-bool dense_decode_supported(int M, int K) { return dense_rows_in_lds(M, K) || (M >= 1 && M <= 16); }
+#ifndef DS_MAX_ROWS
+#define DS_MAX_ROWS 128
+#endif
+bool dense_decode_supported(int M, int K) { return dense_rows_in_lds(M, K) || (M >= 1 && M <= DS_MAX_ROWS); }
 
 template <int WBITS, bool BF16>
 static void launch_dd(const uint16_t* x, int M, int K, int N, const uint8_t* w, const uint16_t* s, int groups,
@@ -248,12 +295,20 @@ static void launch_dd(const uint16_t* x, int M, int K, int N, const uint8_t* w, 
     hipLaunchKernelGGL(kern, dim3(N / TILE_ROWS), dim3(NW * 64), lds, st, x, M, K, N, w, s, groups, y);
 }
 
+template <int WBITS, bool BF16, int NWV, int PF, int R>
+static void launch_ds_r(const uint16_t* x, int M, int K, int N, const uint8_t* w, const uint16_t* s, int groups,
+                        uint16_t* y, hipStream_t st) {
+    const dim3 grid((N / TILE_ROWS + NWV - 1) / NWV, (M + 16 * R - 1) / (16 * R));
+    hipLaunchKernelGGL((dense_stream_kernel<WBITS, BF16, NWV, PF, R>), grid, dim3(NWV * 64), 0, st, x, M, K, N, w, s,
+                       groups, y);
+}
+
 template <int WBITS, bool BF16>
 static void launch_ds(const uint16_t* x, int M, int K, int N, const uint8_t* w, const uint16_t* s, int groups,
                       uint16_t* y, hipStream_t st) {
-    constexpr int NWV = 8, PF = 6;
-    hipLaunchKernelGGL((dense_stream_kernel<WBITS, BF16, NWV, PF>), dim3((N / TILE_ROWS + NWV - 1) / NWV),
-                       dim3(NWV * 64), 0, st, x, M, K, N, w, s, groups, y);
+    if (M <= 16) launch_ds_r<WBITS, BF16, 8, 6, 1>(x, M, K, N, w, s, groups, y, st);
+    else if (M <= 32) launch_ds_r<WBITS, BF16, DS_NW2, 6, 2>(x, M, K, N, w, s, groups, y, st);
+    else launch_ds_r<WBITS, BF16, DS_NW4, DS_PF4, DS_R4>(x, M, K, N, w, s, groups, y, st);
 }
 
 void launch_dense_decode(int wbits, bool bf16, const uint16_t* x, int M, int K, int N, const uint8_t* w,
