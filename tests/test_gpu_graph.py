@@ -2,7 +2,9 @@
 HIP graph: every replay equals the eager call bit for bit, with eager work and
 synchronisations between the replays, and a replay after the inputs are
 updated in place follows the new inputs.  Small-batch and large-batch kernels,
-int8 per-column and int4 act-order weights."""
+the one-launch routing paths, int8 per-column and int4 act-order weights, the
+FP8 layer (one token: x quantised inside gate/up, the top-k sum inside DOWN),
+the dense and 2:4 linear layers."""
 import pytest
 
 import gen
@@ -13,18 +15,28 @@ pytestmark = pytest.mark.gpu
 
 W8 = gen.CFG2.with_(name="w8-graph", E=8, topk=2, K=512, N=384)
 W4AO = gen.CFG3.with_(name="w4ao-graph", E=8, topk=2, K=512, N=384)
-SPECS = {"w8": (W8, 520), "w4ao": (W4AO, 521)}
+F8 = gen.CFG_FP8.with_(name="fp8-graph", E=8, topk=2, K=512, N=384)
+SPECS = {"w8": (W8, 520), "w4ao": (W4AO, 521), "fp8": (F8, 522)}
 _packed = {}
 
 
 def packed(key):
     if key not in _packed:
         spec, seed = SPECS[key]
-        wts = gen.make_moe_weights(spec, seed_config=seed)
-        act = torch.float16 if spec.act == "f16" else torch.bfloat16
-        _packed[key] = (spec, wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2, act, spec.group_size,
-                                          wts.g1, wts.g2))
+        if key == "fp8":
+            fw = gen.make_fp8_weights(spec, seed_config=seed)
+            _packed[key] = (spec, wq.pack_moe_fp8(fw.w1, fw.s1, fw.w2, fw.s2, torch.bfloat16, spec.a1, spec.a2))
+        else:
+            wts = gen.make_moe_weights(spec, seed_config=seed)
+            act = torch.float16 if spec.act == "f16" else torch.bfloat16
+            _packed[key] = (spec, wq.pack_moe(spec.bits, wts.w1q, wts.s1, wts.w2q, wts.s2, act, spec.group_size,
+                                              wts.g1, wts.g2))
     return _packed[key]
+
+
+def runner(key, p, M, spec):
+    cls = wq.Fp8MoERunner if key == "fp8" else wq.MoERunner
+    return cls(p, M, spec.topk, spec.renormalize)
 
 
 def inputs(spec, M, seed):
@@ -32,17 +44,20 @@ def inputs(spec, M, seed):
     return dev_u16(toks.x, spec.act), torch.from_numpy(toks.logits).cuda()
 
 
-@pytest.mark.parametrize("key,M", [("w8", 5), ("w8", 300), ("w4ao", 40), ("w4ao", 600)])
+# one token (routing and sort inside the gate/up launch, the top-k sum inside DOWN), a few
+# tokens, act-order with the routing launch gathering the rows (1 and 16 tokens), large batches
+@pytest.mark.parametrize("key,M", [("w8", 1), ("w8", 5), ("w8", 300), ("w4ao", 1), ("w4ao", 16), ("w4ao", 40),
+                                   ("w4ao", 600), ("fp8", 1), ("fp8", 300)])
 def test_graph_replay_matches_eager(key, M):
     need_gpu()
     spec, p = packed(key)
     say("graph", key, M)
     x, lg = inputs(spec, M, 900 + M)
-    eager = wq.MoERunner(p, M, spec.topk, spec.renormalize)
+    eager = runner(key, p, M, spec)
     ref = eager(x, lg).clone()
     torch.cuda.synchronize()
 
-    r = wq.MoERunner(p, M, spec.topk, spec.renormalize)
+    r = runner(key, p, M, spec)
     assert r.bs == eager.bs
     xs, ls = x.clone(), lg.clone()
     r.capture(xs, ls)
@@ -105,10 +120,10 @@ def _check_replays(call, out, x, x2):
     assert not torch.equal(ref2, ref)
 
 
-@pytest.mark.parametrize("M", [1, 16, 200])
+@pytest.mark.parametrize("M", [1, 16, 64, 200])
 def test_graph_replay_dense(M):
-    """The dense int4 linear layer (one kernel at one row; identity routing,
-    small- or large-batch GEMM and combine above) as a graph."""
+    """The dense int4 linear layer (one kernel up to 128 rows; identity
+    routing, large-batch GEMM and combine above) as a graph."""
     need_gpu()
     import numpy as np
     spec = gen.CFG3.with_(name="w4-dense-graph", E=1, topk=1, K=512, N=192, act_order=False)
