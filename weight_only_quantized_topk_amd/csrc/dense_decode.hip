@@ -132,6 +132,10 @@ __global__ __launch_bounds__(NW * 64) void dense_decode_kernel(const uint16_t* _
 // M = 32 50.9 -> 34.4 us, M = 64 66.6 -> 47.5 us, M = 128 90.7 -> 79.7 us
 // (4 token tiles on 8 waves; 8 token tiles or 4 waves were slower).
 constexpr int DS_ROWB = 2 * 128 + 16;  // LDS bytes per token row of one chunk (int4 chunk + pad)
+#ifndef DS_NW1
+#define DS_NW1 8
+#define DS_PF1 6
+#endif
 #ifndef DS_NW2
 #define DS_NW2 8
 #define DS_NW4 8
@@ -306,7 +310,7 @@ static void launch_ds_r(const uint16_t* x, int M, int K, int N, const uint8_t* w
 template <int WBITS, bool BF16>
 static void launch_ds(const uint16_t* x, int M, int K, int N, const uint8_t* w, const uint16_t* s, int groups,
                       uint16_t* y, hipStream_t st) {
-    if (M <= 16) launch_ds_r<WBITS, BF16, 8, 6, 1>(x, M, K, N, w, s, groups, y, st);
+    if (M <= 16) launch_ds_r<WBITS, BF16, DS_NW1, DS_PF1, 1>(x, M, K, N, w, s, groups, y, st);
     else if (M <= 32) launch_ds_r<WBITS, BF16, DS_NW2, 6, 2>(x, M, K, N, w, s, groups, y, st);
     else launch_ds_r<WBITS, BF16, DS_NW4, DS_PF4, DS_R4>(x, M, K, N, w, s, groups, y, st);
 }
