@@ -37,7 +37,7 @@ def test_sparse_exact_integer():
     assert np.array_equal(y.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("M", [1, 16, 45, 130])
+@pytest.mark.parametrize("M", [1, 16, 45, 72, 96, 130])
 def test_sparse_float(M):
     need_gpu()
     spec = gen.CFG4.with_(K=1024, N=256)

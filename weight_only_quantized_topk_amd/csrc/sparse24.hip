@@ -638,6 +638,8 @@ static void launch_pipe(const uint16_t* x, int M, int K, int N, const uint8_t* v
                        meta, scales, sstride, y);
 }
 
+constexpr long SP_STREAM_SLOTS = 256;  // resident 16-wave streaming workgroups: one per CU
+
 // batch-size dispatch, chosen by timing on MI355X at K = 7168, N = 20480:
 // M = 1, 2: 18 -> 13 us; M = 4: 18.6 -> 17.0 us with the decode kernel
 template <int VBITS>
@@ -654,7 +656,10 @@ static void launch_sparse24_b(const uint16_t* x, int M, int K, int N, const uint
                            scales, ss, y);
     } else if (M <= 16) {
         launch_stream<VBITS, 1>(x, M, K, N, vals, meta, scales, ss, y, s);
-    } else if (M <= 64) {
+    } else if (M <= 64 || (M <= 128 && (long)((N / 16 + 15) / 16) * ((M + 31) / 32) <= SP_STREAM_SLOTS)) {
+        // 32-token groups while they all fit one round of resident 16-wave
+        // workgroups (M = 96: 49.2 -> 37.5 us; M = 128 would take two rounds: 66 us
+        // against 49.5 us for two 64-token groups)
         launch_stream<VBITS, 2>(x, M, K, N, vals, meta, scales, ss, y, s);
     } else {
         launch_stream<VBITS, 4>(x, M, K, N, vals, meta, scales, ss, y, s);
