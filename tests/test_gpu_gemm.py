@@ -221,10 +221,11 @@ def test_down_split_k(key, bs, M):
 
 
 @pytest.mark.parametrize("key", ["w4k", "w8k"])
-@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("M", [1, 5, 64])
 def test_down_decode_long_k(key, M):
     """k_in = 4096 with 256 outputs over few experts through the small-batch
-    kernel (long reductions: 8 waves per workgroup)."""
+    kernel (long reductions: 8 waves per workgroup; int8 takes 4 row tiles per
+    workgroup, with one token block per pass at 5 tokens and two at 64)."""
     _check_down(key, 16, M)
 
 

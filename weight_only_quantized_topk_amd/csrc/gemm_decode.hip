@@ -341,6 +341,14 @@ static void launch_decode_cfg(const GemmArgs& g, hipStream_t s, const RouteArgs&
 // blocks per pass whatever the mean rows per expert: its head experts hold
 // several blocks (DeepSeek-V2 shape M = 64: gate/up 157 -> 132 us in the
 // layer).
+// DOWN of a long reduction (Mixtral, 224 int8 or 112 int4 chunks per row
+// tile) takes four row tiles on 8 waves: every token row a wave loads then
+// feeds four tiles instead of two (the token rows, read again by every
+// workgroup of the expert, are most of what a wave loads at 16 rows per
+// expert) -- Mixtral M = 64: int8 DOWN 106 -> 96 us, int4 100 -> 72 us;
+// int8 M = 32: 90 -> 83 us, M = 8: 75 -> 73 us (int4 keeps its 4-wave shape
+// there); one tile per workgroup (twice the token reads) ran 164-173 us at
+// M = 64, eight (32 workgroups per expert) 167 us.
 template <int WBITS, bool BF16, int STAGE>
 static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
     constexpr bool GU = STAGE == STAGE_GATE_UP;
@@ -370,9 +378,11 @@ static void launch_decode_r(const GemmArgs& g, hipStream_t s) {
         else if (g.E == 1) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 2, 4>(g, s);
         else if (short_k) launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 2, 3>(g, s);
         else if (WBITS == 4 && np4_ok && wg4 >= 512) launch_decode_cfg<WBITS, BF16, STAGE, 1, 4, 4, 2>(g, s);
+        else if (WBITS == 8 && np4_ok) launch_decode_cfg<WBITS, BF16, STAGE, 1, GU ? 1 : 4, 8, 2>(g, s);
         else launch_decode_cfg<WBITS, BF16, STAGE, 1, 2, 8, 3>(g, s);
     } else if (rows <= 24) {
         if (!GU && short_k && np4_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 4, 2, 2>(g, s);
+        else if (!GU && np4_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, GU ? 1 : 4, 8, 2>(g, s);
         else if (np2_ok) launch_decode_cfg<WBITS, BF16, STAGE, 2, 2, 4, 2>(g, s);
         else launch_decode_cfg<WBITS, BF16, STAGE, 2, 1, 4, 2>(g, s);
     } else {

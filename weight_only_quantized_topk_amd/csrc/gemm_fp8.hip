@@ -298,7 +298,10 @@ bool fp8_fold_quant_supported(int stage, int M, int n_out, int k_in, int block_s
 
 // Shapes by the mean rows per touched expert, as for the int8 small-batch
 // kernel (the same bytes per weight); a 2 KiB chunk covers 128 channels, so
-// half as many chunks per row as int8.
+// half as many chunks per row as int8.  DOWN of a long reduction at 9-24 rows
+// per expert takes four row tiles on 8 waves, as int8 does (Mixtral M = 64:
+// layer 0.276 -> 0.266 ms); at 8 tokens that shape measured slower (0.184 ->
+// 0.191 ms), so one block per pass keeps two tiles.
 template <int STAGE>
 static void launch_fp8_decode_r(const Fp8GemmArgs& g, hipStream_t s) {
     constexpr bool GU = STAGE == STAGE_GATE_UP;
@@ -307,6 +310,7 @@ static void launch_fp8_decode_r(const Fp8GemmArgs& g, hipStream_t s) {
     const int touched = T < g.E ? T : g.E;
     const int rows = (T + touched - 1) / touched;
     const bool np2_ok = (g.n_out % (TILE_ROWS * NT1 * 2)) == 0;
+    const bool np4_ok = (g.n_out % (TILE_ROWS * NT1 * 4)) == 0;
     const bool short_k = g.k_in / FP8_KCHUNK <= 16;
     if constexpr (GU) {
         if (g.x16) {  // one token, quantised in the kernel
@@ -324,7 +328,8 @@ static void launch_fp8_decode_r(const Fp8GemmArgs& g, hipStream_t s) {
         else if (short_k) launch_fp8_decode_cfg<STAGE, 1, 2, 2, 3>(g, s);
         else launch_fp8_decode_cfg<STAGE, 1, 2, 8, 2>(g, s);
     } else if (rows <= 24) {
-        if (np2_ok) launch_fp8_decode_cfg<STAGE, 2, 2, 4, 2>(g, s);
+        if (!GU && !short_k && np4_ok) launch_fp8_decode_cfg<STAGE, 2, GU ? 1 : 4, 8, 2>(g, s);
+        else if (np2_ok) launch_fp8_decode_cfg<STAGE, 2, 2, 4, 2>(g, s);
         else launch_fp8_decode_cfg<STAGE, 2, 1, 4, 2>(g, s);
     } else {
         if (!GU && np2_ok) launch_fp8_decode_cfg<STAGE, 4, 2, 4, 2>(g, s);
