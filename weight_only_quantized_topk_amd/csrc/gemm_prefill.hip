@@ -345,9 +345,13 @@ static ShapeInfo shape_info(PrefillShape sh) {
     }
 }
 
-static PrefillShape prefill_shape(int wbits, int stage, int n_out, int block_size) {
+static PrefillShape prefill_shape(int wbits, int stage, int n_out, int k_in, int block_size) {
     if (block_size == 64) return (stage == STAGE_DOWN && n_out % 256 == 0) ? PF_T256 : PF_T128;
-    if (n_out % 512 == 0) return PF_N512;
+    // int8 DOWN with a reduction too short to split (under 32 K steps) takes
+    // two 256-row workgroups per CU (DeepSeek-V2 shape, k_in 1536, M = 4096:
+    // DOWN 715 -> 681 us; Mixtral M = 1024, 3 K slices, stays at 512 rows:
+    // 278 against 284 us)
+    if (n_out % 512 == 0 && !(stage == STAGE_DOWN && wbits == 8 && k_in < 32 * PF_BK)) return PF_N512;
     if (n_out % 256 == 0 && wbits == 8) return PF_N256;
     return PF_N128;
 }
@@ -365,7 +369,7 @@ static long est_mtiles(int T, int E, int bm) { return ((long)T + (long)std::min(
 int prefill_down_split(int T, int E, int n_out, int k_in, int block_size) {
     if (!prefill_supported(n_out, k_in, block_size) || T <= 0) return 1;
     const int steps = k_in / PF_BK;
-    const ShapeInfo si = shape_info(prefill_shape(8, STAGE_DOWN, n_out, block_size));
+    const ShapeInfo si = shape_info(prefill_shape(8, STAGE_DOWN, n_out, k_in, block_size));
     const long wgs = (long)(n_out / si.bn) * est_mtiles(T, E, si.bm);
     auto rounds = [&](int ks) { return (double)((wgs * ks + si.slots - 1) / si.slots) / ks; };
     int best = 1;
@@ -398,7 +402,7 @@ static void launch_prefill_shape(PrefillShape sh, const GemmArgs& g, int ksplit,
 
 template <int WBITS, bool BF16>
 static void launch_prefill_s(int stage, const GemmArgs& g, int ksplit, hipStream_t s) {
-    const PrefillShape sh = prefill_shape(WBITS, stage, g.n_out, g.block_size);
+    const PrefillShape sh = prefill_shape(WBITS, stage, g.n_out, g.k_in, g.block_size);
     if (stage == STAGE_GATE_UP) launch_prefill_shape<WBITS, BF16, STAGE_GATE_UP>(sh, g, 1, s);
     else if (stage == STAGE_DOWN) launch_prefill_shape<WBITS, BF16, STAGE_DOWN>(sh, g, ksplit, s);
     else launch_prefill_shape<WBITS, BF16, STAGE_RAW>(sh, g, 1, s);
