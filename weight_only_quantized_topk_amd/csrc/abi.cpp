@@ -482,6 +482,11 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     if (stage == WQ_STAGE_DOWN) {
         y = static_cast<float*>(workspace);
         g.out = y;
+        // a large-batch DOWN that does not split K writes each pair's routed
+        // row rounded once to the activation type (half the bytes of the
+        // per-pair rows each way); split slices keep fp32 partial sums
+        g.y_act = (large && wq::prefill_down_split(d->M * d->topk, d->E, d->n_out, d->k_in, d->block_size) == 1)
+                      ? 1 : 0;
     }
     int ksplit = 1;
     if (tiny) ksplit = wq::launch_gemm_tiny(wbits, bf16, stage, g, act_order ? d->d_k_perm : nullptr, slabs, s);
@@ -489,7 +494,13 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
     else wq::launch_gemm_decode(wbits, bf16, stage, g, s);
     WQ_TRY(after_launch(who));
     if (stage == WQ_STAGE_DOWN) {
-        wq::launch_combine(y, d->M, d->topk, d->n_out, ksplit, bf16, static_cast<uint16_t*>(d->d_out), s);
+        if (g.y_act) {
+            WQ_REQUIRE(ksplit == 1, WQ_ERR_HIP, "%s: DOWN split K after all", who);
+            wq::launch_combine_act(reinterpret_cast<const uint16_t*>(y), d->M, d->topk, d->n_out, bf16,
+                                   static_cast<uint16_t*>(d->d_out), s);
+        } else {
+            wq::launch_combine(y, d->M, d->topk, d->n_out, ksplit, bf16, static_cast<uint16_t*>(d->d_out), s);
+        }
         WQ_TRY(after_launch(who));
     }
     return ok();

@@ -506,6 +506,51 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<u32x2*>(out + m * n + c) = st;
 }
 
+// the same sum over Y rows already rounded to the activation type (a large-
+// batch DOWN without a K split writes them so): each term widened exactly to
+// fp32, ascending j, one rounding
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_act_kernel(const uint16_t* __restrict__ y, int M, int topk, int n,
+                                                          uint16_t* __restrict__ out) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // 4 outputs each
+    const size_t total = (size_t)M * n / 4;
+    if (q >= total) return;
+    const size_t m = q * 4 / n;
+    const int c = (int)(q * 4 % n);
+    const uint16_t* row = y + m * topk * n + c;  // pair m * topk + j at row + j * n
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](u32x2 v) {
+        const uint32_t lo = v[0], hi = v[1];
+        acc[0] += act_to_f32<BF16>((uint16_t)(lo & 0xffffu));
+        acc[1] += act_to_f32<BF16>((uint16_t)(lo >> 16));
+        acc[2] += act_to_f32<BF16>((uint16_t)(hi & 0xffffu));
+        acc[3] += act_to_f32<BF16>((uint16_t)(hi >> 16));
+    };
+    int j = 0;
+    for (; j + 4 <= topk; j += 4) {  // four rows in flight at once
+        const u32x2 v0 = *reinterpret_cast<const u32x2*>(row + (size_t)j * n);
+        const u32x2 v1 = *reinterpret_cast<const u32x2*>(row + (size_t)(j + 1) * n);
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(row + (size_t)(j + 2) * n);
+        const u32x2 v3 = *reinterpret_cast<const u32x2*>(row + (size_t)(j + 3) * n);
+        add(v0);
+        add(v1);
+        add(v2);
+        add(v3);
+    }
+    for (; j < topk; ++j) add(*reinterpret_cast<const u32x2*>(row + (size_t)j * n));
+    u32x2 st;
+    st[0] = (uint32_t)f32_to_act<BF16>(acc[0]) | ((uint32_t)f32_to_act<BF16>(acc[1]) << 16);
+    st[1] = (uint32_t)f32_to_act<BF16>(acc[2]) | ((uint32_t)f32_to_act<BF16>(acc[3]) << 16);
+    *reinterpret_cast<u32x2*>(out + m * n + c) = st;
+}
+
+void launch_combine_act(const uint16_t* y, int M, int topk, int n, bool bf16, uint16_t* out, hipStream_t s) {
+    const size_t total = (size_t)M * n / 4;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (bf16) hipLaunchKernelGGL(combine_act_kernel<true>, grid, dim3(256), 0, s, y, M, topk, n, out);
+    else hipLaunchKernelGGL(combine_act_kernel<false>, grid, dim3(256), 0, s, y, M, topk, n, out);
+}
+
 void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf16, uint16_t* out, hipStream_t s) {
     const size_t total = (size_t)M * n / 4;
     const dim3 grid((unsigned)((total + 255) / 256));

@@ -297,7 +297,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_prefill_kernel(GemmArgs g) 
                         if constexpr (WBITS == 8) v *= act_to_f32<BF16>(se[n0 + r]);
                         o[r] = v * rw;
                     }
-                    *reinterpret_cast<f32x4*>(yslab + (size_t)pair * g.n_out + n0) = o;
+                    if (STAGE == STAGE_DOWN && g.y_act) {  // one K slice: the row rounded once to act
+                        u32x2 st;
+                        st[0] = (uint32_t)f32_to_act<BF16>(o[0]) | ((uint32_t)f32_to_act<BF16>(o[1]) << 16);
+                        st[1] = (uint32_t)f32_to_act<BF16>(o[2]) | ((uint32_t)f32_to_act<BF16>(o[3]) << 16);
+                        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (size_t)pair * g.n_out + n0) = st;
+                    } else {
+                        *reinterpret_cast<f32x4*>(yslab + (size_t)pair * g.n_out + n0) = o;
+                    }
                 }
             }
         }

@@ -38,12 +38,13 @@ struct GemmArgs {
     const int32_t* expert_ids;
     const int32_t* ntpp;
     const float* topk_w;      // DOWN
-    void* out;                // H (act) / Y (f32) / Z (f32)
+    void* out;                // H (act) / Y (f32, or act with y_act) / Z (f32)
     int M, topk, E, n_out, k_in;
     int block_size;
     int groups;               // scale groups along k_in (1 = per column)
     int a_direct;             // 1: A row = sorted position; 0: A row = token of the pair
     int cap;
+    int y_act;                // large-batch DOWN without a K split: Y rows in the activation type
 };
 
 // ---------------------------------------------------------------------------
@@ -162,6 +163,7 @@ void launch_gather_perm(const uint16_t* x, const int32_t* perm, const int32_t* s
                         hipStream_t s);
 // out[m, c] = sum_j sum_z Y[z][m*topk + j, c] over top-k slots j and K slices z
 // (ascending, fp32), rounded to act; slab z starts at y + z * M*topk*n
+void launch_combine_act(const uint16_t* y, int M, int topk, int n, bool bf16, uint16_t* out, hipStream_t s);
 void launch_combine(const float* y, int M, int topk, int n, int ksplit, bool bf16, uint16_t* out, hipStream_t s);
 
 // 2:4-sparse linear with 4- or 8-bit kept codes; group_size 128 (scales
