@@ -169,7 +169,9 @@ wq_status moe_route_align(const float* d_logits, int M, int E, int topk, int ren
  *           per-pair outputs: fp32 [M*topk, n_out], times 2 or 4 when the
  *           large-batch kernel splits k_in to fill the GPU (small M*topk *
  *           n_out); the slices are added in a fixed order, so results do not
- *           vary from run to run.
+ *           vary from run to run.  A large-batch DOWN that does not split
+ *           k_in stores each pair's weighted row rounded once to the act
+ *           dtype (half that space used) before the fp32 sum.
  *  RAW      d_a = x [M, k_in]; d_out = fp32 [M*topk, n_out]:
  *           Z[i, r] = sum_k x[i/topk, k] * W_{expert(i)}[r, k], packed row order.
  * The workspace size comes from moe_gemm_workspace_bytes() with the call's
