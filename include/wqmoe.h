@@ -212,11 +212,14 @@ wq_status moe_w8a16_gemm(const wq_moe_gemm_desc* d, void* stream);
  * it is one launch: every workgroup of the small-batch GEMM ranks and sorts the
  * batch itself (the decode step's route -> sort -> gate/up chain of "Marlin moe
  * integration", nm-vllm PR 266, with the fused_moe interface of its review
- * thread).  With act-order (int4 with d_k_perm), for at most 16 tokens, 64
- * pairs, 64 experts and a capacity of at most 1024 rows, the routing launch
- * also gathers the permuted activation rows into the workspace, one launch
- * fewer than the two calls.  Otherwise it runs the two calls' launches in
- * order.  The outputs are those of the two calls, bit for bit.
+ * thread).  With act-order (int4 with d_k_perm): one token (within the
+ * limits above, n_out a multiple of 64, k_in at most 16384 and a multiple of
+ * 8) is also one launch, each workgroup gathering the token's row in its
+ * expert's channel order into LDS; for at most 16 tokens, 64 pairs, 64 experts
+ * and a capacity of at most 1024 rows, the routing launch also gathers the
+ * permuted activation rows into the workspace, one launch fewer than the two
+ * calls.  Otherwise it runs the two calls' launches in order.  The outputs are
+ * those of the two calls, bit for bit.
  *   d_logits [M, E] float32, renormalize: as moe_route_align
  *   d_topk_weights [M, topk] float32, d_topk_ids [M, topk] int32: written
  *   d: a GATE_UP descriptor (stage WQ_STAGE_GATE_UP) whose d_sorted_token_ids,

@@ -1,8 +1,10 @@
 """GPU parity of moe_route_gate_up, the call that routes, sorts and runs the
 GATE_UP stage: for up to 16 pairs over up to 64 experts (blocks of 16 or 32,
 no act-order) one kernel whose every workgroup routes and sorts the batch
-itself; with act-order (up to 16 tokens, 64 pairs, 64 experts) a routing
-launch that also gathers the permuted rows; otherwise the separate launches.  Its outputs -- routing weights and
+itself; with act-order one token in the same kernel, each workgroup gathering
+the permuted row into LDS, and up to 16 tokens (64 pairs, 64 experts) a
+routing launch that also gathers the permuted rows; otherwise the separate
+launches.  Its outputs -- routing weights and
 ids, sorted_token_ids, expert_ids, num_tokens_post_padded and every H row up
 to the padded total -- equal those of moe_route_align followed by the GEMM's
 GATE_UP call bit for bit (int8 bf16 and fp16, int4 group-128 and per-column,
@@ -27,6 +29,7 @@ SPECS = {
     # act-order int4: the routing launch also gathers the permuted rows
     "w4ao": gen.CFG3.with_(name="rgu-w4ao", E=8, topk=2, K=256, N=512, act_order=True),
     "w4aoe64": gen.CFG3.with_(name="rgu-w4aoe64", E=64, topk=4, K=384, N=256, act_order=True),
+    "w4ao6": gen.CFG3.with_(name="rgu-w4ao6", E=8, topk=6, K=1024, N=256, act_order=True),
 }
 _cache = {}
 
@@ -96,6 +99,17 @@ def run_pair(key, M, bs, renorm, ties=False):
 def test_route_gate_up_equals_two_calls(key, M, bs):
     need_gpu()
     run_pair(key, M, bs, renorm=True)
+
+
+@pytest.mark.parametrize("key", ["w4ao", "w4aoe64", "w4ao6"])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_route_gate_up_act_order_one_token(key, bs):
+    """One token of an act-order int4 layer: one kernel that routes, sorts and
+    gathers the token's row in each expert's channel order into LDS (top-2,
+    top-4 and top-6: both of its launch shapes) -- the same outputs as the two
+    calls with the gathered rows in the workspace."""
+    need_gpu()
+    run_pair(key, 1, bs, renorm=True)
 
 
 @pytest.mark.parametrize("renorm", [True, False])

@@ -449,6 +449,23 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
             wq::launch_gemm_decode_route(wbits, bf16, g, ra, s);
             return after_launch(who);
         }
+        if (act_order && !tiny && !large &&
+            wq::decode_route_ao_supported(d->M, d->topk, d->n_out, d->k_in) &&
+            wq::decode_route_supported(stage, d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
+            // one token of an act-order layer: one launch routes, sorts, and
+            // multiplies, each workgroup gathering the token's permuted row
+            wq::RouteArgs ra;
+            ra.logits = route->logits;
+            ra.renormalize = route->renormalize ? 1 : 0;
+            ra.w_out = route->topk_weights;
+            ra.ids_out = route->topk_ids;
+            ra.sorted_out = const_cast<int32_t*>(d->d_sorted_token_ids);
+            ra.expert_ids_out = const_cast<int32_t*>(d->d_expert_ids);
+            ra.ntpp_out = const_cast<int32_t*>(d->d_num_tokens_post_padded);
+            ra.perm = d->d_k_perm;
+            wq::launch_gemm_decode_route(wbits, bf16, g, ra, s);
+            return after_launch(who);
+        }
         if (act_order && !tiny &&
             wq::route_gather_supported(d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
             // one launch routes, sorts and gathers the act-order rows

@@ -40,7 +40,10 @@ namespace wq {
 // later stages), so route, sort and gate/up are one launch.  For batches of at
 // most FR_MAX_PAIRS pairs over at most 64 experts and a capacity of at most
 // FR_MAX_CAP rows.
-template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH, bool FR = false>
+// AO (with FR, one token of an act-order layer): the workgroup gathers the
+// token's row in its expert's channel order, x[perm[e][k]], into LDS (the
+// values the act-order gather launch writes) and reads every B operand there.
+template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH, bool FR = false, bool AO = false>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g, RouteArgs ra) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;  // 16-row tiles per workgroup
     constexpr int KCHUNK = WFmt<WBITS>::KCHUNK;
@@ -55,6 +58,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g, RouteA
     const int BS = g.block_size;
     const int spb = BS / 16;
     __shared__ f32x4 red[NW][NT][RMAX][64];
+    extern __shared__ __attribute__((aligned(16))) uint16_t ao_x[];  // AO: the gathered row, k_in values
+    static_assert(!AO || (FR && WBITS == 4 && STAGE == STAGE_GATE_UP), "act-order rows in LDS: one-token int4 GATE_UP");
 
     // the routing arrays: the caller's, or (FR) computed here into LDS
     const int32_t* sorted_ids = g.sorted;
@@ -160,7 +165,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g, RouteA
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) xv[d][r][s] = ldg128(arow[r] + c * KCHUNK + 32 * s);
+                for (int s = 0; s < KSTEPS; ++s) {
+                    if constexpr (AO) xv[d][r][s] = *reinterpret_cast<const u32x4*>(ao_x + c * KCHUNK + 32 * s + 8 * (lane >> 4));
+                    else xv[d][r][s] = ldg128(arow[r] + c * KCHUNK + 32 * s);
+                }
             if constexpr (WBITS == 4) {
                 const size_t gc = grouped ? (size_t)c : 0;  // per-column scales: a harmless reread of group 0
 #pragma unroll
@@ -293,6 +301,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g, RouteA
         }
     }
     if (j >= S) return;
+    if constexpr (AO) {
+        // one token (M == 1): every real row of the expert is row 0 of x
+        const int32_t* pe = ra.perm + (size_t)e * g.k_in;
+        for (int k = threadIdx.x * 8; k < g.k_in; k += 64 * NW * 8) {
+            const u32x4 i0 = ldg128(pe + k);
+            const u32x4 i1 = ldg128(pe + k + 4);
+            u32x4 v;
+            v[0] = (uint32_t)g.a[i0[0]] | ((uint32_t)g.a[i0[1]] << 16);
+            v[1] = (uint32_t)g.a[i0[2]] | ((uint32_t)g.a[i0[3]] << 16);
+            v[2] = (uint32_t)g.a[i1[0]] | ((uint32_t)g.a[i1[1]] << 16);
+            v[3] = (uint32_t)g.a[i1[2]] | ((uint32_t)g.a[i1[3]] << 16);
+            *reinterpret_cast<u32x4*>(ao_x + k) = v;
+        }
+        __syncthreads();
+    }
     // sub-blocks j .. j + RMAX - 1 of the expert: one pass of RMAX, or of 2
     // and/or 1 for the expert's last R < RMAX
     const int R = min(RMAX, S - j);
@@ -312,13 +335,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(GemmArgs g, RouteA
     }
 }
 
-template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH, bool FR = false>
+template <int WBITS, bool BF16, int STAGE, int RMAX, int NP, int NW, int DEPTH, bool FR = false, bool AO = false>
 static void launch_decode_cfg(const GemmArgs& g, hipStream_t s, const RouteArgs& ra = RouteArgs{}) {
     constexpr int NT = (STAGE == STAGE_GATE_UP) ? 2 * NP : NP;
     const int nsb = g.cap / 16;  // 16-row sub-blocks, over grid y (at most 65535) and z
     const dim3 grid(g.n_out / (TILE_ROWS * NT), std::min(nsb, 65535), (nsb + 65534) / 65535);
-    hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH, FR>), grid, dim3(64 * NW), 0, s,
-                       g, ra);
+    hipLaunchKernelGGL((gemm_decode_kernel<WBITS, BF16, STAGE, RMAX, NP, NW, DEPTH, FR, AO>), grid, dim3(64 * NW),
+                       AO ? (size_t)g.k_in * 2 : 0, s, g, ra);
 }
 
 // Shapes by batch, measured on MI355X with the last-level cache flushed before
@@ -398,10 +421,21 @@ bool decode_route_supported(int stage, int M, int topk, int E, int cap, int bloc
            cap <= FR_MAX_CAP && (block_size == 16 || block_size == 32);
 }
 
+bool decode_route_ao_supported(int M, int topk, int n_out, int k_in) {
+    return M == 1 && topk <= 16 && n_out % (TILE_ROWS * 2 * 2) == 0 && k_in <= DECODE_AO_MAX_K && k_in % 8 == 0;
+}
+
 template <int WBITS, bool BF16>
 static void launch_decode_route_w(const GemmArgs& g, const RouteArgs& ra, hipStream_t s) {
     const int T = g.M * g.topk;
     const bool np2_ok = (g.n_out % (TILE_ROWS * 2 * 2)) == 0;
+    if constexpr (WBITS == 4) {
+        if (ra.perm) {  // decode_route_ao_supported: the shapes launch_decode_r picks for one int4 token
+            if (T <= 4) launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 2, 2, 2, true, true>(g, s, ra);
+            else launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 2, 4, 2, true, true>(g, s, ra);
+            return;
+        }
+    }
     if (WBITS == 4 && np2_ok && T <= 4) launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 2, 2, 2, true>(g, s, ra);
     else if (WBITS == 4 && np2_ok) launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 2, 4, 2, true>(g, s, ra);
     else launch_decode_cfg<WBITS, BF16, STAGE_GATE_UP, 1, 1, 4, 2, true>(g, s, ra);

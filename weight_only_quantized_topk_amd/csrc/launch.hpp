@@ -110,6 +110,7 @@ struct RouteArgs {
     int32_t* sorted_out = nullptr;
     int32_t* expert_ids_out = nullptr;
     int32_t* ntpp_out = nullptr;
+    const int32_t* perm = nullptr;  // act-order, one token: the experts' k_in permutations
 };
 constexpr int FR_MAX_PAIRS = 64;   // M * topk
 constexpr int FR_MAX_CAP = 1024;   // capacity rows held in LDS
@@ -122,6 +123,10 @@ void launch_route_align_gather(const float* logits, int M, int E, int topk, int 
                                const uint16_t* x, const int32_t* perm, int k_in, uint16_t* a1, hipStream_t s);
 // up to 16 pairs over at most 64 experts, blocks of 16 or 32 rows
 bool decode_route_supported(int stage, int M, int topk, int E, int cap, int block_size);
+// the same launch for one token of an act-order (int4) layer: each workgroup
+// gathers the token's row in its expert's channel order into LDS
+constexpr int DECODE_AO_MAX_K = 16384;
+bool decode_route_ao_supported(int M, int topk, int n_out, int k_in);
 void launch_gemm_decode_route(int wbits, bool bf16, const GemmArgs& g, const RouteArgs& ra, hipStream_t s);
 // batches of at most 4 tokens: one workgroup per (used block, 16 or 32 weight
 // rows), the block's token rows staged in LDS (through the act-order
