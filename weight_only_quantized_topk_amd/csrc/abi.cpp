@@ -434,9 +434,13 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
                d->k_in);
     bool gathered = false;  // the act-order rows already gathered by the routing launch
     if (route) {
-        if (!act_order && !tiny && !large &&
-            wq::decode_route_supported(stage, d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
-            // one launch: the small-batch kernel routes and sorts the batch itself
+        // one launch: the small-batch kernel routes and sorts the batch itself,
+        // and for one token of an act-order layer each workgroup also gathers
+        // the token's row in its expert's channel order
+        const bool fold = !tiny && !large &&
+                          wq::decode_route_supported(stage, d->M, d->topk, d->E, (int)d->capacity, d->block_size) &&
+                          (!act_order || wq::decode_route_ao_supported(d->M, d->topk, d->n_out, d->k_in));
+        if (fold) {
             wq::RouteArgs ra;
             ra.logits = route->logits;
             ra.renormalize = route->renormalize ? 1 : 0;
@@ -446,23 +450,7 @@ static wq_status moe_gemm(const wq_moe_gemm_desc* d, int wbits, void* stream, co
             ra.sorted_out = const_cast<int32_t*>(d->d_sorted_token_ids);
             ra.expert_ids_out = const_cast<int32_t*>(d->d_expert_ids);
             ra.ntpp_out = const_cast<int32_t*>(d->d_num_tokens_post_padded);
-            wq::launch_gemm_decode_route(wbits, bf16, g, ra, s);
-            return after_launch(who);
-        }
-        if (act_order && !tiny && !large &&
-            wq::decode_route_ao_supported(d->M, d->topk, d->n_out, d->k_in) &&
-            wq::decode_route_supported(stage, d->M, d->topk, d->E, (int)d->capacity, d->block_size)) {
-            // one token of an act-order layer: one launch routes, sorts, and
-            // multiplies, each workgroup gathering the token's permuted row
-            wq::RouteArgs ra;
-            ra.logits = route->logits;
-            ra.renormalize = route->renormalize ? 1 : 0;
-            ra.w_out = route->topk_weights;
-            ra.ids_out = route->topk_ids;
-            ra.sorted_out = const_cast<int32_t*>(d->d_sorted_token_ids);
-            ra.expert_ids_out = const_cast<int32_t*>(d->d_expert_ids);
-            ra.ntpp_out = const_cast<int32_t*>(d->d_num_tokens_post_padded);
-            ra.perm = d->d_k_perm;
+            ra.perm = act_order ? d->d_k_perm : nullptr;
             wq::launch_gemm_decode_route(wbits, bf16, g, ra, s);
             return after_launch(who);
         }
